@@ -1,0 +1,208 @@
+"""Benchmark: one training step (forward + backward) of the deformable 3x3
+layer at N=16, Cin=Cout=256, 56x56, bf16 on one MI355X, through the C ABI.
+
+A step runs every stage of the hot path: the fused offset-conv + bilinear
+sampling kernel, the main-convolution MFMA GEMM, and the backward (dCol and dW
+GEMMs, sampling backward, offset-conv backward).  Inputs are seeded synthetic
+tensors already resident in HBM; the plan's halo comes from the offset
+histogram of a warm-up forward.  Prints one JSON line on stdout.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(wl):
+    """Algorithmic bytes and flops per launch of each kernel (see the header of
+    each kernel for what it must move).  bf16 = 2 bytes, fp32 accumulators 4."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    P = wl.n * wl.ho * wl.wo
+    ck = wl.c_in * wl.taps
+    x = wl.n * wl.c_in * wl.h * wl.w
+    cols = P * ck * esz
+    offs = P * wl.oc * 4
+    gemm_flop = 2.0 * wl.c_out * ck * P
+    off_flop = 2.0 * wl.oc * ck * P
+    return {
+        "fused_offset_sample": (x * esz + cols + wl.oc * ck * esz + (offs if wl.train else 0), off_flop),
+        "gemm_forward": (cols + wl.c_out * ck * esz + P * wl.c_out * esz, gemm_flop),
+        "gemm_dcol": (P * wl.c_out * esz + wl.c_out * ck * esz + cols, gemm_flop),
+        "gemm_dw": (cols + P * wl.c_out * esz + wl.c_out * ck * 4, gemm_flop),
+        "sample_backward": (cols + x * esz + offs + 2 * x * 4 + offs, 0.0),
+        "offset_weight_backward": (offs + x * esz + wl.oc * ck * 4, off_flop),
+        "offset_input_backward": (offs + wl.c_in * wl.oc * wl.taps * esz + x * 4 + x * esz, off_flop),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train_bf16_n16_c256_56x56_s1")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from irregular_gather_cnn_amd import _lib as L
+    from irregular_gather_cnn_amd.layer import DeformConv, halo_histogram
+    from irregular_gather_cnn_amd.synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    inp = make_inputs(wl, with_dy=True)
+    t = {k: torch.from_numpy(v).to(tdt).to(dev) for k, v in inp.items()}
+    geo = dict(n=wl.n, c_in=wl.c_in, h=wl.h, w=wl.w, c_out=wl.c_out, kh=wl.kh, kw=wl.kw,
+               stride=(wl.stride,) * 2, pad=(wl.pad,) * 2, dil=(wl.dil,) * 2, groups=wl.groups, dtype=wl.dtype)
+    log("bench: %s on %s" % (wl.name, torch.cuda.get_device_name(0)))
+
+    # plan from the measured offset distribution
+    probe = DeformConv(**geo, training=True, device=dev)
+    _, off = probe.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    hist = halo_histogram(probe.desc, off, 16)
+    off_h = off.cpu().numpy()
+    del probe
+    layer = DeformConv(**geo, plan=hist, training=True, device=dev)
+    info = layer.info
+    tot = float(sum(hist))
+    log("offset std %.3f px; fully outside taps %.4f; required-halo histogram %s"
+        % (float(off_h.std()), hist[-1] / tot, hist))
+    log("plan: tile %dx%d halo %d chunk %d, %d workgroups, %d B LDS, est. miss %.4f"
+        % (info["tile_h"], info["tile_w"], info["halo"], info["chunk"], info["num_workgroups"],
+           info["lds_bytes"], info["est_miss_fraction"]))
+
+    y = torch.empty((wl.n, wl.c_out, wl.ho, wl.wo), dtype=tdt, device=dev)
+    offs = torch.empty((wl.n, wl.oc, wl.ho, wl.wo), dtype=torch.float32, device=dev)
+    grads = dict(dx=torch.empty_like(t["x"]), dw_off=torch.empty_like(t["w_off"]), dw=torch.empty_like(t["w"]),
+                 db_off=torch.empty_like(t["b_off"]), db=torch.empty_like(t["b"]))
+
+    def step():
+        layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
+        layer.backward(t["x"], t["w_off"], t["w"], offs, t["dy"], out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    # timed region: exactly K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log("timed: %d steps, %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall))
+
+    # instrumented pass: per-kernel durations from events around each launch
+    L.deft_timing_start(64 * args.steps)
+    for _ in range(args.steps):
+        step()
+    L.deft_timing_stop()
+    per = {}
+    for i in range(L.deft_timing_count()):
+        name, ms = L.deft_timing_get(i)
+        per.setdefault(name, []).append(ms)
+    work = kernel_work(wl)
+    kernels = {}
+    for name, v in per.items():
+        avg = sum(v) / len(v)
+        launches = len(v) / args.steps
+        rec = {"avg_ms": round(avg, 5), "launches_per_step": launches, "ms_per_step": round(avg * launches, 5)}
+        if name in work:
+            b, f = work[name]
+            rec["gbs"] = round(b / (avg * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["gbs"] / HBM_PEAK_GBS, 4)
+            if f:
+                rec["tflops"] = round(f / (avg * 1e-3) / 1e12, 2)
+                rec["mfma_frac"] = round(rec["tflops"] / MFMA_PEAK_TFLOPS[wl.dtype], 4)
+        kernels[name] = rec
+    for name, rec in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+        log("  %-24s %s" % (name, rec))
+    fwd_ms = sum(kernels[k]["ms_per_step"] for k in ("prep_forward", "fused_offset_sample", "gemm_forward")
+                 if k in kernels)
+    bwd_ms = sum(r["ms_per_step"] for k, r in kernels.items()
+                 if k not in ("prep_forward", "fused_offset_sample", "gemm_forward"))
+
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
+    b, f = work[dom]
+    avg = kernels[dom]["avg_ms"]
+    gbs = b / (avg * 1e-3) / 1e9
+    if f and (f / b) > MFMA_PEAK_TFLOPS[wl.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(f / (avg * 1e-3) / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = int(b)
+    roof["traffic"] = None
+
+    total_flop = sum(f for k, (b_, f) in work.items())
+    gflops = total_flop / (ms_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        s1 = oracle.Shape(1, wl.c_in, wl.h, wl.w, wl.c_out, wl.kh, wl.kw, (wl.stride,) * 2, (wl.pad,) * 2,
+                          (wl.dil,) * 2, wl.groups)
+        done, t_cpu = 0, 0.0
+        while done < wl.n and t_cpu < args.cpu_seconds:
+            sl = slice(done, done + 1)
+            c0 = time.perf_counter()
+            _, o = oracle.forward(s1, inp["x"][sl], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+            oracle.backward(s1, inp["x"][sl], inp["w_off"], inp["w"], o, inp["dy"][sl])
+            t_cpu += time.perf_counter() - c0
+            done += 1
+        cpu_ms = t_cpu / done * wl.n * 1e3
+        cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
+               "sample": "fp64 forward+backward of %d of the %d images (%.1f s), scaled x%d/%d to one full step"
+                         % (done, wl.n, t_cpu, wl.n, done)}
+        log("cpu baseline: %s" % cpu)
+
+    line = {
+        "metric": "deformable 3x3 layer fwd+bwd ms & GB/s / MFMA % (N=16,C=256,56x56,bf16)",
+        "value": round(ms_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "n": wl.n, "c_in": wl.c_in, "c_out": wl.c_out, "h": wl.h, "w": wl.w,
+                   "kernel": [wl.kh, wl.kw], "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil,
+                   "offset_groups": wl.groups, "offset_std_px": wl.offset_std,
+                   "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk")}},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
+        "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
+        "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * deft.h -- C ABI of the MI355X (gfx950) deformable 3x3 convolution library.
+ *
+ * The layer (DefT explainer page, "The argument in one glance", parts "What
+ * people did" and "This paper's idea"; "Following a deformable layer through
+ * DefT", step 1): an offset convolution over the input predicts, for every
+ * filter tap at every output pixel, a fractional (dy, dx); each tap's sample
+ * point (its grid position plus that offset) is bilinearly interpolated from
+ * its four neighbouring input pixels into a deformed column buffer; the main
+ * convolution is a dense GEMM over those columns.  The offset convolution and
+ * the sampling run fused in one kernel so the offsets never leave the chip,
+ * and the input tile plus a halo sized from the offset distribution is staged
+ * in LDS (section "How DefT works", "The idea"; "Why it works").
+ *
+ * Conventions for every call:
+ *  - Tensors are dense, row-major, on the device, owned by the caller.  The
+ *    library allocates no device memory in forward/backward; all scratch lives
+ *    in the caller's workspace.
+ *  - x [N][Cin][H][W]; w_off [Oc][Cin][kh][kw] with Oc = 2*G*kh*kw, channel
+ *    2*(g*kh*kw + k) is dy and 2*(g*kh*kw + k)+1 is dx of tap k = i*kw + j of
+ *    offset group g (channels [g*Cin/G, (g+1)*Cin/G)); b_off [Oc];
+ *    w [Cout][Cin][kh][kw]; b [Cout]; y [N][Cout][Ho][Wo];
+ *    offsets [N][Oc][Ho][Wo] are always fp32.  x, weights, biases, y, dy and
+ *    the gradients have the descriptor's dtype.
+ *  - Ho = (H + 2*pad_h - dil_h*(kh-1) - 1)/stride_h + 1, likewise Wo.
+ *  - Out-of-image corners read zero; a tap whose sample point is not inside
+ *    -1 < py < H, -1 < px < W (or is NaN) reads zero and gets no gradient.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous on that stream; nothing synchronises implicitly.
+ *  - Return 0 on success or a negative DEFT_ERR_* code.  Every argument is
+ *    validated before anything is launched; on error nothing is launched and
+ *    no output is touched.  A plan with N = 0 makes deft_forward,
+ *    deft_backward and deft_debug_sample no-ops that return 0 without
+ *    checking the tensor pointers (an empty batch has none).
+ */
+#ifndef DEFT_H
+#define DEFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum deft_dtype { DEFT_F32 = 0, DEFT_BF16 = 1 };
+
+enum deft_status {
+  DEFT_OK = 0,
+  DEFT_ERR_BAD_DESC = -1,     /* non-positive size, kernel, stride or dilation; negative pad */
+  DEFT_ERR_GROUPS = -2,       /* offset_groups < 1 or Cin not divisible by it */
+  DEFT_ERR_SHAPE = -3,        /* Ho or Wo < 1 */
+  DEFT_ERR_NULLPTR = -4,      /* a required pointer is NULL */
+  DEFT_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than deft_workspace_bytes */
+  DEFT_ERR_DTYPE = -6,        /* dtype not DEFT_F32 / DEFT_BF16 */
+  DEFT_ERR_ALIGN = -7,        /* a device pointer is not 16-byte aligned */
+  DEFT_ERR_HIP = -8,          /* a HIP runtime call or launch failed */
+  DEFT_ERR_PLAN = -9,         /* forced tile/halo/chunk outside the supported range */
+  DEFT_ERR_UNSUPPORTED = -10  /* channels per offset group not a multiple of 16, or size limits */
+};
+
+/* Layer descriptor.  Main-convolution groups are 1; offset_groups = G. */
+typedef struct deft_desc {
+  int n, c_in, h, w, c_out, kh, kw;
+  int stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+  int offset_groups;
+  int dtype; /* enum deft_dtype */
+} deft_desc;
+
+/* Execution plan (opaque): output tile, halo, channel chunk, launch shape. */
+typedef struct deft_plan deft_plan;
+
+typedef struct deft_plan_info {
+  int tile_h, tile_w;     /* output pixels per workgroup tile of the fused kernel */
+  int halo;               /* LDS halo in input pixels around the tile's footprint */
+  int chunk;              /* channels staged per LDS pass */
+  int groups_per_wg;      /* offset groups handled by one workgroup */
+  int num_workgroups;     /* fused-kernel grid size */
+  int ho, wo, oc;
+  int lds_bytes;          /* fused-kernel LDS per workgroup */
+  double est_miss_fraction; /* planner's estimate of taps outside the halo (-1: forced plan) */
+  size_t ws_forward, ws_training;
+  size_t ws_cols_offset;  /* byte offset in the workspace of the deformed columns
+                             [N*Ho*Wo][kh*kw][Cin] that deft_forward leaves there */
+} deft_plan_info;
+
+/* Checks the descriptor alone.  Pure host function. */
+int deft_desc_validate(const deft_desc* d);
+
+/* Builds a plan.  halo_hist (host memory, may be NULL) is the required-halo
+ * histogram of deft_halo_histogram: hist[i] for i < hist_len-2 counts taps
+ * whose corner (y0, x0) lies exactly i pixels (Chebyshev distance) from the
+ * tap's grid position, hist[hist_len-2] counts taps at hist_len-2 or more,
+ * hist[hist_len-1] counts fully outside taps.  NULL selects a default halo of
+ * 2.  The planner sizes the halo so that the expected share of taps outside
+ * it stays small and picks the tile and chunk from the LDS budget and the
+ * launch shape (DefT page, "How DefT works", "The idea": pad each tile by
+ * just enough margin that most sampled pixels stay on chip; "What it costs":
+ * tile sizing depends on platform and layer shape).  Pure host function. */
+int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len,
+                     deft_plan** out);
+
+/* Plan with a forced tile (tile_h*tile_w <= 64), halo (0..32) and channel
+ * chunk (multiple of 16 dividing Cin/G, at most 64; 0 = largest that fits).
+ * DEFT_ERR_PLAN if its LDS does not fit; deft_backward returns DEFT_ERR_PLAN
+ * for a forced plan whose backward tile does not fit even with 8 channels.
+ * Forward results (offsets, columns, y) are bit-identical across plans; the
+ * backward's atomically accumulated sums (dx, dw, dw_off) and the per-chunk
+ * offset-gradient partials agree across plans within rounding. */
+int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo, int chunk,
+                            deft_plan** out);
+
+int deft_plan_get_info(const deft_plan* p, deft_plan_info* info);
+void deft_plan_destroy(deft_plan* p);
+
+/* Workspace bytes for deft_forward (training = 0) or for a forward whose
+ * columns are kept for deft_backward (training = 1). */
+size_t deft_workspace_bytes(const deft_plan* p, int training);
+
+/* Forward.  x, w_off, w, y and workspace are required; b_off and b may be
+ * NULL (zero bias).  offsets_out (fp32 [N][Oc][Ho][Wo]) may be NULL; when
+ * given, the fused kernel also writes the offsets it computed there (needed
+ * by deft_backward).  The deformed columns are left in the workspace. */
+int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
+                 const void* w, const void* b, void* y, float* offsets_out, void* workspace,
+                 size_t ws_bytes, void* stream);
+
+/* Backward of the forward that last ran on this workspace (it must have been
+ * sized with training = 1 and the forward must have written offsets_out,
+ * passed here as `offsets`).  dy [N][Cout][Ho][Wo].  Writes (overwrites) dx,
+ * dw_off, dw; db_off and db may be NULL.  Gradients are accumulated in fp32
+ * and rounded once to the dtype. */
+int deft_backward(const deft_plan* p, const void* x, const void* w_off, const void* w,
+                  const float* offsets, const void* dy, void* workspace, size_t ws_bytes,
+                  void* dx, void* dw_off, void* db_off, void* dw, void* db, void* stream);
+
+/* The integer tap-index / corner-mask stage on its own, from fp32 offsets:
+ * for every (n, g, k, ho, wo), laid out [N][G][kh*kw][Ho][Wo]:
+ * py = float(ho*s - p + i*d) + dy (one fp32 add), px likewise; fully outside
+ * taps give y0 = x0 = 0, mask = 0; otherwise y0 = floor(py), x0 = floor(px)
+ * and mask bit q (q = 0..3 for corners (y0,x0), (y0,x0+1), (y0+1,x0),
+ * (y0+1,x0+1)) is set when that corner is in the image.  Same device code as
+ * the fused kernel. */
+int deft_debug_sample_index(const deft_desc* d, const float* offsets, int32_t* y0, int32_t* x0,
+                            uint8_t* mask, void* stream);
+
+/* The sampling stage alone from given fp32 offsets (unfused path), writing
+ * the deformed columns [N][Ho*Wo][kh*kw][Cin] (tap-major, channel-minor) of
+ * the descriptor's dtype to `cols`. */
+int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, void* cols,
+                      void* stream);
+
+/* Required-halo histogram (device uint32 [hist_len], hist_len >= 3,
+ * overwritten) of fp32 offsets, as described at deft_plan_create. */
+int deft_halo_histogram(const deft_desc* d, const float* offsets, uint32_t* hist, int hist_len,
+                        void* stream);
+
+/* Per-kernel timing for benchmarks (host-side events only; no device memory).
+ * deft_timing_start(capacity) creates `capacity` event pairs for the calling
+ * thread; while active, each kernel that deft_forward / deft_backward /
+ * deft_debug_sample launch on this thread is bracketed by two events recorded
+ * on the call's stream (launches beyond capacity are not recorded).
+ * deft_timing_stop() waits for the last recorded event, computes each
+ * launch's duration and deactivates timing; deft_timing_count and
+ * deft_timing_get(i, &name, &ms) then return the i-th launch's kernel name
+ * (a static string) and milliseconds.  Errors: DEFT_ERR_BAD_DESC for a
+ * capacity < 1 or an index out of range, DEFT_ERR_HIP for event failures. */
+int deft_timing_start(int capacity);
+int deft_timing_stop(void);
+int deft_timing_count(void);
+int deft_timing_get(int i, const char** name, float* ms);
+
+/* Static description of an error code. */
+const char* deft_error_string(int code);
+
+/* Text of the last HIP error seen by this thread, or "" */
+const char* deft_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DEFT_H */

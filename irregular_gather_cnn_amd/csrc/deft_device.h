@@ -1,0 +1,186 @@
+// Device-side building blocks shared by the gfx950 kernels of the deformable
+// convolution library: storage types, bf16 conversion, 32x32 MFMA wrappers
+// and the tap-index stage.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace deft {
+
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values rounded to bf16 (nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+// Element type traits.  VEC = elements per 16-byte chunk.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int VEC = 8;
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// Unpack a 16-byte chunk into 8 floats (bf16) / 4 floats (f32).
+__device__ __forceinline__ void unpack8(const uint4 q, float* f) {
+  f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x); f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
+  f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z); f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+}
+
+// One k-chunk step of a 32x32 output block.  Each lane holds one 16-byte
+// chunk of A (row lane%32) and of B (column lane%32), covering the k values
+// its lane half (lane/32) owns; the two operands use the same k assignment,
+// so the product pairs matching k.  bf16: one 32x32x16 MFMA; f32: four
+// 32x32x2 MFMAs, one per float of the chunk.
+__device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const uint4 a, const uint4 b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const uint4 a, const uint4 b, float) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// Row (within the 32x32 block) of accumulator register r of lane `lane`;
+// the column is lane % 32.
+__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Tap-index stage (fp32).  base_y/base_x: the tap's grid position
+// (ho*s - p + i*d, exact integers).  py = base + dy is one fp32 add.  A tap
+// is fully outside unless -1 < py < H and -1 < px < W (NaN is outside).
+struct TapIndex {
+  int y0, x0;
+  float ly, lx;
+  bool outside;
+};
+__device__ __forceinline__ TapIndex tap_index(int base_y, int base_x, float dy, float dx, int H, int W) {
+  TapIndex t;
+  const float py = __fadd_rn((float)base_y, dy);
+  const float px = __fadd_rn((float)base_x, dx);
+  t.outside = !(py > -1.0f && py < (float)H && px > -1.0f && px < (float)W);
+  if (t.outside) {
+    t.y0 = 0; t.x0 = 0; t.ly = 0.f; t.lx = 0.f;
+  } else {
+    const float fy = floorf(py), fx = floorf(px);
+    t.y0 = (int)fy; t.x0 = (int)fx;
+    t.ly = __fsub_rn(py, fy); t.lx = __fsub_rn(px, fx);
+  }
+  return t;
+}
+__device__ __forceinline__ uint32_t corner_mask(const TapIndex& t, int H, int W) {
+  if (t.outside) return 0u;
+  uint32_t m = 0;
+  if (t.y0 >= 0 && t.x0 >= 0) m |= 1u;
+  if (t.y0 >= 0 && t.x0 + 1 < W) m |= 2u;
+  if (t.y0 + 1 < H && t.x0 >= 0) m |= 4u;
+  if (t.y0 + 1 < H && t.x0 + 1 < W) m |= 8u;
+  return m;
+}
+
+// Bilinear weights of corners (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1);
+// all zero for a fully outside tap.
+__device__ __forceinline__ void tap_weights(const TapIndex& t, float* w) {
+  if (t.outside) { w[0] = w[1] = w[2] = w[3] = 0.f; return; }
+  const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
+  w[0] = hy * hx; w[1] = hy * t.lx; w[2] = t.ly * hx; w[3] = t.ly * t.lx;
+}
+
+// The four-corner blend in a fixed order (every path uses this one).
+__device__ __forceinline__ float blend4(const float* w, float v00, float v01, float v10, float v11) {
+  float a = w[0] * v00;
+  a = __builtin_fmaf(w[1], v01, a);
+  a = __builtin_fmaf(w[2], v10, a);
+  a = __builtin_fmaf(w[3], v11, a);
+  return a;
+}
+
+// XCD-aware workgroup order: gfx950 dispatches consecutive workgroup ids
+// round-robin over its 8 XCDs.  This maps the hardware id to a logical id
+// such that each XCD receives a contiguous range of logical ids (bijective
+// for any grid size), so neighbouring tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_swizzle(int wg, int num_wg) {
+  const int q = num_wg >> 3, r = num_wg & 7;
+  const int xcd = wg & 7, slot = wg >> 3;
+  return xcd * q + (xcd < r ? xcd : r) + slot;
+}
+
+// Division by an invariant positive integer d: q = (umulhi(x, m) + x) >> s,
+// exact for 0 <= x < 2^31 (round-up multiplier method).
+struct FastDiv {
+  uint32_t m, s;
+};
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, l};
+}
+__device__ __forceinline__ int fdiv(int x, FastDiv f) {
+  const uint32_t t = __umulhi((uint32_t)x, f.m);
+  return (int)((t + (uint32_t)x) >> f.s);
+}
+
+template <typename T> __device__ __forceinline__ T zero_elem() { return T(0); }
+
+// Copies channels [c0, c0+nc) of image n of x [N][Cin][H][W] over input rows
+// [ry0, ry0+RH) and columns [rx0, rx0+RW) into LDS as [row][col][channel]
+// with pixel stride pstr (elements); locations outside the image are zero.
+// drw/drh divide by RW/RH.  Called by all 256 threads of the workgroup.
+template <typename T>
+__device__ __forceinline__ void stage_region_hwc(T* dst, const T* __restrict__ x, int Cin, int H, int W,
+                                                 int n, int c0, int nc, int ry0, int rx0, int RH, int RW,
+                                                 FastDiv drw, FastDiv drh, int pstr) {
+  const int total = nc * RH * RW;
+  const T* xb = x + ((size_t)n * Cin + c0) * H * W;
+  for (int e = threadIdx.x; e < total; e += 256) {
+    const int r1 = fdiv(e, drw);
+    const int rx = e - r1 * RW;
+    const int c = fdiv(r1, drh);
+    const int ry = r1 - c * RH;
+    const int y = ry0 + ry, xx = rx0 + rx;
+    T v = zero_elem<T>();
+    if ((unsigned)y < (unsigned)H && (unsigned)xx < (unsigned)W) v = xb[((size_t)c * H + y) * W + xx];
+    dst[(ry * RW + rx) * pstr + c] = v;
+  }
+}
+
+// 8 consecutive channels at one LDS pixel, as floats.
+__device__ __forceinline__ void lds_read8(const bf16_t* src, float* f) { unpack8(*(const uint4*)src, f); }
+__device__ __forceinline__ void lds_read8(const float* src, float* f) {
+  const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t* src, float* f) { unpack8(*(const uint4*)src, f); }
+__device__ __forceinline__ void load8(const float* src, float* f) { lds_read8(src, f); }
+__device__ __forceinline__ void store8(bf16_t* dst, const float* f) {
+  uint4 q;
+  q.x = pack_bf16x2(f[0], f[1]); q.y = pack_bf16x2(f[2], f[3]);
+  q.z = pack_bf16x2(f[4], f[5]); q.w = pack_bf16x2(f[6], f[7]);
+  *(uint4*)dst = q;
+}
+__device__ __forceinline__ void store8(float* dst, const float* f) {
+  *(float4*)dst = make_float4(f[0], f[1], f[2], f[3]);
+  *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+}  // namespace deft

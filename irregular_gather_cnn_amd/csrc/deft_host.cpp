@@ -1,0 +1,434 @@
+// C ABI of the deformable convolution library: descriptor validation, the
+// tile planner, workspace layout and launch sequencing.  Everything here runs
+// on the host; kernels live in deft_sample.hip, deft_gemm.hip and
+// deft_backward.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "deft.h"
+#include "deft_internal.h"
+
+namespace {
+
+thread_local char g_last_hip[256] = "";
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_last_hip, sizeof(g_last_hip), "%s (%d)", hipGetErrorString(e), (int)e);
+  return DEFT_ERR_HIP;
+}
+
+constexpr int kMaxLds = 160 * 1024;     // gfx950 LDS per workgroup
+constexpr int kTargetLds = 64 * 1024;   // keeps >= 2 workgroups per CU
+constexpr int kNumCUs = 256;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+int align16(int v) { return (v + 15) & ~15; }
+
+int out_dim(int in, int k, int s, int p, int d) { return (in + 2 * p - d * (k - 1) - 1) / s + 1; }
+
+int validate(const deft_desc* d) {
+  if (!d) return DEFT_ERR_NULLPTR;
+  if (d->dtype != DEFT_F32 && d->dtype != DEFT_BF16) return DEFT_ERR_DTYPE;
+  if (d->n < 0 || d->c_in < 1 || d->h < 1 || d->w < 1 || d->c_out < 1 || d->kh < 1 || d->kw < 1 ||
+      d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1 || d->pad_h < 0 || d->pad_w < 0)
+    return DEFT_ERR_BAD_DESC;
+  if (d->offset_groups < 1 || d->c_in % d->offset_groups != 0) return DEFT_ERR_GROUPS;
+  if (out_dim(d->h, d->kh, d->stride_h, d->pad_h, d->dil_h) < 1 ||
+      out_dim(d->w, d->kw, d->stride_w, d->pad_w, d->dil_w) < 1)
+    return DEFT_ERR_SHAPE;
+  if ((d->c_in / d->offset_groups) % 16 != 0) return DEFT_ERR_UNSUPPORTED;
+  if (d->h >= 32767 || d->w >= 32767 || d->kh * d->kw > 48) return DEFT_ERR_UNSUPPORTED;
+  const double x_elems = (double)d->n * d->c_in * d->h * d->w;
+  const double col_elems = (double)d->n * out_dim(d->h, d->kh, d->stride_h, d->pad_h, d->dil_h) *
+                           out_dim(d->w, d->kw, d->stride_w, d->pad_w, d->dil_w) * d->c_in * d->kh * d->kw;
+  if (x_elems >= 2147483647.0 || (double)d->n * d->c_out * d->h * d->w >= 2147483647.0 ||
+      col_elems / (d->c_in * d->kh * d->kw) >= 2147483647.0)
+    return DEFT_ERR_UNSUPPORTED;
+  return DEFT_OK;
+}
+
+struct Shape {
+  int ho, wo, taps, oc, cg, ck, esz;
+};
+Shape shape_of(const deft_desc& d) {
+  Shape s;
+  s.ho = out_dim(d.h, d.kh, d.stride_h, d.pad_h, d.dil_h);
+  s.wo = out_dim(d.w, d.kw, d.stride_w, d.pad_w, d.dil_w);
+  s.taps = d.kh * d.kw;
+  s.oc = 2 * d.offset_groups * s.taps;
+  s.cg = d.c_in / d.offset_groups;
+  s.ck = d.c_in * s.taps;
+  s.esz = d.dtype == DEFT_BF16 ? 2 : 4;
+  return s;
+}
+
+// Fills every derived field of a plan for the given tile / halo / chunk.
+// Returns false if the LDS does not fit.
+bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
+  const deft_desc& d = p.d;
+  const Shape s = shape_of(d);
+  p.ho = s.ho; p.wo = s.wo; p.taps = s.taps; p.oc = s.oc; p.cg = s.cg; p.ck = s.ck;
+  p.tile_h = th; p.tile_w = tw; p.halo = halo; p.chunk = chunk;
+  p.chunk_a = d.c_in % 64 == 0 ? 64 : (d.c_in % 32 == 0 ? 32 : 16);
+  p.gw = 1;
+  p.gsplit = d.offset_groups / p.gw;
+  p.tiles_h = (s.ho + th - 1) / th;
+  p.tiles_w = (s.wo + tw - 1) / tw;
+  p.num_tiles = d.n * p.tiles_h * p.tiles_w;
+  p.num_wg = p.num_tiles * p.gsplit;
+  const int ocw = 2 * p.gw * s.taps;
+  p.mblocks = (ocw + 31) / 32;
+  p.oc_pad = (s.oc + 31) / 32 * 32 + 32;
+  p.foot_h = (th - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
+  p.foot_w = (tw - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;
+  p.reg_h = std::min(p.foot_h + 2 * halo + 1, d.h + 2);
+  p.reg_w = std::min(p.foot_w + 2 * halo + 1, d.w + 2);
+  const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
+  p.pstr = chunk + vec;
+  p.pstr_a = p.chunk_a + vec;
+  const int pt = th * tw;
+  const int region = std::max({p.foot_h * p.foot_w * p.pstr_a * s.esz, p.reg_h * p.reg_w * p.pstr * s.esz,
+                               4 * ocw * pt * 4});
+  p.lds_region = 0;
+  p.lds_off = align16(region);
+  p.lds_info = p.lds_off + align16(ocw * pt * 4);
+  p.lds_total = p.lds_info + p.gw * s.taps * pt * 16;
+  if (p.lds_total > kMaxLds) return false;
+  // backward sampling kernel: its own chunk (<= 32), shrunk until the LDS
+  // fits; chunk_b = 0 marks a plan whose backward does not fit.
+  p.chunk_b = 0;
+  for (int cb = std::min(chunk, 32); cb >= 8; cb /= 2) {
+    if (s.cg % cb) continue;
+    p.chunk_b = cb;
+    p.pstr_b = cb + vec;
+    p.dstr_b = cb + 1;
+    p.lb_x = 0;
+    p.lb_dx = align16(p.reg_h * p.reg_w * p.pstr_b * s.esz);
+    p.lb_off = p.lb_dx + align16(p.reg_h * p.reg_w * p.dstr_b * 4);
+    p.lb_info = p.lb_off + align16(ocw * pt * 4);
+    p.lb_doff = p.lb_info + p.gw * s.taps * pt * 16;
+    p.lb_total = p.lb_doff + p.gw * s.taps * pt * 8;
+    if (p.lb_total <= kMaxLds) break;
+    p.chunk_b = 0;
+  }
+  // workspace
+  const size_t P = (size_t)d.n * s.ho * s.wo;
+  p.kk_pad = (s.oc * s.taps + 15) / 16 * 16;
+  size_t o = 0;
+  p.ws_wt = o; o = align256(o + (size_t)d.c_out * s.ck * s.esz);
+  p.ws_woff = o; o = align256(o + (size_t)p.oc_pad * s.ck * s.esz);
+  p.ws_cols = o; o = align256(o + P * s.ck * s.esz);
+  p.ws_fwd_end = o;
+  p.ws_w2 = o; o = align256(o + (size_t)s.ck * d.c_out * s.esz);
+  p.ws_wofft = o; o = align256(o + (size_t)d.c_in * p.kk_pad * s.esz);
+  p.ws_dcol = o; o = align256(o + P * s.ck * s.esz);
+  p.ws_dx32 = o; o = align256(o + (size_t)d.n * d.c_in * d.h * d.w * 4);
+  p.ws_dw32 = o; o = align256(o + (size_t)d.c_out * s.ck * 4);
+  p.ws_dwoff32 = o; o = align256(o + (size_t)s.oc * s.ck * 4);
+  p.ws_doff = o; o = align256(o + P * s.oc * 4);
+  p.ws_train_end = o;
+  return true;
+}
+
+// Share of (not fully outside) taps whose corner lies beyond `halo` pixels.
+double miss_fraction(const uint32_t* hist, int len, int halo) {
+  if (!hist || len < 3) return halo >= 2 ? 0.01 : (halo == 1 ? 0.3 : 0.7);
+  double in = 0, tot = 0;
+  for (int i = 0; i < len - 1; ++i) {
+    tot += hist[i];
+    if (i <= halo && i < len - 2) in += hist[i];
+  }
+  return tot > 0 ? 1.0 - in / tot : 0.0;
+}
+
+// Planner: pick (tile, halo, chunk) minimising a byte-cost estimate of the
+// fused kernel: the columns it must write, the input staged into LDS (served
+// mostly from L2, weighted down), and the taps outside the halo, each of which
+// reads four corners per channel from global memory uncoalesced (weighted up),
+// divided by the fraction of the machine the launch keeps busy.
+int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len) {
+  const Shape s = shape_of(d);
+  static const int tiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}, {4, 4}, {2, 16}, {16, 2}, {2, 8}, {1, 16}};
+  double best_cost = 1e300;
+  bool found = false;
+  const double samples = (double)d.n * s.ho * s.wo * s.taps * d.c_in;
+  const double col_bytes = samples * s.esz;
+  for (auto& t : tiles) {
+    for (int halo = 0; halo <= 16; ++halo) {
+      for (int chunk = 64; chunk >= 16; chunk /= 2) {
+        if (s.cg % chunk) continue;
+        deft_plan p;
+        p.d = d;
+        if (!layout_plan(p, t[0], t[1], halo, chunk) || p.chunk_b == 0) continue;
+        const double miss = miss_fraction(hist, hist_len, halo);
+        const double pt = (double)t[0] * t[1];
+        const double per_tile_stage = (double)p.reg_h * p.reg_w * s.cg + (double)p.foot_h * p.foot_w * d.c_in;
+        const double stage_bytes = (double)p.num_wg * per_tile_stage * s.esz;
+        const double miss_bytes = miss * samples * 4.0 * s.esz * 8.0;
+        const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
+        const double slots = (double)kNumCUs * occ;
+        const double waves = std::ceil(p.num_wg / slots);
+        const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
+        double cost = (col_bytes + 0.25 * stage_bytes + miss_bytes) / std::max(busy, 0.05);
+        if (p.lds_total > kTargetLds) cost *= 1.15;
+        if (pt < 32) cost *= 1.1;  // phase-A MFMA blocks half empty
+        if (cost < best_cost * 0.999) {
+          best_cost = cost;
+          best = p;
+          best.est_miss = miss;
+          found = true;
+        }
+      }
+    }
+  }
+  return found ? DEFT_OK : DEFT_ERR_UNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Timing {
+  bool active = false;
+  int used = 0;
+  std::vector<hipEvent_t> ev;       // 2 per launch
+  std::vector<const char*> names;
+  std::vector<float> ms;
+  // events are not destroyed at thread exit: that may run after the HIP
+  // runtime has shut down; the process releases them
+};
+thread_local Timing g_timing;
+
+}  // namespace
+
+namespace deft {
+void timing_before(hipStream_t s, const char* name) {
+  Timing& t = g_timing;
+  if (!t.active || 2 * (size_t)t.used + 1 >= t.ev.size()) return;
+  t.names[t.used] = name;
+  (void)hipEventRecord(t.ev[2 * t.used], s);
+}
+void timing_after(hipStream_t s) {
+  Timing& t = g_timing;
+  if (!t.active || 2 * (size_t)t.used + 1 >= t.ev.size()) return;
+  (void)hipEventRecord(t.ev[2 * t.used + 1], s);
+  ++t.used;
+}
+}  // namespace deft
+
+extern "C" {
+
+int deft_desc_validate(const deft_desc* d) { return validate(d); }
+
+int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len, deft_plan** out) {
+  if (!out) return DEFT_ERR_NULLPTR;
+  const int v = validate(d);
+  if (v) return v;
+  deft_plan* p = new (std::nothrow) deft_plan();
+  if (!p) return DEFT_ERR_UNSUPPORTED;
+  const int r = plan_auto(*p, *d, halo_hist, halo_hist ? hist_len : 0);
+  if (r) {
+    delete p;
+    return r;
+  }
+  *out = p;
+  return DEFT_OK;
+}
+
+int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo, int chunk, deft_plan** out) {
+  if (!out) return DEFT_ERR_NULLPTR;
+  const int v = validate(d);
+  if (v) return v;
+  const Shape s = shape_of(*d);
+  if (tile_h < 1 || tile_w < 1 || tile_h * tile_w > 64 || halo < 0 || halo > 32) return DEFT_ERR_PLAN;
+  if (chunk != 0 && (chunk < 16 || chunk > 64 || chunk % 16 || s.cg % chunk)) return DEFT_ERR_PLAN;
+  deft_plan* p = new (std::nothrow) deft_plan();
+  if (!p) return DEFT_ERR_UNSUPPORTED;
+  p->d = *d;
+  bool ok = false;
+  if (chunk != 0) {
+    ok = layout_plan(*p, tile_h, tile_w, halo, chunk);
+  } else {
+    for (int c = 64; c >= 16 && !ok; c /= 2)
+      if (s.cg % c == 0) ok = layout_plan(*p, tile_h, tile_w, halo, c);
+  }
+  if (!ok) {
+    delete p;
+    return DEFT_ERR_PLAN;
+  }
+  p->est_miss = -1.0;
+  *out = p;
+  return DEFT_OK;
+}
+
+int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
+  if (!p || !info) return DEFT_ERR_NULLPTR;
+  info->tile_h = p->tile_h; info->tile_w = p->tile_w; info->halo = p->halo; info->chunk = p->chunk;
+  info->groups_per_wg = p->gw; info->num_workgroups = p->num_wg;
+  info->ho = p->ho; info->wo = p->wo; info->oc = p->oc;
+  info->lds_bytes = p->lds_total;
+  info->est_miss_fraction = p->est_miss;
+  info->ws_forward = p->ws_fwd_end;
+  info->ws_training = p->ws_train_end;
+  info->ws_cols_offset = p->ws_cols;
+  return DEFT_OK;
+}
+
+void deft_plan_destroy(deft_plan* p) { delete p; }
+
+size_t deft_workspace_bytes(const deft_plan* p, int training) {
+  if (!p) return 0;
+  return training ? p->ws_train_end : p->ws_fwd_end;
+}
+
+int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
+                 const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!p) return DEFT_ERR_NULLPTR;
+  if (p->d.n == 0) return DEFT_OK;  // empty batch: nothing is read or written
+  if (!x || !w_off || !w || !y) return DEFT_ERR_NULLPTR;
+  if (!workspace || ws_bytes < p->ws_fwd_end) return DEFT_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_off) || !aligned16(w) || !aligned16(y) || !aligned16(workspace) ||
+      (offsets_out && !aligned16(offsets_out)))
+    return DEFT_ERR_ALIGN;
+  const size_t esz = p->d.dtype == DEFT_BF16 ? 2 : 4;
+  if (((uintptr_t)b_off % esz) || ((uintptr_t)b % esz)) return DEFT_ERR_ALIGN;
+  if (p->d.n == 0) return DEFT_OK;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e = deft::launch_prep_forward(*p, w, w_off, ws + p->ws_wt, ws + p->ws_woff, st);
+  if (e != hipSuccess) return hip_fail(e);
+  deft::SampleArgs a;
+  a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_in = nullptr; a.off_out = offsets_out;
+  a.cols = ws + p->ws_cols;
+  e = deft::launch_sample(*p, true, a, st);
+  if (e != hipSuccess) return hip_fail(e);
+  e = deft::launch_gemm_forward(*p, ws + p->ws_wt, ws + p->ws_cols, b, y, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return DEFT_OK;
+}
+
+int deft_backward(const deft_plan* p, const void* x, const void* w_off, const void* w, const float* offsets,
+                  const void* dy, void* workspace, size_t ws_bytes, void* dx, void* dw_off, void* db_off, void* dw,
+                  void* db, void* stream) {
+  if (!p) return DEFT_ERR_NULLPTR;
+  if (p->d.n == 0) return DEFT_OK;  // empty batch
+  if (!x || !w_off || !w || !offsets || !dy || !dx || !dw_off || !dw) return DEFT_ERR_NULLPTR;
+  if (!workspace || ws_bytes < p->ws_train_end) return DEFT_ERR_WORKSPACE;
+  if (p->chunk_b == 0) return DEFT_ERR_PLAN;
+  if (!aligned16(x) || !aligned16(w_off) || !aligned16(w) || !aligned16(offsets) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(dw_off) || !aligned16(dw) || !aligned16(workspace))
+    return DEFT_ERR_ALIGN;
+  const size_t esz = p->d.dtype == DEFT_BF16 ? 2 : 4;
+  if (((uintptr_t)db_off % esz) || ((uintptr_t)db % esz)) return DEFT_ERR_ALIGN;
+  if (p->d.n == 0) return DEFT_OK;
+  deft::BackwardArgs a;
+  a.x = x; a.w_off = w_off; a.w = w; a.offsets = offsets; a.dy = dy; a.dx = dx; a.dw_off = dw_off;
+  a.db_off = db_off; a.dw = dw; a.db = db; a.ws = (char*)workspace;
+  const hipError_t e = deft::launch_backward(*p, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DEFT_OK;
+}
+
+int deft_debug_sample_index(const deft_desc* d, const float* offsets, int32_t* y0, int32_t* x0, uint8_t* mask,
+                            void* stream) {
+  const int v = validate(d);
+  if (v) return v;
+  if (!offsets || !y0 || !x0 || !mask) return DEFT_ERR_NULLPTR;
+  if (((uintptr_t)offsets & 3u) || ((uintptr_t)y0 & 3u) || ((uintptr_t)x0 & 3u)) return DEFT_ERR_ALIGN;
+  const Shape s = shape_of(*d);
+  const hipError_t e = deft::launch_sample_index(*d, s.ho, s.wo, offsets, y0, x0, mask, (hipStream_t)stream);
+  return e == hipSuccess ? DEFT_OK : hip_fail(e);
+}
+
+int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, void* cols, void* stream) {
+  if (!p) return DEFT_ERR_NULLPTR;
+  if (p->d.n == 0) return DEFT_OK;
+  if (!x || !offsets || !cols) return DEFT_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(cols) || ((uintptr_t)offsets & 3u)) return DEFT_ERR_ALIGN;
+  if (p->d.n == 0) return DEFT_OK;
+  deft::SampleArgs a;
+  a.x = x; a.woff_p = nullptr; a.b_off = nullptr; a.off_in = offsets; a.off_out = nullptr; a.cols = cols;
+  const hipError_t e = deft::launch_sample(*p, false, a, (hipStream_t)stream);
+  return e == hipSuccess ? DEFT_OK : hip_fail(e);
+}
+
+int deft_halo_histogram(const deft_desc* d, const float* offsets, uint32_t* hist, int hist_len, void* stream) {
+  const int v = validate(d);
+  if (v) return v;
+  if (!offsets || !hist) return DEFT_ERR_NULLPTR;
+  if (hist_len < 3 || hist_len > 64) return DEFT_ERR_BAD_DESC;
+  if (((uintptr_t)offsets & 3u) || ((uintptr_t)hist & 3u)) return DEFT_ERR_ALIGN;
+  const Shape s = shape_of(*d);
+  const hipError_t e = deft::launch_halo_hist(*d, s.ho, s.wo, offsets, hist, hist_len, (hipStream_t)stream);
+  return e == hipSuccess ? DEFT_OK : hip_fail(e);
+}
+
+int deft_timing_start(int capacity) {
+  if (capacity < 1) return DEFT_ERR_BAD_DESC;
+  Timing& t = g_timing;
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& e : t.ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      t.ev.clear();
+      t.active = false;
+      return hip_fail(r);
+    }
+  }
+  t.names.assign(capacity, "");
+  t.ms.clear();
+  t.used = 0;
+  t.active = true;
+  return DEFT_OK;
+}
+
+int deft_timing_stop(void) {
+  Timing& t = g_timing;
+  t.active = false;
+  t.ms.assign(t.used, 0.f);
+  if (t.used == 0) return DEFT_OK;
+  hipError_t r = hipEventSynchronize(t.ev[2 * t.used - 1]);
+  if (r != hipSuccess) return hip_fail(r);
+  for (int i = 0; i < t.used; ++i) {
+    r = hipEventElapsedTime(&t.ms[i], t.ev[2 * i], t.ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_fail(r);
+  }
+  return DEFT_OK;
+}
+
+int deft_timing_count(void) { return (int)g_timing.ms.size(); }
+
+int deft_timing_get(int i, const char** name, float* ms) {
+  const Timing& t = g_timing;
+  if (i < 0 || i >= (int)t.ms.size()) return DEFT_ERR_BAD_DESC;
+  if (name) *name = t.names[i];
+  if (ms) *ms = t.ms[i];
+  return DEFT_OK;
+}
+
+const char* deft_error_string(int code) {
+  switch (code) {
+    case DEFT_OK: return "ok";
+    case DEFT_ERR_BAD_DESC: return "invalid descriptor (sizes, kernel, stride, dilation or padding)";
+    case DEFT_ERR_GROUPS: return "offset_groups must be >= 1 and divide c_in";
+    case DEFT_ERR_SHAPE: return "output height or width is < 1";
+    case DEFT_ERR_NULLPTR: return "a required pointer is NULL";
+    case DEFT_ERR_WORKSPACE: return "workspace missing or smaller than deft_workspace_bytes";
+    case DEFT_ERR_DTYPE: return "dtype must be DEFT_F32 or DEFT_BF16";
+    case DEFT_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case DEFT_ERR_HIP: return "HIP runtime error (see deft_last_hip_error)";
+    case DEFT_ERR_PLAN: return "forced tile/halo/chunk outside the supported range";
+    case DEFT_ERR_UNSUPPORTED: return "unsupported shape (channels per offset group must be a multiple of 16)";
+    default: return "unknown error";
+  }
+}
+
+const char* deft_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Host-side internals of the deformable convolution library: the plan and
+// the launchers each kernel file exports to deft_host.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "deft.h"
+
+struct deft_plan {
+  deft_desc d;
+  int ho, wo, oc, taps, ck, cg;
+  // fused sampling kernel
+  int tile_h, tile_w, halo, chunk, chunk_a, gw, gsplit;
+  int tiles_h, tiles_w, num_tiles, num_wg, mblocks;
+  int foot_h, foot_w;          // nominal tile footprint (input pixels)
+  int reg_h, reg_w;            // largest halo region (input pixels)
+  int pstr, pstr_a;            // LDS pixel strides (elements)
+  int lds_region, lds_off, lds_info, lds_total;  // byte offsets / total
+  int oc_pad;                  // rows of the prepared offset-conv weight
+  double est_miss;
+  // workspace layout (byte offsets, 256-aligned)
+  size_t ws_wt, ws_woff, ws_cols, ws_fwd_end;
+  size_t ws_w2, ws_dcol, ws_dx32, ws_dw32, ws_dwoff32, ws_doff, ws_wofft, ws_train_end;
+  int kk_pad;                  // padded (o, tap) depth of the transposed offset conv
+  // sampling backward (same tiles, its own channel chunk)
+  int chunk_b, pstr_b, dstr_b;
+  int lb_x, lb_dx, lb_off, lb_info, lb_doff, lb_total;
+};
+
+namespace deft {
+
+// Timing hook (deft_timing_start): brackets a launch with events when active.
+void timing_before(hipStream_t s, const char* name);
+void timing_after(hipStream_t s);
+
+#define DEFT_LAUNCH(name, kernel, grid, block, lds, stream, ...)               \
+  do {                                                                        \
+    ::deft::timing_before((stream), (name));                                  \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);        \
+    ::deft::timing_after((stream));                                           \
+  } while (0)
+
+struct SampleArgs {
+  const void* x;
+  const void* woff_p;      // prepared offset-conv weight [oc_pad][taps][Cin]
+  const void* b_off;       // nullable, dtype
+  const float* off_in;     // unfused: offsets to sample from
+  float* off_out;          // nullable
+  void* cols;              // [N*Ho*Wo][taps][Cin]
+};
+
+hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt,
+                               void* woff_p, hipStream_t s);
+hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hipStream_t s);
+hipError_t launch_sample_index(const deft_desc& d, int ho, int wo, const float* off, int32_t* y0,
+                               int32_t* x0, uint8_t* mask, hipStream_t s);
+hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off, uint32_t* hist,
+                            int hist_len, hipStream_t s);
+
+hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b,
+                               void* y, hipStream_t s);
+
+struct BackwardArgs {
+  const void* x;
+  const void* w_off;
+  const void* w;
+  const float* offsets;
+  const void* dy;
+  void* dx;
+  void* dw_off;
+  void* db_off;
+  void* dw;
+  void* db;
+  char* ws;
+};
+hipError_t launch_backward(const deft_plan& p, const BackwardArgs& a, hipStream_t s);
+
+}  // namespace deft

@@ -95,11 +95,18 @@ def _load():
         lib.oracle_forward.argtypes = [desc, dp, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_backward.argtypes = [desc, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_sample_index_f32.argtypes = [desc, vp, vp, vp, vp]
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         for f in (lib.oracle_offset_conv, lib.oracle_sample_cols, lib.oracle_main_conv,
                   lib.oracle_forward, lib.oracle_backward, lib.oracle_sample_index_f32):
             f.restype = None
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().oracle_threads())
 
 
 def _d(a, shape=None):

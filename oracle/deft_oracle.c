@@ -34,6 +34,7 @@
  * y [N][Cout][Ho][Wo].
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -50,6 +51,9 @@ static int out_h(const odesc* d) {
 static int out_w(const odesc* d) {
   return (d->w + 2 * d->pad_w - d->dil_w * (d->kw - 1) - 1) / d->stride_w + 1;
 }
+
+/* Threads the OpenMP loops below use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 int oracle_out_hw(const odesc* d, int* ho, int* wo) {
   *ho = out_h(d);

@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/deft.h declares, and every validation error is returned before any
+launch (so fake, never-dereferenced pointers are safe here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from irregular_gather_cnn_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "deft.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(deft_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTED) == names
+
+
+def desc(**kw):
+    base = dict(n=2, c_in=32, h=9, w=11, c_out=8, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1), groups=1,
+                dtype=L.DEFT_BF16)
+    base.update(kw)
+    return L.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(dtype=7), -6),
+    (dict(c_in=0), -1),
+    (dict(h=0), -1),
+    (dict(stride=(0, 1)), -1),
+    (dict(dil=(1, 0)), -1),
+    (dict(pad=(-1, 0)), -1),
+    (dict(kh=0), -1),
+    (dict(groups=0), -2),
+    (dict(groups=3), -2),
+    (dict(h=2, pad=(0, 0)), -3),
+    (dict(c_in=24), -10),
+    (dict(c_in=32, groups=4), -10),
+    (dict(n=0), 0),
+])
+def test_descriptor_validation(kw, code):
+    assert L.deft_desc_validate(desc(**kw)) == code
+
+
+def test_plan_and_workspace_sizes():
+    d = desc()
+    p = L.deft_plan_create(d)
+    info = L.deft_plan_get_info(p)
+    assert info["ho"] == 9 and info["wo"] == 11 and info["oc"] == 18
+    assert info["halo"] == 2  # default without a histogram
+    cols = 2 * 9 * 11 * 9 * 32 * 2
+    assert info["ws_forward"] >= cols and info["ws_training"] >= info["ws_forward"] + cols
+    assert L.deft_workspace_bytes(p, 0) == info["ws_forward"]
+    assert L.deft_workspace_bytes(p, 1) == info["ws_training"]
+    assert info["ws_cols_offset"] % 256 == 0 and info["ws_cols_offset"] + cols <= info["ws_forward"]
+    L.deft_plan_destroy(p)
+
+
+def test_planner_sizes_halo_from_histogram():
+    d = desc(n=16, c_in=256, h=56, w=56, c_out=256)
+    tight = [900, 90, 9, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0]
+    wide = [100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 100, 0]
+    pt = L.deft_plan_get_info(L.deft_plan_create(d, tight))
+    pw = L.deft_plan_get_info(L.deft_plan_create(d, wide))
+    assert pt["halo"] <= 3
+    assert pw["halo"] > pt["halo"]
+    assert pt["est_miss_fraction"] < 0.01
+
+
+def test_forced_plan_limits():
+    d = desc()
+    with pytest.raises(L.DeftError) as e:
+        L.deft_plan_create_forced(d, 16, 8, 2, 0)
+    assert e.value.code == -9
+    with pytest.raises(L.DeftError):
+        L.deft_plan_create_forced(d, 8, 8, 2, 48)
+    p = L.deft_plan_create_forced(d, 8, 8, 0, 16)
+    info = L.deft_plan_get_info(p)
+    assert (info["tile_h"], info["tile_w"], info["halo"], info["chunk"]) == (8, 8, 0, 16)
+
+
+FAKE = 1 << 40  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def test_forward_validation_before_launch():
+    d = desc()
+    p = L.deft_plan_create(d)
+    ws = L.deft_workspace_bytes(p, 0)
+    lib = L.load()
+    ok = [p, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, ws, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.deft_forward(*a)
+
+    assert call(1, None) == -4   # x
+    assert call(2, None) == -4   # w_off
+    assert call(4, None) == -4   # w
+    assert call(6, None) == -4   # y
+    assert call(8, None) == -5   # workspace
+    assert call(9, ws - 1) == -5  # too small
+    assert call(1, FAKE + 8) == -7  # misaligned x
+    assert call(7, FAKE + 4) == -7  # misaligned offsets_out
+    assert call(3, FAKE + 1) == -7  # bias not element aligned
+    assert lib.deft_forward(None, *ok[1:]) == -4
+
+
+def test_empty_batch_is_a_no_op():
+    d = desc(n=0)
+    p = L.deft_plan_create(d)
+    lib = L.load()
+    assert lib.deft_forward(p, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.deft_backward(p, *([None] * 6), 0, *([None] * 6)) == 0
+    assert lib.deft_debug_sample(p, None, None, None, None) == 0
+
+
+def test_backward_validation_before_launch():
+    d = desc()
+    p = L.deft_plan_create(d)
+    ws = L.deft_workspace_bytes(p, 1)
+    lib = L.load()
+    ok = [p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, FAKE, None, FAKE, None, None]
+    for i in (1, 2, 3, 4, 5, 8, 9, 11):
+        a = list(ok)
+        a[i] = None
+        assert lib.deft_backward(*a) == -4, i
+    a = list(ok)
+    a[7] = L.deft_workspace_bytes(p, 0)
+    assert lib.deft_backward(*a) == -5
+    a = list(ok)
+    a[8] = FAKE + 2
+    assert lib.deft_backward(*a) == -7
+
+
+def test_other_entry_points_validate():
+    lib = L.load()
+    d = desc()
+    assert lib.deft_debug_sample_index(ctypes.byref(d), None, FAKE, FAKE, FAKE, None) == -4
+    assert lib.deft_halo_histogram(ctypes.byref(d), FAKE, FAKE, 2, None) == -1
+    assert lib.deft_halo_histogram(ctypes.byref(d), FAKE, None, 16, None) == -4
+    bad = desc(groups=3)
+    assert lib.deft_debug_sample_index(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == -2
+    p = L.deft_plan_create(d)
+    assert lib.deft_debug_sample(p, FAKE, FAKE, None, None) == -4
+
+
+def test_error_strings():
+    for code in range(-10, 1):
+        s = L.deft_error_string(code)
+        assert s and s != "unknown error"
+    assert L.deft_error_string(-99) == "unknown error"
+    assert L.deft_last_hip_error() == ""

@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (rel-L2 per output tensor): 1e-5 for fp32 workloads, 2e-2 for bf16
+inputs with fp32 accumulation; the integer tap-index / corner-mask stage is
+bit-exact; forward results are bit-identical across plans and between the
+fused and the unfused sampling paths.  The oracle always receives the same
+(bf16-rounded) input values; where a check isolates a later stage it also
+receives the GPU's fp32 offsets, so offset rounding does not blur it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from irregular_gather_cnn_amd import _lib as L
+from irregular_gather_cnn_amd.layer import DeformConv, halo_histogram, index_stage
+from irregular_gather_cnn_amd.synth import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b.ravel())
+    return float(np.linalg.norm((a - b).ravel()) / (nb if nb > 0 else 1.0))
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(
+        torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def shape_of(wl):
+    return oracle.Shape(wl.n, wl.c_in, wl.h, wl.w, wl.c_out, wl.kh, wl.kw, (wl.stride,) * 2, (wl.pad,) * 2,
+                        (wl.dil,) * 2, wl.groups)
+
+
+def make_layer(wl, plan=None, training=False):
+    return DeformConv(wl.n, wl.c_in, wl.h, wl.w, wl.c_out, wl.kh, wl.kw, (wl.stride,) * 2, (wl.pad,) * 2,
+                      (wl.dil,) * 2, wl.groups, wl.dtype, plan=plan, training=training)
+
+
+def cols_to_oracle_layout(cols, wl):
+    """[N][P][taps][Cin] (library) -> [N][P][Cin][taps] (oracle)."""
+    return np.transpose(cols, (0, 1, 3, 2))
+
+
+def image_shape(wl, n):
+    return oracle.Shape(n, wl.c_in, wl.h, wl.w, wl.c_out, wl.kh, wl.kw, (wl.stride,) * 2, (wl.pad,) * 2,
+                        (wl.dil,) * 2, wl.groups)
+
+
+# --- forward, every workload at its full size -----------------------------------
+
+FWD = ["tiny_fp32_n1_c16_16x16", "fp32_n8_c128_64x64", "bf16_n16_c256_56x56", "bf16_n16_c512_28x28_g4_wide"]
+
+
+@pytest.mark.parametrize("name", FWD)
+def test_forward_matches_oracle(name):
+    wl = WORKLOADS[name]
+    say("forward parity", name)
+    inp = make_inputs(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl)
+    y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    cols = layer.cols_view()
+    torch.cuda.synchronize()
+    # images checked against the oracle: all for small workloads, first/last otherwise
+    imgs = list(range(wl.n)) if wl.n * wl.c_in * wl.h * wl.w <= 8 * 128 * 64 * 64 else [0, wl.n - 1]
+    s1 = image_shape(wl, 1)
+    y_h, off_h = host(y), host(off)
+    cols_h = host(cols)
+    tol = TOL[wl.dtype]
+    for n in imgs:
+        xs = inp["x"][n:n + 1]
+        y_ref, off_ref = oracle.forward(s1, xs, inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+        e_off = rel(off_h[n:n + 1], off_ref)
+        e_y = rel(y_h[n:n + 1], y_ref)
+        # columns from the GPU's own offsets, so only the sampling is compared
+        col_ref = oracle.sample_cols(s1, xs, off_h[n:n + 1].astype(np.float64))
+        e_col = rel(cols_to_oracle_layout(cols_h[n:n + 1], wl), col_ref)
+        say("  image %d: rel offsets %.2e cols %.2e y %.2e" % (n, e_off, e_col, e_y))
+        assert e_off <= 1e-5
+        # fp32: the sample point is one fp32 add by contract, so its fraction
+        # carries up to half an ulp of |py| (about 4e-6 at 64 pixels)
+        assert e_col <= (1e-5 if wl.dtype == "f32" else 4e-3)
+        assert e_y <= tol
+
+
+@pytest.mark.parametrize("name", FWD)
+def test_index_stage_bit_exact(name):
+    """Tap index / corner mask from the GPU's own offsets equals the oracle's
+    fp32 index stage on the same offsets, element for element."""
+    wl = WORKLOADS[name]
+    say("index bit-exact", name)
+    inp = make_inputs(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl)
+    _, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    y0, x0, m = index_stage(layer.desc, off, wl.groups, wl.taps, layer.ho, layer.wo, wl.n)
+    torch.cuda.synchronize()
+    ry0, rx0, rm = oracle.sample_index_f32(shape_of(wl), host(off))
+    assert np.array_equal(host(y0), ry0)
+    assert np.array_equal(host(x0), rx0)
+    assert np.array_equal(host(m), rm)
+    if wl.pushed_pairs:
+        frac = float(np.mean(rm == 0))
+        say("  fully outside taps: %.3f" % frac)
+        assert frac >= wl.pushed_pairs / (wl.groups * wl.taps)
+
+
+def test_index_stage_adversarial_offsets():
+    """Offsets on integer lines, on the -1 / H boundaries, just inside and just
+    outside in fp32, NaN and huge values."""
+    s = oracle.Shape(2, 32, 7, 9, 16, stride=(2, 1), pad=(1, 2), dil=(1, 2), groups=2)
+    r = np.random.default_rng(5)
+    shp = (s.n, s.oc, s.ho, s.wo)
+    choices = np.array([0.0, 1.0, -1.0, -2.0, 0.5, -0.5, 7.0, -7.0, 9.0, 1e-8, -1e-8, 0.99999994, -0.99999994,
+                        3.4e38, -3.4e38, np.nan, np.inf, -np.inf, 2.5, -3.25], np.float32)
+    off = choices[r.integers(0, len(choices), shp)] + r.integers(-2, 3, shp).astype(np.float32)
+    off = off.astype(np.float32)
+    desc = L.make_desc(s.n, s.c_in, s.h, s.w, s.c_out, 3, 3, s.stride, s.pad, s.dil, s.groups, L.DEFT_F32)
+    say("index adversarial")
+    offd = torch.from_numpy(off).cuda()
+    y0, x0, m = index_stage(desc, offd, s.groups, 9, s.ho, s.wo, s.n)
+    torch.cuda.synchronize()
+    ry0, rx0, rm = oracle.sample_index_f32(s, off)
+    assert np.array_equal(host(y0), ry0) and np.array_equal(host(x0), rx0) and np.array_equal(host(m), rm)
+
+
+# --- structural invariants ---------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_offsets_columns_are_plain_im2col(dtype):
+    """W_off = 0, b_off = 0: every tap lands on its grid point, weight 1 on one
+    corner, so the GPU columns equal the plain patches bit for bit."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(n=3, c_in=32, h=13, w=10, c_out=24, dtype=dtype, stride=2,
+                                                     pad=2, dil=2)
+    say("zero offsets im2col", dtype)
+    inp = make_inputs(wl)
+    t = {k: dev(v, dtype) for k, v in inp.items()}
+    layer = make_layer(wl)
+    z = torch.zeros_like(t["w_off"])
+    layer.forward(t["x"], z, torch.zeros_like(t["b_off"]), t["w"], t["b"])
+    cols = host(layer.cols_view())
+    torch.cuda.synchronize()
+    unf = torch.nn.functional.unfold(torch.from_numpy(inp["x"]), (3, 3), dilation=2, padding=2, stride=2).numpy()
+    unf = np.transpose(unf.reshape(wl.n, wl.c_in, 9, -1), (0, 3, 2, 1))  # [N][P][taps][Cin]
+    assert np.array_equal(cols, unf)
+
+
+@pytest.mark.parametrize("name", ["bf16_n16_c256_56x56", "bf16_n16_c512_28x28_g4_wide", "fp32_n8_c128_64x64"])
+def test_fused_equals_unfused_and_plan_invariance(name):
+    """The fused kernel's columns equal the sample-only kernel's from the same
+    offsets; offsets, columns and y are bit-identical across tile/halo/chunk
+    plans (including halo 0, where most taps take the global fallback)."""
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    ref = None
+    for plan in [None, (8, 8, 0, 16), (4, 16, 3, 32), (2, 8, 1, 0), (8, 8, 12, 0)]:
+        say("plan", name, plan)
+        layer = make_layer(wl, plan=plan)
+        y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+        cols = layer.cols_view().clone()
+        un = layer.sample(t["x"], off)
+        torch.cuda.synchronize()
+        assert torch.equal(cols.view(torch.int16 if wl.dtype == "bf16" else torch.int32),
+                           un.view(torch.int16 if wl.dtype == "bf16" else torch.int32))
+        cur = (y.clone(), off.clone(), cols)
+        if ref is None:
+            ref = cur
+        else:
+            for a, b in zip(ref, cur):
+                assert torch.equal(a, b)
+        del layer
+
+
+def test_halo_histogram_matches_index_stage():
+    wl = WORKLOADS["bf16_n16_c512_28x28_g4_wide"]
+    say("halo histogram")
+    inp = make_inputs(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl)
+    _, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    hist = halo_histogram(layer.desc, off, 16)
+    torch.cuda.synchronize()
+    s = shape_of(wl)
+    ry0, rx0, rm = oracle.sample_index_f32(s, host(off))
+    by = (np.arange(s.ho) - s.pad[0])[None, None, None, :, None] + (np.arange(9) // 3)[None, None, :, None, None]
+    bx = (np.arange(s.wo) - s.pad[1])[None, None, None, None, :] + (np.arange(9) % 3)[None, None, :, None, None]
+    need = np.maximum(np.abs(ry0 - by), np.abs(rx0 - bx))
+    # a tap that is not fully outside always has an in-image corner, so the
+    # fp32 index stage's mask is 0 exactly for the fully outside taps
+    outside = rm == 0
+    exp = np.zeros(16, np.int64)
+    np.add.at(exp, np.minimum(need[~outside], 14), 1)
+    exp[15] = outside.sum()
+    assert list(exp) == hist
+
+
+@pytest.mark.parametrize("case", [
+    dict(n=0),
+    dict(h=9, w=13, c_out=40),
+    dict(stride=2, pad=0),
+    dict(dil=2, pad=2, groups=2),
+    dict(kh=5, kw=5, pad=2),
+    dict(kh=3, kw=2, pad=1),
+    dict(h=5, w=70, c_in=48, c_out=8),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_shapes_forward(case, dtype):
+    base = dict(n=2, c_in=32, c_out=16, h=11, w=12)
+    base.update(case)
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, **base)
+    say("edge forward", dtype, case)
+    inp = make_inputs(wl)
+    t = {k: dev(v, dtype) for k, v in inp.items()}
+    layer = make_layer(wl)
+    y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    torch.cuda.synchronize()
+    if wl.n == 0:
+        return
+    s = shape_of(wl)
+    y_ref, off_ref = oracle.forward(s, inp["x"], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+    assert rel(host(off), off_ref) <= 1e-5
+    assert rel(host(y), y_ref) <= TOL[dtype]
+
+
+# --- backward -------------------------------------------------------------------------
+
+def run_backward(wl, plan=None):
+    inp = make_inputs(wl, with_dy=True)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl, plan=plan, training=True)
+    y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    g = layer.backward(t["x"], t["w_off"], t["w"], off, t["dy"])
+    torch.cuda.synchronize()
+    return inp, layer, y, off, g
+
+
+@pytest.mark.parametrize("case", [
+    dict(),
+    dict(stride=2),
+    dict(dil=2, pad=2, groups=2),
+    dict(pad=0, groups=4, c_in=64),
+    dict(h=9, w=13, c_out=40, offset_std=3.0),
+    dict(kh=5, kw=5, pad=2),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_matches_oracle_small(case, dtype):
+    base = dict(n=2, c_in=32, c_out=24, h=10, w=11)
+    base.update(case)
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, train=True, **base)
+    say("backward small", dtype, case)
+    inp, layer, y, off, g = run_backward(wl)
+    s = shape_of(wl)
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    tol = TOL[dtype]
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= tol, k
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["train_bf16_n16_c256_56x56_s1", "train_bf16_n16_c256_56x56_s2"])
+def test_training_step_full_size(name):
+    """Full-size forward + backward in the benchmark's launch configuration.
+    Per-image outputs (y, dx) are compared with the oracle on two sampled
+    images; the weight and bias gradients, which sum over all images, against
+    the sum of the oracle's per-image backward passes over all 16 images."""
+    wl = WORKLOADS[name]
+    say("training step full size", name)
+    inp, layer, y, off, g = run_backward(wl)
+    off_h = host(off).astype(np.float64)
+    s1 = image_shape(wl, 1)
+    y_h = host(y)
+    tol = TOL[wl.dtype]
+    sums = {k: None for k in ("dw", "db", "dw_off", "db_off")}
+    for n in range(wl.n):
+        sl = slice(n, n + 1)
+        ref = oracle.backward(s1, inp["x"][sl], inp["w_off"], inp["w"], off_h[sl], inp["dy"][sl])
+        say("  oracle image %d done" % n)
+        for k in sums:
+            sums[k] = ref[k] if sums[k] is None else sums[k] + ref[k]
+        if n in (0, wl.n - 1):
+            y_ref, _ = oracle.forward(s1, inp["x"][sl], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+            e_y, e_dx = rel(y_h[sl], y_ref), rel(host(g["dx"][sl]), ref["dx"])
+            say("  image %d: y %.2e dx %.2e" % (n, e_y, e_dx))
+            assert e_y <= tol and e_dx <= tol
+    for k, v in sums.items():
+        e = rel(host(g[k]), v)
+        say("  %s rel %.2e" % (k, e))
+        assert e <= tol, k
