@@ -40,9 +40,9 @@ def kernel_work(wl):
         "gemm_forward": (cols + wl.c_out * ck * esz + P * wl.c_out * esz, gemm_flop),
         "gemm_dcol": (P * wl.c_out * esz + wl.c_out * ck * esz + cols, gemm_flop),
         "gemm_dw": (cols + P * wl.c_out * esz + wl.c_out * ck * 4, gemm_flop),
-        "sample_backward": (cols + x * esz + offs + 2 * x * 4 + offs, 0.0),
+        "sample_backward": (cols + x * esz + offs + offs + x * 4, 0.0),
         "offset_weight_backward": (offs + x * esz + wl.oc * ck * 4, off_flop),
-        "offset_input_backward": (offs + wl.c_in * wl.oc * wl.taps * esz + x * 4 + x * esz, off_flop),
+        "dx_final": (offs + wl.c_in * wl.oc * wl.taps * esz + x * 4 + x * esz, off_flop),
     }
 
 
@@ -88,9 +88,9 @@ def main():
     tot = float(sum(hist))
     log("offset std %.3f px; fully outside taps %.4f; required-halo histogram %s"
         % (float(off_h.std()), hist[-1] / tot, hist))
-    log("plan: tile %dx%d halo %d chunk %d, %d workgroups, %d B LDS, est. miss %.4f"
+    log("plan: tile %dx%d halo %d chunk %d, %d workgroups, %d B LDS, est. miss %.4f; backward tile %dx%d chunk %d"
         % (info["tile_h"], info["tile_w"], info["halo"], info["chunk"], info["num_workgroups"],
-           info["lds_bytes"], info["est_miss_fraction"]))
+           info["lds_bytes"], info["est_miss_fraction"], info["bwd_tile_h"], info["bwd_tile_w"], info["bwd_chunk"]))
 
     y = torch.empty((wl.n, wl.c_out, wl.ho, wl.wo), dtype=tdt, device=dev)
     offs = torch.empty((wl.n, wl.oc, wl.ho, wl.wo), dtype=torch.float32, device=dev)
@@ -193,7 +193,8 @@ def main():
         "config": {"workload": wl.name, "n": wl.n, "c_in": wl.c_in, "c_out": wl.c_out, "h": wl.h, "w": wl.w,
                    "kernel": [wl.kh, wl.kw], "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil,
                    "offset_groups": wl.groups, "offset_std_px": wl.offset_std,
-                   "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk")}},
+                   "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk", "bwd_tile_h", "bwd_tile_w",
+                                                 "bwd_chunk")}},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),

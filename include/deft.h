@@ -82,6 +82,8 @@ typedef struct deft_plan_info {
   size_t ws_forward, ws_training;
   size_t ws_cols_offset;  /* byte offset in the workspace of the deformed columns
                              [N*Ho*Wo][kh*kw][Cin] that deft_forward leaves there */
+  int bwd_tile_h, bwd_tile_w; /* output tile of the sampling backward */
+  int bwd_chunk;          /* its channel chunk; 0: this plan has no backward (LDS) */
 } deft_plan_info;
 
 /* Checks the descriptor alone.  Pure host function. */

@@ -2,337 +2,495 @@
 //
 // The DefT explainer page speaks of training time only ("The argument in one
 // glance", "This paper's idea"), so the backward is the exact derivative of
-// the forward: dCol = W^T dY and dW = dY Col run on the MFMA GEMMs
-// (deft_gemm.hip); this file holds
-//   k_sample_bwd  -- per output tile: re-derives each tap's corner and weights
-//                    from the saved offsets, scatters dCol times the bilinear
-//                    weights into an LDS copy of the tile's halo region
-//                    (fp32 LDS atomics) that is then added to dX with global
-//                    atomics, and reduces dOffset = sum over the group's
-//                    channels of dCol times the corner differences;
-//   k_woff_bwd    -- dW_off = dOffset against the plain patches of x (MFMA,
-//                    per image and channel slice) and db_off;
-//   k_dx_off      -- dX_offset, the transposed offset convolution of dOffset
-//                    (MFMA, per input tile), added to the accumulated dX and
-//                    rounded once to the output dtype;
-//   finalize / prep kernels (weight transposes, fp32 -> dtype, bias sums).
+// the forward.  dCol = W^T dY and the per-image partials of dW = dY Col run
+// on the MFMA GEMMs (deft_gemm.hip); this file holds
+//   k_sample_bwd   -- per core tile of input pixels: lists the (output pixel,
+//                     tap) pairs whose corners touch the core within the
+//                     halo, then per channel chunk (lanes = channels)
+//                     scatters dCol x bilinear weight into an fp32 LDS copy
+//                     of the core (64 consecutive addresses per LDS atomic,
+//                     no collisions) and writes the core's dX once with plain
+//                     stores; the unique owner of each pair reduces
+//                     dOffset = sum over the group's channels of dCol x the
+//                     corner differences.
+//   k_sample_bwd_miss -- the rare taps beyond the halo: dOffset from global
+//                     memory, dX added with global atomics.
+//   k_woff_bwd     -- per (image, 32-channel slice, band of output rows):
+//                     dW_off partials = dOffset rows against the plain
+//                     patches of x, both staged in LDS, on MFMA.
+//   k_dx_final     -- per 64 input pixels x 128 channels: dX_offset, the
+//                     transposed offset convolution (MFMA), plus the sampling
+//                     part of dX; rounded once.
+//   k_bias_partial, k_reduce_final -- per-image bias sums, then one fixed-order
+//                     reduction of all partials to dW, dW_off, db, db_off.
+// Global atomics are avoided on every hot path: on gfx950 they run far below
+// the bandwidth of plain stores.
 #include "deft_device.h"
 #include "deft_internal.h"
 
 namespace deft {
 
-hipError_t launch_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, hipStream_t st);
-hipError_t launch_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* dw32, hipStream_t st);
+hipError_t launch_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
+                            hipStream_t st);
+hipError_t launch_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* dwpart, hipStream_t st);
 
 struct BwdParams {
-  int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, G, Cg, K2, Oc, Ck, Cout;
-  int TH, TW, halo, CC, GW, gsplit, tiles_h, tiles_w, num_wg;
-  int FH, FW, pstr, dstr, lognv;
-  int lds_x, lds_dx, lds_off, lds_info, lds_doff;
-  FastDiv div_tw, div_k2;
+  int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, G, Cg, K2, Oc, Ck;
+  int CH, CW, bt_h, bt_w, halo, CC, num_wg, list_cap, capbits, xstr, dcstr;
+  int lds_dx, lds_dc, lds_cnt;
   const void* x;
   const float* off;
   const void* dcol;
-  float* dx32;
-  float* doff;
+  const uint32_t* maxbits;  // max |dcol| as fp32 bits
+  float* dxs;    // [N][Cin][H][W] fp32: the sampling part of dX
+  float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials, zeroed beforehand
+  int4* lists;   // [num_wg][list_cap]
 };
 
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+__device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }
+
+// Corner q of a tap: (y0 + (q >> 1), x0 + (q & 1)), the order of tap_weights.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
-  const int tile = lw / p.gsplit, gs = lw - tile * p.gsplit;
-  const int tpi = p.tiles_h * p.tiles_w;
+  const int tile = lw / p.G, g = lw - tile * p.G;
+  const int tpi = p.bt_h * p.bt_w;
   const int n = tile / tpi, trem = tile - n * tpi;
-  const int tyi = trem / p.tiles_w, txi = trem - tyi * p.tiles_w;
-  const int oh0 = tyi * p.TH, ow0 = txi * p.TW;
-  const int thn = min(p.TH, p.Ho - oh0), twn = min(p.TW, p.Wo - ow0);
-  const int PT = p.TH * p.TW;
-  const int g0 = gs * p.GW;
-  const int ocw = 2 * p.GW * p.K2;
-  const int obase = 2 * g0 * p.K2;
-  T* xr = (T*)(smem + p.lds_x);
-  float* dxr = (float*)(smem + p.lds_dx);
-  float* off_l = (float*)(smem + p.lds_off);
-  int4* info = (int4*)(smem + p.lds_info);
-  float* doff_l = (float*)(smem + p.lds_doff);  // [GW][K2][PT][2]
+  const int Y0 = (trem / p.bt_w) * p.CH, X0 = (trem % p.bt_w) * p.CW;
+  const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
+  const int obase = 2 * g * p.K2;
+  const int HoWo = p.Ho * p.Wo;
+  T* xl = (T*)smem;  // [(CH+2)*(CW+2)][xstr]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
+  int* cnt = (int*)(smem + p.lds_cnt);
+  int4* list = p.lists + (size_t)lw * p.list_cap;
+  const float* __restrict__ offn = p.off + ((size_t)n * p.Oc + obase) * HoWo;
   const T* __restrict__ x = (const T*)p.x;
   const T* __restrict__ dcol = (const T*)p.dcol;
-  const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
 
-  for (int e = tid; e < ocw * PT; e += 256) {
-    const int o = e / PT, pix = e - o * PT;
-    const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-    float v = 0.f;
-    if (ty < thn && tx < twn) v = p.off[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx];
-    off_l[e] = v;
+  // ---- the pairs touching this core ----
+  // Candidates: for every tap, the output pixels whose tap grid point lies
+  // within halo+1 above/left and halo below/right of the core (where a corner
+  // can touch it).  The per-tap rectangles are flattened into one index space
+  // and evaluated four per thread per step, loads first.
+  int* rlo_h = cnt + 4;          // per tap: first output row / column of the
+  int* rlo_w = rlo_h + 48;        // candidate rectangle, its width, and the
+  int* rnw = rlo_w + 48;          // prefix sum of the rectangle sizes
+  int* rstart = rnw + 48;
+  if (tid < p.K2) {
+    const int t = tid;
+    const int ti = t / p.KW, tj = t - ti * p.KW;
+    const int ho_lo = max(0, ceil_div(Y0 - 1 - p.halo + p.PH - ti * p.DH, p.SH));
+    const int ho_hi = min(p.Ho - 1, floor_div(Y0 + chn - 1 + p.halo + p.PH - ti * p.DH, p.SH));
+    const int wo_lo = max(0, ceil_div(X0 - 1 - p.halo + p.PW - tj * p.DW, p.SW));
+    const int wo_hi = min(p.Wo - 1, floor_div(X0 + cwn - 1 + p.halo + p.PW - tj * p.DW, p.SW));
+    const int nh = max(0, ho_hi - ho_lo + 1), nw = max(0, wo_hi - wo_lo + 1);
+    rlo_h[t] = ho_lo; rlo_w[t] = wo_lo; rnw[t] = nw > 0 ? nw : 1;
+    rstart[t + 1] = nh * nw;
   }
-  for (int e = tid; e < p.GW * p.K2 * PT * 2; e += 256) doff_l[e] = 0.f;
-  const int fha = (thn - 1) * p.SH + (p.KH - 1) * p.DH + 1;
-  const int fwa = (twn - 1) * p.SW + (p.KW - 1) * p.DW + 1;
-  const int ry0 = max(fy0 - p.halo, -1), ry1 = min(fy0 + fha + p.halo, p.H);
-  const int rx0 = max(fx0 - p.halo, -1), rx1 = min(fx0 + fwa + p.halo, p.W);
-  int RH = ry1 - ry0 + 1, RW = rx1 - rx0 + 1;
-  if (RH <= 0 || RW <= 0) { RH = 0; RW = 0; }
+  if (tid == 0) *cnt = 0;
   __syncthreads();
-  for (int e = tid; e < p.GW * p.K2 * PT; e += 256) {
-    const int gt = e / PT, pix = e - gt * PT;
-    const int gl = fdiv(gt, p.div_k2), t = gt - gl * p.K2;
-    const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-    int4 inf = make_int4(-2, 0, 0, 0);
-    if (ty < thn && tx < twn) {
+  if (tid == 0) {
+    rstart[0] = 0;
+    for (int t = 0; t < p.K2; ++t) rstart[t + 1] += rstart[t];
+  }
+  __syncthreads();
+  const int ncand = rstart[p.K2];
+  for (int e0 = tid; e0 < ncand; e0 += 4 * 256) {
+    float dyv[4], dxv[4];
+    int tt[4], pp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 256;
+      tt[u] = -1;
+      dyv[u] = dxv[u] = 0.f;
+      pp[u] = 0;
+      if (e < ncand) {
+        int t = 0;
+        while (e >= rstart[t + 1]) ++t;
+        const int k = e - rstart[t];
+        const int ho = rlo_h[t] + k / rnw[t], wo = rlo_w[t] + k % rnw[t];
+        tt[u] = t;
+        pp[u] = ho * p.Wo + wo;
+        dyv[u] = offn[(size_t)(2 * t) * HoWo + pp[u]];
+        dxv[u] = offn[(size_t)(2 * t + 1) * HoWo + pp[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tt[u];
+      if (t < 0) continue;
       const int ti = t / p.KW, tj = t - ti * p.KW;
-      const int by = (oh0 + ty) * p.SH - p.PH + ti * p.DH;
-      const int bx = (ow0 + tx) * p.SW - p.PW + tj * p.DW;
-      const TapIndex ix = tap_index(by, bx, off_l[(2 * (gl * p.K2 + t)) * PT + pix],
-                                    off_l[(2 * (gl * p.K2 + t) + 1) * PT + pix], p.H, p.W);
-      if (!ix.outside) {
-        const bool in = ix.y0 >= ry0 && ix.y0 + 1 <= ry1 && ix.x0 >= rx0 && ix.x0 + 1 <= rx1 && RH > 0;
-        inf.x = in ? (ix.y0 - ry0) * RW + (ix.x0 - rx0) : -1;
-        inf.y = (int)(((uint32_t)ix.y0 << 16) | ((uint32_t)ix.x0 & 0xffffu));
-        inf.z = __float_as_int(ix.ly);
-        inf.w = __float_as_int(ix.lx);
-      }
-    }
-    info[e] = inf;
-  }
-
-  const FastDiv drw = make_fastdiv(RW > 0 ? RW : 1), drh = make_fastdiv(RH > 0 ? RH : 1);
-  const int nv = p.CC >> 3;
-  const int nitems = PT * p.K2 * nv;
-  const size_t HW = (size_t)p.H * p.W;
-  const int rtot = RH * RW;
-  for (int gl = 0; gl < p.GW; ++gl) {
-    const int g = g0 + gl;
-    for (int c0 = 0; c0 < p.Cg; c0 += p.CC) {
-      const int cglob = g * p.Cg + c0;
-      __syncthreads();
-      if (RH > 0) stage_region_hwc<T>(xr, x, p.Cin, p.H, p.W, n, cglob, p.CC, ry0, rx0, RH, RW, drw, drh, p.pstr);
-      for (int e = tid; e < rtot * p.dstr; e += 256) dxr[e] = 0.f;
-      __syncthreads();
-      for (int it = tid; it < nitems; it += 256) {
-        const int v = it & (nv - 1);
-        const int rest = it >> p.lognv;
-        const int pix = fdiv(rest, p.div_k2), t = rest - pix * p.K2;
-        const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-        if (ty >= thn || tx >= twn) continue;
-        const int4 inf = info[(gl * p.K2 + t) * PT + pix];
-        float gy = 0.f, gx = 0.f;
-        if (inf.x != -2) {
-          const size_t q = (size_t)n * p.Ho * p.Wo + (size_t)(oh0 + ty) * p.Wo + (ow0 + tx);
-          float gc[8];
-          load8(dcol + q * p.Ck + (size_t)t * p.Cin + cglob + v * 8, gc);
-          TapIndex ix;
-          ix.outside = false;
-          ix.ly = __int_as_float(inf.z);
-          ix.lx = __int_as_float(inf.w);
-          float w[4];
-          tap_weights(ix, w);
-          const float hy = 1.0f - ix.ly, hx = 1.0f - ix.lx;
-          float f00[8], f01[8], f10[8], f11[8];
-          if (inf.x >= 0) {
-            const T* b0 = xr + (size_t)inf.x * p.pstr + v * 8;
-            lds_read8(b0, f00);
-            lds_read8(b0 + p.pstr, f01);
-            lds_read8(b0 + (size_t)RW * p.pstr, f10);
-            lds_read8(b0 + (size_t)(RW + 1) * p.pstr, f11);
-            float* d0 = dxr + (size_t)inf.x * p.dstr + v * 8;
+      const int ho = pp[u] / p.Wo, wo = pp[u] - ho * p.Wo;
+      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
+      const TapIndex ix = tap_index(by, bx, dyv[u], dxv[u], p.H, p.W);
+      if (ix.outside) continue;
+      if (max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo) continue;
+      uint32_t cm = 0;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              atomicAdd(d0 + c, w[0] * gc[c]);
-              atomicAdd(d0 + p.dstr + c, w[1] * gc[c]);
-              atomicAdd(d0 + (size_t)RW * p.dstr + c, w[2] * gc[c]);
-              atomicAdd(d0 + (size_t)(RW + 1) * p.dstr + c, w[3] * gc[c]);
-            }
-          } else {
-            const int y0 = inf.y >> 16, x0 = (int)(short)(inf.y & 0xffff);
-            const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
-            const T* base = x + ((size_t)n * p.Cin + cglob + v * 8) * HW;
-            float* dbase = p.dx32 + ((size_t)n * p.Cin + cglob + v * 8) * HW;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const T* pl = base + c * HW;
-              float* dl = dbase + c * HW;
-              f00[c] = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
-              f01[c] = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
-              f10[c] = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
-              f11[c] = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
-              if (r0 && q0) atomicAdd(dl + (size_t)y0 * p.W + x0, w[0] * gc[c]);
-              if (r0 && q1) atomicAdd(dl + (size_t)y0 * p.W + x0 + 1, w[1] * gc[c]);
-              if (r1 && q0) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0, w[2] * gc[c]);
-              if (r1 && q1) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0 + 1, w[3] * gc[c]);
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            gy = __builtin_fmaf(gc[c], hx * (f10[c] - f00[c]) + ix.lx * (f11[c] - f01[c]), gy);
-            gx = __builtin_fmaf(gc[c], hy * (f01[c] - f00[c]) + ix.ly * (f11[c] - f10[c]), gx);
-          }
-        }
-        // reduce over the nv lanes that share this (pixel, tap)
-        for (int s = 1; s < nv; s <<= 1) {
-          gy += __shfl_xor(gy, s);
-          gx += __shfl_xor(gx, s);
-        }
-        if (v == 0) {
-          float* dd = doff_l + ((gl * p.K2 + t) * PT + pix) * 2;
-          dd[0] += gy;
-          dd[1] += gx;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int cy = ix.y0 + (q >> 1), cx = ix.x0 + (q & 1);
+        if (cy >= Y0 && cy < Y0 + chn && cx >= X0 && cx < X0 + cwn) cm |= 1u << q;
       }
-      __syncthreads();
-      // add the region's dX to global memory (in-image pixels only)
-      const int ntot = p.CC * rtot;
-      for (int e = tid; e < ntot; e += 256) {
-        const int r = fdiv(e, drw);
-        const int rx = e - r * RW;
-        const int c = fdiv(r, drh);
-        const int ry = r - c * RH;
-        const int yy = ry0 + ry, xx = rx0 + rx;
-        if ((unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) {
-          const float v = dxr[(ry * RW + rx) * p.dstr + c];
-          if (v != 0.f) atomicAdd(p.dx32 + ((size_t)n * p.Cin + cglob + c) * HW + (size_t)yy * p.W + xx, v);
-        }
-      }
+      if (!cm) continue;
+      const int oy = max(ix.y0, 0), ox = max(ix.x0, 0);
+      const uint32_t owned = (oy >= Y0 && oy < Y0 + chn && ox >= X0 && ox < X0 + cwn) ? 1u : 0u;
+      const int slot = atomicAdd(cnt, 1);
+      list[slot] = make_int4(pp[u], (int)((uint32_t)t | (owned << 8) | (cm << 9) | ((uint32_t)(ix.y0 - Y0 + 1) << 16) |
+                                          ((uint32_t)(ix.x0 - X0 + 1) << 24)),
+                             __float_as_int(ix.ly), __float_as_int(ix.lx));
     }
   }
   __syncthreads();
-  for (int e = tid; e < p.GW * p.K2 * PT; e += 256) {
-    const int gt = e / PT, pix = e - gt * PT;
-    const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-    if (ty >= thn || tx >= twn) continue;
-    const size_t base = (((size_t)n * p.Oc + obase + 2 * gt) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx;
-    p.doff[base] = doff_l[2 * e];
-    p.doff[base + (size_t)p.Ho * p.Wo] = doff_l[2 * e + 1];
+  const int L = *cnt;
+
+  // ---- per channel chunk: stage, scatter, dOffset, write the core ----
+  // dX is accumulated in 64-bit fixed point with integer LDS atomics (fast
+  // on this LDS, unlike float atomics; exact, so the sum is independent of
+  // the order of the atomics).  Scale 2^S: every contribution |w*g| <= max|g|
+  // < 2^(e+1) and a (pixel, channel) receives at most list_cap of them, so
+  // |sum| * 2^S < 2^63 for S = 61 - capbits - e; one contribution is split as
+  // hi*2^32 + lo with |hi| < 2^30.
+  const uint32_t gb = *p.maxbits;
+  const int e = max((int)((gb >> 23) & 255u) - 126, -100);
+  const int S = 61 - p.capbits - e;
+  const float sc = ldexpf(1.0f, S - 32);
+  const double inv = ldexp(1.0, -S);
+  // Each wave walks blocks of BLK list entries: the block's dCol rows are
+  // copied into a wave-private LDS buffer with 16-byte loads (the next
+  // block's rows are already in flight in registers), then processed one
+  // entry at a time with lanes = channels.
+  constexpr int BLK = 32;
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int KQ = BLK / VEC;  // loads per lane per block, at most
+  const int XW = p.CW + 2;
+  const int c = lane;  // channel within the chunk (lanes >= CC idle)
+  const bool act = c < p.CC;
+  const size_t HW = (size_t)p.H * p.W;
+  T* dst = (T*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;
+  unsigned long long* dxl = (unsigned long long*)(smem + p.lds_dx);  // [CH*CW][CC]
+  const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
+  const int epi = 64 / lpe;    // rows per load instruction
+  const size_t pstride = (size_t)p.N * p.Oc * HoWo;
+  for (int c0 = 0; c0 < p.Cg; c0 += p.CC) {
+    const int cglob = g * p.Cg + c0;
+    float* doffp = p.doffp + (size_t)(c0 / p.CC) * pstride + ((size_t)n * p.Oc + obase) * HoWo;
+    __syncthreads();
+    {
+      const int np = (p.CH + 2) * XW;
+      for (int k = tid; k < np * p.CC; k += 256) {
+        const int cc = k / np, r = k - cc * np;
+        const int ry = r / XW, rx = r - ry * XW;
+        const int y = Y0 - 1 + ry, xx = X0 - 1 + rx;
+        T v = zero_elem<T>();
+        if ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
+          v = x[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)y * p.W + xx];
+        xl[r * p.xstr + cc] = v;
+      }
+      for (int k = tid; k < p.CH * p.CW * p.CC; k += 256) dxl[k] = 0ull;
+    }
+    __syncthreads();
+    int eb = wave * BLK;
+    int4 my = make_int4(0, 0, 0, 0);
+    uint4 q[KQ];
+    auto load_block = [&](int b0) {
+      const int nb = min(BLK, L - b0);
+      my = lane < nb ? list[b0 + lane] : make_int4(0, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < KQ; ++k) {
+        const int r = k * epi + lane / lpe, v = lane % lpe;
+        const int pix = __shfl(my.x, r & 63), t = __shfl(my.y, r & 63) & 255;
+        q[k] = make_uint4(0, 0, 0, 0);
+        if (k * epi < BLK && r < nb)
+          q[k] = *(const uint4*)(dcol + ((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cglob + v * VEC);
+      }
+    };
+    if (eb < L) load_block(eb);
+    for (; eb < L; eb += 4 * BLK) {
+      const int nb = min(BLK, L - eb);
+#pragma unroll
+      for (int k = 0; k < KQ; ++k) {
+        const int r = k * epi + lane / lpe, v = lane % lpe;
+        if (k * epi < BLK && r < nb) *(uint4*)(dst + r * p.dcstr + v * VEC) = q[k];
+      }
+      const int4 cur = my;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
+      // scatter: lanes = channels, one entry at a time
+      for (int r = 0; r < nb; ++r) {
+        const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
+        const uint32_t cm = (info >> 9) & 15u;
+        const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+        TapIndex ix;
+        ix.outside = false;
+        ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
+        ix.lx = __int_as_float(__builtin_amdgcn_readlane(cur.w, r));
+        float w[4];
+        tap_weights(ix, w);
+        if (act) {
+          const float gcv = Elem<T>::to_f32(dst[r * p.dcstr + c]);
+          unsigned long long* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            if (cm & (1u << qq)) {
+              const float xv = gcv * (w[qq] * sc);
+              const float fh = floorf(xv);
+              const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
+              const unsigned long long v64 = ((unsigned long long)(uint32_t)(int)fh << 32) | lo;
+              atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, v64);
+            }
+          }
+        }
+      }
+      // dOffset of the block's owned entries: lanes = entries (lane & 31);
+      // the two lane halves take the two halves of the chunk's channels
+      {
+        const int r = lane & 31, half = lane >> 5;
+        const int ex = __shfl(cur.x, r), ey = __shfl(cur.y, r), ez = __shfl(cur.z, r), ew = __shfl(cur.w, r);
+        const uint32_t info = (uint32_t)ey;
+        const bool own = r < nb && ((info >> 8) & 1u);
+        float gy = 0.f, gx = 0.f;
+        if (own) {
+          const int cy = (info >> 16) & 255, cx = info >> 24;
+          const float ly = __int_as_float(ez), lx = __int_as_float(ew);
+          const float hy = 1.0f - ly, hx = 1.0f - lx;
+          const T* drow = dst + r * p.dcstr;
+          const T* b0 = xl + (cy * XW + cx) * p.xstr;
+          const T* b1 = b0 + p.xstr;
+          const T* b2 = b0 + XW * p.xstr;
+          const T* b3 = b2 + p.xstr;
+          const int hc = p.CC >> 1;
+          for (int cc = half * hc; cc < (half + 1) * hc; ++cc) {
+            const float gv = Elem<T>::to_f32(drow[cc]);
+            const float v00 = Elem<T>::to_f32(b0[cc]), v01 = Elem<T>::to_f32(b1[cc]);
+            const float v10 = Elem<T>::to_f32(b2[cc]), v11 = Elem<T>::to_f32(b3[cc]);
+            gy = __builtin_fmaf(gv, hx * (v10 - v00) + lx * (v11 - v01), gy);
+            gx = __builtin_fmaf(gv, hy * (v01 - v00) + ly * (v11 - v10), gx);
+          }
+        }
+        gy += __shfl_xor(gy, 32);
+        gx += __shfl_xor(gx, 32);
+        if (own && half == 0) {
+          const int t = info & 255;
+          doffp[(size_t)(2 * t) * HoWo + ex] = gy;
+          doffp[(size_t)(2 * t + 1) * HoWo + ex] = gx;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    for (int k = tid; k < p.CC * chn * cwn; k += 256) {
+      const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
+      const int y = r / cwn, xx = r - y * cwn;
+      const long long sv = (long long)dxl[(y * p.CW + xx) * p.CC + cc];
+      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = (float)((double)sv * inv);
+    }
+  }
+}
+
+// Taps beyond the halo (need > halo, not fully outside): every wave scans 64
+// taps (lane = tap); for each miss, the wave (lanes = channels) computes the
+// offset gradient from global memory and adds the dX contributions with
+// global atomics.  Runs after k_sample_bwd has written dX.
+template <typename T>
+__global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int HoWo = p.Ho * p.Wo;
+  const size_t total = (size_t)p.N * p.G * p.K2 * HoWo;
+  const size_t HW = (size_t)p.H * p.W;
+  const T* __restrict__ x = (const T*)p.x;
+  const T* __restrict__ dcol = (const T*)p.dcol;
+  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 64; base < total; base += (size_t)gridDim.x * 256) {
+    const size_t pid = base + lane;
+    bool miss = false;
+    if (pid < total) {
+      const int pix = (int)(pid % HoWo);
+      const size_t r = pid / HoWo;
+      const int t = (int)(r % p.K2);
+      const size_t r2 = r / p.K2;
+      const int g = (int)(r2 % p.G), n = (int)(r2 / p.G);
+      const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
+      const int ti = t / p.KW, tj = t - ti * p.KW;
+      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
+      const float* o = p.off + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
+      const TapIndex ix = tap_index(by, bx, o[0], o[HoWo], p.H, p.W);
+      miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
+    }
+    unsigned long long mask = __ballot(miss);
+    while (mask) {
+      const int l = __ffsll((long long)mask) - 1;
+      mask &= mask - 1;
+      const size_t q = base + l;
+      const int pix = (int)(q % HoWo);
+      const size_t r = q / HoWo;
+      const int t = (int)(r % p.K2);
+      const size_t r2 = r / p.K2;
+      const int g = (int)(r2 % p.G), n = (int)(r2 / p.G);
+      const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
+      const int ti = t / p.KW, tj = t - ti * p.KW;
+      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
+      const size_t oidx = ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
+      float* dd = p.doffp + oidx;  // chunk-0 partial; the other chunks' stay 0 for a miss
+      const TapIndex ix = tap_index(by, bx, p.off[oidx], p.off[oidx + HoWo], p.H, p.W);
+      float w[4];
+      tap_weights(ix, w);
+      const int y0 = ix.y0, x0 = ix.x0;
+      const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
+      float gy = 0.f, gx = 0.f;
+      for (int c = lane; c < p.Cg; c += 64) {
+        const int cg = g * p.Cg + c;
+        const float gcv = Elem<T>::to_f32(dcol[((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cg]);
+        const T* pl = x + ((size_t)n * p.Cin + cg) * HW;
+        float* dl = p.dxs + ((size_t)n * p.Cin + cg) * HW;
+        const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
+        const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
+        const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
+        const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
+        if (r0 && q0) atomicAdd(dl + (size_t)y0 * p.W + x0, w[0] * gcv);
+        if (r0 && q1) atomicAdd(dl + (size_t)y0 * p.W + x0 + 1, w[1] * gcv);
+        if (r1 && q0) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0, w[2] * gcv);
+        if (r1 && q1) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0 + 1, w[3] * gcv);
+        gy += gcv * ((1.0f - ix.lx) * (v10 - v00) + ix.lx * (v11 - v01));
+        gx += gcv * ((1.0f - ix.ly) * (v01 - v00) + ix.ly * (v11 - v10));
+      }
+      for (int s = 1; s < 64; s <<= 1) {
+        gy += __shfl_xor(gy, s);
+        gx += __shfl_xor(gx, s);
+      }
+      if (lane == 0) {
+        dd[0] = gy;
+        dd[HoWo] = gx;
+      }
+    }
+  }
+}
+
+// dOffset = sum of the per-chunk partials, in chunk order.
+__global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part, float* doff, size_t n, int chunks) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int k = 1; k < chunks; ++k) v += part[(size_t)k * n + i];
+    doff[i] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// dW_off[o][t][c] += sum over output pixels of dOff[o][pix] * xz[c][tap t of
-// pix].  GEMM with rows o (MB blocks of 32), columns (tap, channel) and depth
-// pixels.  Workgroup = (image, 32-channel slice, band of output pixels); N
-// block t of the GEMM is tap t for the slice's 32 channels, and wave w owns
-// taps t = w, w+4, ...  Both operands are gathered from global memory (L2):
-// A = 8 consecutive pixels of one dOff row, B = x at 8 consecutive pixels'
-// tap-t positions for one channel.
+// dW_off partials.  GEMM rows o (MB blocks of 32 starting at o0), columns
+// (tap, channel) for a 32-channel slice, depth = output pixels of one row at a
+// time.  Per output row the KH input rows it reads are staged channel-major
+// in LDS ([c][i][column], zero outside the image) with the dOffset rows
+// ([o][pixel], dtype); wave w owns taps tg+w, tg+w+4, tg+w+8.
 struct WoffParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc;
-  int o0, orows;  // offset-channel rows [o0, o0+orows) handled by this launch (orows <= 96)
-  int slices, bands, band_pix, num_wg;
+  int o0, orows, slices, bands, band_rows, num_wg, WoP, XS, DLS;
   const void* x;
   const float* doff;
-  float* dwoff32;  // [Oc][K2][Cin]
+  float* part;  // [N*bands][Oc][K2][Cin]
 };
 
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int KC = 2 * VEC;  // pixels per k-chunk
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* xs = (T*)smem;                                                        // [32][KH][XS]
+  T* dl = (T*)(smem + ((32 * p.KH * p.XS * (int)sizeof(T) + 15) & ~15));  // [MB*32][DLS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
   const int per_img = p.slices * p.bands;
   const int n = lw / per_img, r = lw - n * per_img;
   const int band = r / p.slices, cs = r - band * p.slices;
+  const int ho0 = band * p.band_rows, ho1 = min(p.Ho, ho0 + p.band_rows);
   const int HoWo = p.Ho * p.Wo;
-  const int pb0 = band * p.band_pix, pb1 = min(HoWo, pb0 + p.band_pix);
-  const int c = cs * 32 + (lane & 31);
-  const bool cval = c < p.Cin;
-  const int half = lane >> 5;
+  const int cl = lane & 31, half = lane >> 5;
+  const int c = cs * 32 + cl;
   const T* __restrict__ x = (const T*)p.x;
   const float* __restrict__ doff = p.doff + (size_t)n * p.Oc * HoWo;
-  const T* xc = x + ((size_t)n * p.Cin + (cval ? c : 0)) * p.H * p.W;
-  // taps are processed 12 at a time (3 per wave) so any kernel size fits
+  const int xrow = p.KH * p.XS;
   for (int tg = 0; tg < p.K2; tg += 12) {
-  f32x16_t acc[MB][3];
+    f32x16_t acc[MB][3];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[mb][j][q] = 0.f;
-  for (int k0 = pb0; k0 < pb1; k0 += KC) {
-    const int kp = k0 + half * VEC;  // this lane's first pixel
-    uint4 a[MB];
+        for (int q = 0; q < 16; ++q) acc[mb][j][q] = 0.f;
+    for (int ho = ho0; ho < ho1; ++ho) {
+      __syncthreads();
+      for (int e = tid; e < 32 * xrow; e += 256) {
+        const int cc = e / xrow, rr = e - cc * xrow;
+        const int i = rr / p.XS, xi = rr - i * p.XS;
+        const int y = ho * p.SH - p.PH + i * p.DH, xx = xi - p.PW;
+        const int ch = cs * 32 + cc;
+        T v = zero_elem<T>();
+        if (ch < p.Cin && (unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
+          v = x[(((size_t)n * p.Cin + ch) * p.H + y) * p.W + xx];
+        xs[e] = v;
+      }
+      for (int e = tid; e < MB * 32 * p.DLS; e += 256) {
+        const int o = e / p.DLS, wo = e - o * p.DLS;
+        float v = 0.f;
+        if (o < p.orows && wo < p.Wo) v = doff[(size_t)(p.o0 + o) * HoWo + (size_t)ho * p.Wo + wo];
+        dl[e] = Elem<T>::from_f32(v);
+      }
+      __syncthreads();
+      for (int kc = 0; kc < p.WoP; kc += KC) {
+        const int w0 = kc + half * VEC;
+        uint4 a[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int o = p.o0 + mb * 32 + (lane & 31);
-      float f[VEC];
+        for (int mb = 0; mb < MB; ++mb) a[mb] = *(const uint4*)(dl + (mb * 32 + cl) * p.DLS + w0);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        f[e] = (o < p.o0 + p.orows && kp + e < pb1) ? doff[(size_t)o * HoWo + kp + e] : 0.f;
-      if constexpr (VEC == 8) {
-        a[mb] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                           pack_bf16x2(f[6], f[7]));
-      } else {
-        a[mb] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                           __float_as_uint(f[3]));
+        for (int j = 0; j < 3; ++j) {
+          const int t = tg + wave + 4 * j;
+          if (t >= p.K2) break;
+          const int ti = t / p.KW, tj = t - ti * p.KW;
+          const T* src = xs + (cl * p.KH + ti) * p.XS + tj * p.DW + w0 * p.SH;
+          T v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = src[e * p.SH];
+          const uint4 b = *(const uint4*)v;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][j], a[mb], b, T());
+        }
       }
     }
-    int ho[VEC], wo[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int q = kp + e;
-      ho[e] = q / p.Wo;
-      wo[e] = q - ho[e] * p.Wo;
-    }
+    float* part = p.part + (size_t)(n * p.bands + band) * p.Oc * p.K2 * p.Cin;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int t = tg + wave + 4 * j;
       if (t >= p.K2) break;
-      const int ti = t / p.KW, tj = t - ti * p.KW;
-      float f[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int yy = ho[e] * p.SH - p.PH + ti * p.DH, xx = wo[e] * p.SW - p.PW + tj * p.DW;
-        f[e] = (cval && kp + e < pb1 && (unsigned)yy < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
-                   ? Elem<T>::to_f32(xc[(size_t)yy * p.W + xx])
-                   : 0.f;
-      }
-      uint4 b;
-      if constexpr (VEC == 8) {
-        b = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                       pack_bf16x2(f[6], f[7]));
-      } else {
-        b = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-      }
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][j], a[mb], b, T());
+        for (int q = 0; q < 16; ++q) {
+          const int o = mb * 32 + acc_row(lane, q);
+          if (o < p.orows && c < p.Cin) part[((size_t)(p.o0 + o) * p.K2 + t) * p.Cin + c] = acc[mb][j][q];
+        }
     }
-  }
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int t = tg + wave + 4 * j;
-    if (t >= p.K2) break;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int o = p.o0 + mb * 32 + acc_row(lane, q);
-        if (o < p.o0 + p.orows && cval) atomicAdd(p.dwoff32 + ((size_t)o * p.K2 + t) * p.Cin + c, acc[mb][j][q]);
-      }
-  }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dX_offset, the transposed offset convolution, plus the sampling part of dX
-// accumulated so far, rounded once: dx[n][c][y][x] = dtype(dx32 + sum over
-// (o, tap) of W_off[o][c][tap] * dOff[o][ho][wo]) with (y, x) the tap's grid
-// position of (ho, wo).  GEMM with rows c (one 32-channel block per wave),
-// columns = 64 input pixels, depth kk = o*K2 + tap (padded to KKP).  The B
-// tile [pixel][kk] is built once per workgroup in LDS.
-struct DxoffParams {
+// Final dX: dx[n][c][y][x] = dtype(dX_offset + the sampling part of dX).
+// dX_offset is a GEMM with rows c (one 32-channel block per wave), columns =
+// 64 input pixels, depth kk = o*K2 + tap (padded to KKP, in chunks of KKC);
+// its B tile [pixel][kk] (dOffset at the output pixel whose tap lands on the
+// input pixel, or 0) is built in LDS.
+struct DxParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc, KKP, KKC;
   int pix_blocks, cblocks, num_wg;
   const void* wofft;  // [Cin][KKP]
   const float* doff;
-  const float* dx32;
+  const float* dxs;   // sampling part of dX, fp32
   void* dx;
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_dx_off(const DxoffParams p) {
+__global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
   constexpr int VEC = Elem<T>::VEC;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -342,8 +500,8 @@ __global__ __launch_bounds__(256) void k_dx_off(const DxoffParams p) {
   const int pbk = r / p.cblocks, cb = r - pbk * p.cblocks;
   const int HW = p.H * p.W, HoWo = p.Ho * p.Wo;
   const int pix0 = pbk * 64;
-  const int bstr = p.KKC + VEC;  // LDS row stride (elements)
-  T* bt = (T*)smem;              // [64][bstr]
+  const int bstr = p.KKC + VEC;
+  T* bt = (T*)smem;  // [64][bstr]
   const float* __restrict__ doff = p.doff + (size_t)n * p.Oc * HoWo;
   const int c0 = cb * 128 + wave * 32;
   const bool active = c0 < p.Cin;
@@ -398,7 +556,7 @@ __global__ __launch_bounds__(256) void k_dx_off(const DxoffParams p) {
       const int cc = c0 + acc_row(lane, r2);
       if (cc < p.Cin) {
         const size_t idx = ((size_t)n * p.Cin + cc) * HW + q;
-        dx[idx] = Elem<T>::from_f32(p.dx32[idx] + acc[j][r2]);
+        dx[idx] = Elem<T>::from_f32(acc[j][r2] + p.dxs[idx]);
       }
     }
   }
@@ -406,14 +564,14 @@ __global__ __launch_bounds__(256) void k_dx_off(const DxoffParams p) {
 
 // ---------------------------------------------------------------------------
 // Prep: W2[(t,c)][co] = W[co][c][t]; WoffT[c][o*K2+t] = W_off[o][c][t] (zero
-// for kk >= Oc*K2); fp32 accumulators zeroed.
+// for kk >= Oc*K2); the nz0 floats at z0 zeroed.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_backward(const T* __restrict__ w, const T* __restrict__ w_off, T* w2,
-                                                       T* wofft, float* z0, size_t nz0, float* z1, size_t nz1,
-                                                       float* z2, size_t nz2, int Cout, int Cin, int K2, int Oc,
-                                                       int KKP) {
+                                                       T* wofft, float* z0, size_t nz0, int Cout, int Cin, int K2,
+                                                       int Oc, int KKP) {
   const size_t n1 = (size_t)Cout * K2 * Cin, n2 = (size_t)Cin * KKP;
-  const size_t total = n1 + n2 + nz0 + nz1 + nz2;
+  const size_t nz4 = nz0 / 4;
+  const size_t total = n1 + n2 + nz4 + (nz0 & 3);
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     if (e < n1) {
       const int co = (int)(e % Cout);
@@ -426,60 +584,68 @@ __global__ __launch_bounds__(256) void k_prep_backward(const T* __restrict__ w, 
       const int kk = (int)(f % KKP);
       const int c = (int)(f / KKP);
       wofft[f] = kk < Oc * K2 ? w_off[((size_t)(kk / K2) * Cin + c) * K2 + kk % K2] : zero_elem<T>();
+    } else if (e < n1 + n2 + nz4) {
+      ((float4*)z0)[e - n1 - n2] = make_float4(0.f, 0.f, 0.f, 0.f);
     } else {
-      size_t f = e - n1 - n2;
-      if (f < nz0) { z0[f] = 0.f; continue; }
-      f -= nz0;
-      if (f < nz1) { z1[f] = 0.f; continue; }
-      f -= nz1;
-      z2[f] = 0.f;
+      z0[nz4 * 4 + (e - n1 - n2 - nz4)] = 0.f;
     }
   }
 }
 
-// dw[co][c][t] = dtype(dw32[co][t][c]); dw_off likewise.
+// Per-(channel, image) sums: part[ch][n] = sum over pixels of dY (ch < Cout)
+// or of dOffset (ch >= Cout).  Fixed-order tree reduction.
 template <typename T>
-__global__ __launch_bounds__(256) void k_finalize_w(const float* __restrict__ dw32, T* dw, int Cout,
-                                                    const float* __restrict__ dwoff32, T* dwoff, int Oc, int Cin,
-                                                    int K2) {
-  const size_t n1 = (size_t)Cout * Cin * K2, n2 = (size_t)Oc * Cin * K2;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * 256) {
-    const bool first = e < n1;
-    const size_t f = first ? e : e - n1;
-    const int t = (int)(f % K2);
-    const size_t r = f / K2;
-    const int c = (int)(r % Cin);
-    const size_t o = r / Cin;
-    const float v = (first ? dw32 : dwoff32)[(o * K2 + t) * Cin + c];
-    (first ? dw : dwoff)[f] = Elem<T>::from_f32(v);
-  }
-}
-
-// db[co] = sum over (n, pixel) of dY; db_off[o] = sum of dOff.  One workgroup
-// per output channel, fixed-order tree reduction.
-template <typename T>
-__global__ __launch_bounds__(256) void k_bias_sums(const T* __restrict__ dy, T* db, int Cout, const float* __restrict__ doff,
-                                                   T* dboff, int Oc, int N, int HoWo) {
+__global__ __launch_bounds__(256) void k_bias_partial(const T* __restrict__ dy, const float* __restrict__ doff,
+                                                      float* part, int Cout, int Oc, int N, int HoWo) {
   __shared__ float red[256];
-  const int ch = blockIdx.x;
+  const int ch = blockIdx.x, n = blockIdx.y;
   const bool main = ch < Cout;
-  if (main && !db) return;
-  if (!main && !dboff) return;
   const int o = main ? ch : ch - Cout;
-  const int C = main ? Cout : Oc;
+  const size_t base = ((size_t)n * (main ? Cout : Oc) + o) * HoWo;
   float s = 0.f;
-  for (int n = 0; n < N; ++n) {
-    const size_t base = ((size_t)n * C + o) * HoWo;
-    for (int q = threadIdx.x; q < HoWo; q += 256)
-      s += main ? Elem<T>::to_f32(dy[base + q]) : doff[base + q];
-  }
+  for (int q = threadIdx.x; q < HoWo; q += 256) s += main ? Elem<T>::to_f32(dy[base + q]) : doff[base + q];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) (main ? db : dboff)[o] = Elem<T>::from_f32(red[0]);
+  if (threadIdx.x == 0) part[(size_t)ch * N + n] = red[0];
+}
+
+// All weight and bias gradients from their partials, summed in a fixed order
+// and rounded once: dw[co][c][t] (from [N][co][t][c]), dw_off[o][c][t] (from
+// [N*bands][o][t][c]), db, db_off (from [ch][N]).
+template <typename T>
+__global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ dwpart, T* dw, int Cout,
+                                                      const float* __restrict__ dwoffpart, T* dwoff, int Oc, int nwp,
+                                                      const float* __restrict__ bpart, T* db, T* dboff, int N, int Cin,
+                                                      int K2) {
+  const size_t ck = (size_t)Cin * K2;
+  const size_t n1 = (size_t)Cout * ck, n2 = (size_t)Oc * ck, n3 = (size_t)Cout + Oc;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2 + n3; e += (size_t)gridDim.x * 256) {
+    if (e < n1 + n2) {
+      const bool first = e < n1;
+      const size_t f = first ? e : e - n1;  // partial order: [o][t][c]
+      const int c = (int)(f % Cin);
+      const size_t r = f / Cin;
+      const int t = (int)(r % K2);
+      const size_t o = r / K2;
+      const float* src = first ? dwpart : dwoffpart;
+      const size_t stride = first ? n1 : n2;
+      const int cnt = first ? N : nwp;
+      float s = 0.f;
+      for (int z = 0; z < cnt; ++z) s += src[(size_t)z * stride + f];
+      (first ? dw : dwoff)[(o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
+    } else {
+      const int ch = (int)(e - n1 - n2);
+      T* dst = ch < Cout ? db : dboff;
+      if (!dst) continue;
+      float s = 0.f;
+      for (int z = 0; z < N; ++z) s += bpart[(size_t)ch * N + z];
+      dst[ch < Cout ? ch : ch - Cout] = Elem<T>::from_f32(s);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -497,76 +663,104 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   T* wofft = (T*)(ws + p.ws_wofft);
   T* dcol = (T*)(ws + p.ws_dcol);
   const T* cols = (const T*)(ws + p.ws_cols);
-  float* dx32 = (float*)(ws + p.ws_dx32);
-  float* dw32 = (float*)(ws + p.ws_dw32);
-  float* dwoff32 = (float*)(ws + p.ws_dwoff32);
+  float* dxs = (float*)(ws + p.ws_dx32);
   float* doff = (float*)(ws + p.ws_doff);
-  const size_t ndx = (size_t)d.n * d.c_in * d.h * d.w;
-  const size_t ndw = (size_t)d.c_out * p.ck, ndwoff = (size_t)p.oc * p.ck;
+  float* doffp = (float*)(ws + p.ws_doffp);
+  uint32_t* maxbits = (uint32_t*)(ws + p.ws_maxbits);
+  int4* lists = (int4*)(ws + p.ws_list);
+  float* dwpart = (float*)(ws + p.ws_dwpart);
+  float* dwoffpart = (float*)(ws + p.ws_dwoffpart);
+  float* bpart = (float*)(ws + p.ws_biaspart);
+  const size_t ndoff = (size_t)d.n * p.oc * p.ho * p.wo;
+  hipError_t e;
   {
-    const size_t total = (size_t)d.c_out * p.ck + (size_t)d.c_in * p.kk_pad + ndx + ndw + ndwoff;
-    DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid_cap(total, 8192)), dim3(256), 0, st, (const T*)a.w,
-                       (const T*)a.w_off, w2, wofft, dx32, ndx, dw32, ndw, dwoff32, ndwoff, d.c_out, d.c_in,
-                       p.taps, p.oc, p.kk_pad);
-    hipError_t e = hipGetLastError();
+    // zero: the dOffset partials (fully outside taps keep 0) and the max |dCol|
+    // word that follows them
+    const size_t nz = ndoff * (size_t)(p.cg / p.chunk_b) + 4;
+    const size_t total = (size_t)d.c_out * p.ck + (size_t)d.c_in * p.kk_pad + nz / 4 + 4;
+    DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid_cap(total, 8192)), dim3(256), 0, st,
+                (const T*)a.w, (const T*)a.w_off, w2, wofft, doffp, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_gemm_dcol(p, w2, a.dy, dcol, st);
+  e = launch_gemm_dcol(p, w2, a.dy, dcol, maxbits, st);
   if (e != hipSuccess) return e;
-  e = launch_gemm_dw(p, a.dy, cols, dw32, st);
+  e = launch_gemm_dw(p, a.dy, cols, dwpart, st);
   if (e != hipSuccess) return e;
 
-  // sampling backward
+  // sampling backward, the taps beyond the halo, then dOffset
   {
     BwdParams b;
     b.N = d.n; b.Cin = d.c_in; b.H = d.h; b.W = d.w; b.Ho = p.ho; b.Wo = p.wo; b.KH = d.kh; b.KW = d.kw;
     b.SH = d.stride_h; b.SW = d.stride_w; b.PH = d.pad_h; b.PW = d.pad_w; b.DH = d.dil_h; b.DW = d.dil_w;
-    b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck; b.Cout = d.c_out;
-    b.TH = p.tile_h; b.TW = p.tile_w; b.halo = p.halo; b.CC = p.chunk_b; b.GW = p.gw; b.gsplit = p.gsplit;
-    b.tiles_h = p.tiles_h; b.tiles_w = p.tiles_w; b.num_wg = p.num_wg; b.FH = p.foot_h; b.FW = p.foot_w;
-    b.pstr = p.pstr_b; b.dstr = p.dstr_b;
-    int l = 0;
-    while ((1 << l) < (p.chunk_b >> 3)) ++l;
-    b.lognv = l;
-    b.lds_x = p.lb_x; b.lds_dx = p.lb_dx; b.lds_off = p.lb_off; b.lds_info = p.lb_info; b.lds_doff = p.lb_doff;
-    b.div_tw = make_fastdiv(p.tile_w); b.div_k2 = make_fastdiv(p.taps);
-    b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.dx32 = dx32; b.doff = doff;
+    b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck;
+    b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
+    b.CC = p.chunk_b;
+    b.dcstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
+    b.num_wg = p.num_btiles * d.offset_groups; b.list_cap = p.list_cap;
+    int cb = 0;
+    while ((1 << cb) < p.list_cap + 1) ++cb;
+    b.capbits = cb;
+    b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 2 : 1);
+    b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
+    b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
+    b.lists = lists;
     auto kern = k_sample_bwd<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
     if (e != hipSuccess) return e;
-    if (p.num_wg) DEFT_LAUNCH("sample_backward", kern, dim3(p.num_wg), dim3(256), p.lb_total, st, b);
+    if (b.num_wg) DEFT_LAUNCH("sample_backward", kern, dim3(b.num_wg), dim3(256), p.lb_total, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t pairs = (size_t)d.n * d.offset_groups * p.taps * p.ho * p.wo;
+    DEFT_LAUNCH("sample_backward_miss", k_sample_bwd_miss<T>, dim3(grid_cap(pairs, 2048)), dim3(256), 0, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int chunks = p.cg / p.chunk_b;
+    DEFT_LAUNCH("doff_sum", k_doff_sum, dim3(grid_cap(ndoff, 2048)), dim3(256), 0, st, doffp, doff, ndoff, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // offset-conv weight gradient
+  // offset-conv weight gradient partials
   {
     WoffParams w;
     w.N = d.n; w.Cin = d.c_in; w.H = d.h; w.W = d.w; w.Ho = p.ho; w.Wo = p.wo; w.KH = d.kh; w.KW = d.kw;
     w.SH = d.stride_h; w.SW = d.stride_w; w.PH = d.pad_h; w.PW = d.pad_w; w.DH = d.dil_h; w.DW = d.dil_w;
     w.K2 = p.taps; w.Oc = p.oc;
     w.slices = (d.c_in + 31) / 32;
-    const int howo = p.ho * p.wo;
-    int bands = 1;
-    while (d.n * w.slices * bands < 256 && bands * 64 < howo) bands *= 2;
-    const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
-    w.band_pix = ((howo + bands - 1) / bands + kc - 1) / kc * kc;
-    w.bands = (howo + w.band_pix - 1) / w.band_pix;
+    w.bands = p.woff_bands;
+    w.band_rows = (p.ho + w.bands - 1) / w.bands;
     w.num_wg = d.n * w.slices * w.bands;
-    w.x = a.x; w.doff = doff; w.dwoff32 = dwoff32;
+    const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
+    w.WoP = (p.wo + kc - 1) / kc * kc;
+    w.XS = (w.WoP - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;
+    w.DLS = w.WoP + (d.dtype == DEFT_BF16 ? 8 : 4);
+    w.x = a.x; w.doff = doff; w.part = dwoffpart;
     for (int o0 = 0; o0 < p.oc && w.num_wg; o0 += 96) {
       w.o0 = o0;
       w.orows = p.oc - o0 < 96 ? p.oc - o0 : 96;
       const int mb = (w.orows + 31) / 32;
-      if (mb == 1) DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 1>), dim3(w.num_wg), dim3(256), 0, st, w);
-      else if (mb == 2) DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 2>), dim3(w.num_wg), dim3(256), 0, st, w);
-      else DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 3>), dim3(w.num_wg), dim3(256), 0, st, w);
+      const int lds = ((32 * d.kh * w.XS * (int)sizeof(T) + 15) & ~15) + mb * 32 * w.DLS * (int)sizeof(T);
+      if (mb == 1) {
+        e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 1>), dim3(w.num_wg), dim3(256), lds, st, w);
+      } else if (mb == 2) {
+        e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 2>), dim3(w.num_wg), dim3(256), lds, st, w);
+      } else {
+        e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 3>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 3>), dim3(w.num_wg), dim3(256), lds, st, w);
+      }
+      if (e != hipSuccess) return e;
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  // dX_offset + final dx
+  // final dX
   {
-    DxoffParams q;
+    DxParams q;
     q.N = d.n; q.Cin = d.c_in; q.H = d.h; q.W = d.w; q.Ho = p.ho; q.Wo = p.wo; q.KH = d.kh; q.KW = d.kw;
     q.SH = d.stride_h; q.SW = d.stride_w; q.PH = d.pad_h; q.PW = d.pad_w; q.DH = d.dil_h; q.DW = d.dil_w;
     q.K2 = p.taps; q.Oc = p.oc; q.KKP = p.kk_pad;
@@ -574,23 +768,23 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     q.pix_blocks = (d.h * d.w + 63) / 64;
     q.cblocks = (d.c_in + 127) / 128;
     q.num_wg = d.n * q.pix_blocks * q.cblocks;
-    q.wofft = wofft; q.doff = doff; q.dx32 = dx32; q.dx = a.dx;
+    q.wofft = wofft; q.doff = doff; q.dxs = dxs; q.dx = a.dx;
     const int lds = 64 * (q.KKC + (d.dtype == DEFT_BF16 ? 8 : 4)) * (int)sizeof(T);
-    auto kern = k_dx_off<T>;
+    auto kern = k_dx_final<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    if (q.num_wg) DEFT_LAUNCH("offset_input_backward", kern, dim3(q.num_wg), dim3(256), lds, st, q);
+    if (q.num_wg) DEFT_LAUNCH("dx_final", kern, dim3(q.num_wg), dim3(256), lds, st, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // weights and biases
+  // bias partials, then every weight / bias gradient
   {
-    const size_t total = ((size_t)d.c_out + p.oc) * d.c_in * p.taps;
-    DEFT_LAUNCH("finalize_weights", k_finalize_w<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dw32, (T*)a.dw, d.c_out,
-                       dwoff32, (T*)a.dw_off, p.oc, d.c_in, p.taps);
-    if (a.db || a.db_off)
-      DEFT_LAUNCH("bias_sums", k_bias_sums<T>, dim3(d.c_out + p.oc), dim3(256), 0, st, (const T*)a.dy, (T*)a.db, d.c_out,
-                         doff, (T*)a.db_off, p.oc, d.n, p.ho * p.wo);
+    DEFT_LAUNCH("bias_partial", k_bias_partial<T>, dim3(d.c_out + p.oc, d.n), dim3(256), 0, st, (const T*)a.dy, doff,
+                bpart, d.c_out, p.oc, d.n, p.ho * p.wo);
+    const size_t total = ((size_t)d.c_out + p.oc) * p.ck + d.c_out + p.oc;
+    DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dwpart, (T*)a.dw,
+                d.c_out, dwoffpart, (T*)a.dw_off, p.oc, d.n * p.woff_bands, bpart, (T*)a.db, (T*)a.db_off, d.n,
+                d.c_in, p.taps);
     e = hipGetLastError();
   }
   return e;

@@ -209,6 +209,7 @@ struct DcolOp {
   const T* A;   // W2 [M=Ck][K=Cout]
   const T* dy;  // [N_img][Cout][HoWo]
   T* dcol;      // [N][M]
+  uint32_t* maxbits;  // running max of |dcol| as fp32 bits (zeroed before the launch)
   int M, N, K, HoWo, tilesM, tilesN, BM, BN;
   bool vec_ok;  // HoWo % VEC == 0
   __device__ TileCoord tile(int bid) const {
@@ -243,6 +244,21 @@ struct DcolOp {
   }
   __device__ void store(const TileCoord&, int mb, int nb, const f32x16_t& acc, int lane) const {
     const int q = nb + (lane & 31);
+    // max |value| of this block (valid entries only), one atomic per wave
+    float mx = 0.f;
+    if (q < N) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e0 = mb + 8 * j + 4 * (lane >> 5);
+        if (e0 < M)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[4 * j + r]));
+      }
+    }
+    for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+    // most blocks do not raise the running max: skip their atomics
+    if (lane == 0 && __float_as_uint(mx) > __hip_atomic_load(maxbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(maxbits, __float_as_uint(mx));
     if (q >= N) return;
     T* row = dcol + (size_t)q * M;
 #pragma unroll
@@ -261,13 +277,13 @@ struct DcolOp {
   }
 };
 
-// ---- backward dW (split over images): dw32[co][e] += sum_p dY[n][co][p] Col[n*HoWo+p][e] ----
+// ---- backward dW, one partial per image: dwpart[n][co][e] = sum_p dY[n][co][p] Col[n*HoWo+p][e] ----
 template <typename T>
 struct DwOp {
   static constexpr bool B_KMAJOR = true;
   const T* dy;    // A: [N_img][M=Cout][HoWo]
   const T* cols;  // B': [N_img*HoWo][Ck]
-  float* dw32;    // [M][Ncols]
+  float* dwpart;  // [N_img][M][Ncols]
   int M, Ncols, HoWo, tilesM, tilesN, nimg, BM, BN;
   bool vec_ok;
   __device__ TileCoord tile(int bid) const {
@@ -287,13 +303,14 @@ struct DwOp {
     if (k >= HoWo || n >= Ncols) return make_uint4(0, 0, 0, 0);
     return *(const uint4*)(cols + ((size_t)tc.z * HoWo + k) * Ncols + n);
   }
-  __device__ void store(const TileCoord&, int mb, int nb, const f32x16_t& acc, int lane) const {
+  __device__ void store(const TileCoord& tc, int mb, int nb, const f32x16_t& acc, int lane) const {
     const int n = nb + (lane & 31);
     if (n >= Ncols) return;
+    float* part = dwpart + (size_t)tc.z * M * Ncols;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = mb + acc_row(lane, r);
-      if (m < M) atomicAdd(dw32 + (size_t)m * Ncols + n, acc[r]);
+      if (m < M) part[(size_t)m * Ncols + n] = acc[r];
     }
   }
 };
@@ -336,10 +353,11 @@ hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* c
 }
 
 template <typename T>
-hipError_t gemm_dcol_t(const deft_plan& p, const void* w2, const void* dy, void* dcol, hipStream_t st) {
+hipError_t gemm_dcol_t(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
+                       hipStream_t st) {
   const char* GEMM_NAME = "gemm_dcol";
   DcolOp<T> op;
-  op.A = (const T*)w2; op.dy = (const T*)dy; op.dcol = (T*)dcol;
+  op.A = (const T*)w2; op.dy = (const T*)dy; op.dcol = (T*)dcol; op.maxbits = maxbits;
   op.M = p.ck; op.N = p.d.n * p.ho * p.wo; op.K = p.d.c_out; op.HoWo = p.ho * p.wo;
   op.vec_ok = (op.HoWo % Elem<T>::VEC) == 0;
   op.BM = 256; op.BN = 128;
@@ -349,10 +367,10 @@ hipError_t gemm_dcol_t(const deft_plan& p, const void* w2, const void* dy, void*
 }
 
 template <typename T>
-hipError_t gemm_dw_t(const deft_plan& p, const void* dy, const void* cols, float* dw32, hipStream_t st) {
+hipError_t gemm_dw_t(const deft_plan& p, const void* dy, const void* cols, float* dwpart, hipStream_t st) {
   const char* GEMM_NAME = "gemm_dw";
   DwOp<T> op;
-  op.dy = (const T*)dy; op.cols = (const T*)cols; op.dw32 = dw32;
+  op.dy = (const T*)dy; op.cols = (const T*)cols; op.dwpart = dwpart;
   op.M = p.d.c_out; op.Ncols = p.ck; op.HoWo = p.ho * p.wo; op.nimg = p.d.n;
   op.vec_ok = (op.HoWo % Elem<T>::VEC) == 0;
   op.BN = 128;
@@ -368,11 +386,14 @@ hipError_t gemm_dw_t(const deft_plan& p, const void* dy, const void* cols, float
   return run_gemm<T, 64, 128>(GEMM_NAME, op, op.tilesN * op.nimg, st);
 }
 
-hipError_t launch_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, hipStream_t st) {
-  return p.d.dtype == DEFT_BF16 ? gemm_dcol_t<bf16_t>(p, w2, dy, dcol, st) : gemm_dcol_t<float>(p, w2, dy, dcol, st);
+hipError_t launch_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
+                            hipStream_t st) {
+  return p.d.dtype == DEFT_BF16 ? gemm_dcol_t<bf16_t>(p, w2, dy, dcol, maxbits, st)
+                                : gemm_dcol_t<float>(p, w2, dy, dcol, maxbits, st);
 }
-hipError_t launch_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* dw32, hipStream_t st) {
-  return p.d.dtype == DEFT_BF16 ? gemm_dw_t<bf16_t>(p, dy, cols, dw32, st) : gemm_dw_t<float>(p, dy, cols, dw32, st);
+hipError_t launch_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* dwpart, hipStream_t st) {
+  return p.d.dtype == DEFT_BF16 ? gemm_dw_t<bf16_t>(p, dy, cols, dwpart, st)
+                                : gemm_dw_t<float>(p, dy, cols, dwpart, st);
 }
 
 }  // namespace deft

@@ -69,6 +69,47 @@ Shape shape_of(const deft_desc& d) {
   return s;
 }
 
+// Backward tiling: the sampling backward gives each workgroup a core tile of
+// input pixels; it gathers the (output pixel, tap) pairs whose corners touch
+// the core (within the halo) into a list, then per channel chunk scatters
+// dCol x weight into an fp32 LDS copy of the core (lanes = channels) and
+// writes the core's dX once.  A pair straddling two cores is read by both, so
+// larger cores read dCol fewer times; the LDS holds the core plus a one-pixel
+// ring of the input (for the offset gradient) and the fp32 core.
+bool layout_backward(deft_plan& p) {
+  const deft_desc& d = p.d;
+  const Shape s = shape_of(d);
+  // 8x8 cores keep several workgroups per CU; chunk = 64 channels (one per
+  // lane) when the group allows it
+  const int ch = std::min(8, d.h), cw = std::min(8, d.w);
+  int cb = 64;
+  while (cb > 16 && s.cg % cb) cb /= 2;
+  if (s.cg % cb) return false;
+  const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
+  const int xstr = cb + (d.dtype == DEFT_BF16 ? 2 : 1);
+  const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
+  const int ldx = align16(ch * cw * cb * 8);  // 64-bit fixed-point dX of the core
+  const int ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
+  const int total = lx + ldx + ldc + 16 + 4 * 49 * 4;  // + list counter and per-tap tables
+  if (total > kMaxLds) return false;
+  p.btile_h = ch; p.btile_w = cw;
+  p.btiles_h = (d.h + ch - 1) / ch; p.btiles_w = (d.w + cw - 1) / cw;
+  p.num_btiles = d.n * p.btiles_h * p.btiles_w;
+  p.chunk_b = cb;
+  p.lb_dx = lx; p.lb_dc = lx + ldx; p.lb_cnt = lx + ldx + ldc; p.lb_total = total;
+  // list capacity: every output pixel whose tap's grid point lies within the
+  // halo (plus one row/column for the +1 corners) of the core, for every tap
+  const int wh = (p.btile_h + 2 * p.halo + 1 + d.stride_h - 1) / d.stride_h + 1;
+  const int ww = (p.btile_w + 2 * p.halo + 1 + d.stride_w - 1) / d.stride_w + 1;
+  p.list_cap = s.taps * std::min(wh, s.ho) * std::min(ww, s.wo);
+  // offset-weight backward: enough (image, channel slice, row band) workgroups
+  const int slices = (d.c_in + 31) / 32;
+  int bands = 1;
+  while ((double)d.n * slices * bands < 512 && bands * 2 <= s.ho) bands *= 2;
+  p.woff_bands = bands;
+  return true;
+}
+
 // Fills every derived field of a plan for the given tile / halo / chunk.
 // Returns false if the LDS does not fit.
 bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
@@ -101,23 +142,8 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   p.lds_info = p.lds_off + align16(ocw * pt * 4);
   p.lds_total = p.lds_info + p.gw * s.taps * pt * 16;
   if (p.lds_total > kMaxLds) return false;
-  // backward sampling kernel: its own chunk (<= 32), shrunk until the LDS
-  // fits; chunk_b = 0 marks a plan whose backward does not fit.
-  p.chunk_b = 0;
-  for (int cb = std::min(chunk, 32); cb >= 8; cb /= 2) {
-    if (s.cg % cb) continue;
-    p.chunk_b = cb;
-    p.pstr_b = cb + vec;
-    p.dstr_b = cb + 1;
-    p.lb_x = 0;
-    p.lb_dx = align16(p.reg_h * p.reg_w * p.pstr_b * s.esz);
-    p.lb_off = p.lb_dx + align16(p.reg_h * p.reg_w * p.dstr_b * 4);
-    p.lb_info = p.lb_off + align16(ocw * pt * 4);
-    p.lb_doff = p.lb_info + p.gw * s.taps * pt * 16;
-    p.lb_total = p.lb_doff + p.gw * s.taps * pt * 8;
-    if (p.lb_total <= kMaxLds) break;
-    p.chunk_b = 0;
-  }
+  p.num_btiles = 0; p.list_cap = 0; p.woff_bands = 1;
+  if (!layout_backward(p)) p.chunk_b = 0;
   // workspace
   const size_t P = (size_t)d.n * s.ho * s.wo;
   p.kk_pad = (s.oc * s.taps + 15) / 16 * 16;
@@ -130,9 +156,18 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   p.ws_wofft = o; o = align256(o + (size_t)d.c_in * p.kk_pad * s.esz);
   p.ws_dcol = o; o = align256(o + P * s.ck * s.esz);
   p.ws_dx32 = o; o = align256(o + (size_t)d.n * d.c_in * d.h * d.w * 4);
-  p.ws_dw32 = o; o = align256(o + (size_t)d.c_out * s.ck * 4);
-  p.ws_dwoff32 = o; o = align256(o + (size_t)s.oc * s.ck * 4);
   p.ws_doff = o; o = align256(o + P * s.oc * 4);
+  p.ws_list = o;
+  o = align256(o + (size_t)p.num_btiles * d.offset_groups * p.list_cap * 16);
+  // dOffset partials (one per backward channel chunk) followed by one word
+  // for max |dCol|; both zeroed by the backward's prep kernel
+  p.ws_doffp = o;
+  const size_t nchunks = p.chunk_b ? (size_t)(s.cg / p.chunk_b) : 1;
+  p.ws_maxbits = p.ws_doffp + nchunks * P * s.oc * 4;
+  o = align256(p.ws_maxbits + 16);
+  p.ws_dwpart = o; o = align256(o + (size_t)d.n * d.c_out * s.ck * 4);
+  p.ws_dwoffpart = o; o = align256(o + (size_t)d.n * p.woff_bands * s.oc * s.ck * 4);
+  p.ws_biaspart = o; o = align256(o + (size_t)(d.c_out + s.oc) * d.n * 4);
   p.ws_train_end = o;
   return true;
 }
@@ -250,6 +285,7 @@ int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo
   deft_plan* p = new (std::nothrow) deft_plan();
   if (!p) return DEFT_ERR_UNSUPPORTED;
   p->d = *d;
+  p->num_btiles = 0;
   bool ok = false;
   if (chunk != 0) {
     ok = layout_plan(*p, tile_h, tile_w, halo, chunk);
@@ -276,6 +312,9 @@ int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
   info->ws_forward = p->ws_fwd_end;
   info->ws_training = p->ws_train_end;
   info->ws_cols_offset = p->ws_cols;
+  info->bwd_tile_h = p->btile_h;
+  info->bwd_tile_w = p->btile_w;
+  info->bwd_chunk = p->chunk_b;
   return DEFT_OK;
 }
 

@@ -21,11 +21,14 @@ struct deft_plan {
   double est_miss;
   // workspace layout (byte offsets, 256-aligned)
   size_t ws_wt, ws_woff, ws_cols, ws_fwd_end;
-  size_t ws_w2, ws_dcol, ws_dx32, ws_dw32, ws_dwoff32, ws_doff, ws_wofft, ws_train_end;
+  size_t ws_w2, ws_dcol, ws_dx32, ws_doff, ws_wofft, ws_train_end;
   int kk_pad;                  // padded (o, tap) depth of the transposed offset conv
-  // sampling backward (same tiles, its own channel chunk)
-  int chunk_b, pstr_b, dstr_b;
-  int lb_x, lb_dx, lb_off, lb_info, lb_doff, lb_total;
+  // sampling backward: each workgroup owns a core tile of input pixels
+  // (btile_h x btile_w) and the (output pixel, tap) pairs that touch it
+  int btile_h, btile_w, btiles_h, btiles_w, num_btiles, list_cap;
+  int chunk_b, lb_dx, lb_dc, lb_cnt, lb_total;
+  int woff_bands;              // row bands of the offset-weight backward
+  size_t ws_list, ws_doffp, ws_maxbits, ws_dwpart, ws_dwoffpart, ws_biaspart;
 };
 
 namespace deft {
