@@ -54,6 +54,9 @@ def main():
     ap.add_argument("--workload", default="train_bf16_n16_c256_56x56_s1")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times) after the timed steps, as the "
+                         "reference kernel for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -118,6 +121,14 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
     log("timed: %d steps, %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall))
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dstc = torch.empty_like(src)
+        for _ in range(3):
+            dstc.copy_(src)
+        torch.cuda.synchronize()
+        del src, dstc
 
     # instrumented pass: per-kernel durations from events around each launch
     L.deft_timing_start(64 * args.steps)
