@@ -84,6 +84,10 @@ typedef struct deft_plan_info {
                              [N*Ho*Wo][kh*kw][Cin] that deft_forward leaves there */
   int bwd_tile_h, bwd_tile_w; /* output tile of the sampling backward */
   int bwd_chunk;          /* its channel chunk; 0: this plan has no backward (LDS) */
+  int gemm_direct;        /* 1: the three GEMMs stage operands with direct global-to-LDS
+                             loads (bf16, Ho*Wo and c_out multiples of 8, operands under
+                             2 GiB); 0: register-staged generic GEMM */
+  int dw_splits;          /* pixel ranges the dW GEMM is split into (one fp32 partial each) */
 } deft_plan_info;
 
 /* Checks the descriptor alone.  Pure host function. */

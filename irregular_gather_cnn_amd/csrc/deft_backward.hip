@@ -614,10 +614,11 @@ __global__ __launch_bounds__(256) void k_bias_partial(const T* __restrict__ dy, 
 }
 
 // All weight and bias gradients from their partials, summed in a fixed order
-// and rounded once: dw[co][c][t] (from [N][co][t][c]), dw_off[o][c][t] (from
+// and rounded once: dw[co][c][t] (from [ndw][co][t][c], one partial per
+// pixel range of the dW GEMM), dw_off[o][c][t] (from
 // [N*bands][o][t][c]), db, db_off (from [ch][N]).
 template <typename T>
-__global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ dwpart, T* dw, int Cout,
+__global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ dwpart, int ndw, T* dw, int Cout,
                                                       const float* __restrict__ dwoffpart, T* dwoff, int Oc, int nwp,
                                                       const float* __restrict__ bpart, T* db, T* dboff, int N, int Cin,
                                                       int K2) {
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ 
       const size_t o = r / K2;
       const float* src = first ? dwpart : dwoffpart;
       const size_t stride = first ? n1 : n2;
-      const int cnt = first ? N : nwp;
+      const int cnt = first ? ndw : nwp;
       float s = 0.f;
       for (int z = 0; z < cnt; ++z) s += src[(size_t)z * stride + f];
       (first ? dw : dwoff)[(o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
@@ -782,7 +783,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     DEFT_LAUNCH("bias_partial", k_bias_partial<T>, dim3(d.c_out + p.oc, d.n), dim3(256), 0, st, (const T*)a.dy, doff,
                 bpart, d.c_out, p.oc, d.n, p.ho * p.wo);
     const size_t total = ((size_t)d.c_out + p.oc) * p.ck + d.c_out + p.oc;
-    DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dwpart, (T*)a.dw,
+    DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dwpart, p.dw_splits, (T*)a.dw,
                 d.c_out, dwoffpart, (T*)a.dw_off, p.oc, d.n * p.woff_bands, bpart, (T*)a.db, (T*)a.db_off, d.n,
                 d.c_in, p.taps);
     e = hipGetLastError();

@@ -61,6 +61,12 @@ __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const uint4 a, const u
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// Output tile of one GEMM workgroup: rows from m0, columns from n0, k range
+// [kb, ke), z = batch / split index.
+struct TileCoord {
+  int m0, n0, kb, ke, z;
+};
+
 // Row (within the 32x32 block) of accumulator register r of lane `lane`;
 // the column is lane % 32.
 __device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

@@ -15,21 +15,18 @@
 
 namespace deft {
 
-struct TileCoord {
-  int m0, n0, kb, ke, z;
-};
-
-template <typename T, int BM, int BN, class Op>
+template <typename T, int BM, int BN, int KCH, class Op>
 __global__ __launch_bounds__(256) void k_gemm(const Op op) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int BK = 8 * VEC;
+  constexpr int BK = KCH * VEC;       // k elements per stage (KCH 16-byte chunks per row)
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
-  constexpr int LA = BM * 8 / 256;
-  constexpr int LB = BN * 8 / 256;
-  static_assert(LA >= 1 && LB >= 2 && MI >= 1 && NI >= 1, "tile too small");
+  constexpr int LA = BM * KCH / 256;
+  constexpr int LB = BN * KCH / 256;
+  static_assert(LA >= 1 && LB >= 2 && MI >= 1 && NI >= 1 && (KCH == 4 || KCH == 8), "tile shape");
+  static_assert(!Op::B_KMAJOR || (BN / VEC) % 4 == 0, "k-major B needs a multiple of 4 n-chunks");
   extern __shared__ __align__(16) unsigned char smem[];
-  uint4* sA = (uint4*)smem;   // [2][BM*8]
-  uint4* sB = sA + 2 * BM * 8;  // [2][BN*8]
+  uint4* sA = (uint4*)smem;        // [2][BM*KCH]
+  uint4* sB = sA + 2 * BM * KCH;   // [2][BN*KCH]
   const TileCoord tc = op.tile(blockIdx.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -42,87 +39,98 @@ __global__ __launch_bounds__(256) void k_gemm(const Op op) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[LA], rb[LB];
-  auto gload = [&](int k0) {
+  // Row r, logical 16-byte chunk c is stored at physical chunk c ^ swz(r):
+  // the 16 rows a 16-lane group reads at one chunk land on 16 distinct
+  // 16-byte slots of a 256-byte bank window (and 8 rows on 8 slots of 128 B).
+  auto swz = [](int r) { return (r ^ (r >> 3)) & (KCH - 1); };
+  // k-major B items (VEC consecutive n at k-rows 2kp, 2kp+1): the low two
+  // bits pick one of 4 n-chunks, then the k-pair, then the rest of n, so a
+  // 16-lane group loads 64 contiguous bytes of 4 rows and its transposed LDS
+  // stores hit 16 distinct banks.
+  auto kmajor_item = [](int it, int& nc, int& kp) {
+    constexpr int KP = BK / 2;
+    nc = (it / (4 * KP)) * 4 + (it & 3);
+    kp = (it >> 2) & (KP - 1);
+  };
+  auto gload = [&](int k0, uint4* ra, uint4* rb) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, ch = c & 7;
+      const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
       ra[i] = op.load_a(tc, tc.m0 + row, k0 + ch * VEC);
     }
     if constexpr (!Op::B_KMAJOR) {
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
-        const int c = tid + i * 256, row = c >> 3, ch = c & 7;
+        const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
         rb[i] = op.load_b(tc, tc.n0 + row, k0 + ch * VEC);
       }
     } else {
-      constexpr int NC = BN / VEC;
 #pragma unroll
       for (int i = 0; i < LB / 2; ++i) {
-        const int it = tid + i * 256, nc = it % NC, kp = it / NC;
+        int nc, kp;
+        kmajor_item(tid + i * 256, nc, kp);
         rb[2 * i] = op.load_bt(tc, k0 + 2 * kp, tc.n0 + nc * VEC);
         rb[2 * i + 1] = op.load_bt(tc, k0 + 2 * kp + 1, tc.n0 + nc * VEC);
       }
     }
   };
-  auto sstore = [&](int s) {
-    uint4* a = sA + s * BM * 8;
-    uint4* b = sB + s * BN * 8;
+  auto sstore = [&](int s, const uint4* ra, const uint4* rb) {
+    uint4* a = sA + s * BM * KCH;
+    uint4* b = sB + s * BN * KCH;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, ch = c & 7;
-      a[row * 8 + (ch ^ (row & 7))] = ra[i];
+      const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
+      a[row * KCH + (ch ^ swz(row))] = ra[i];
     }
     if constexpr (!Op::B_KMAJOR) {
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
-        const int c = tid + i * 256, row = c >> 3, ch = c & 7;
-        b[row * 8 + (ch ^ (row & 7))] = rb[i];
+        const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
+        b[row * KCH + (ch ^ swz(row))] = rb[i];
       }
     } else {
-      constexpr int NC = BN / VEC;
       unsigned char* bb = (unsigned char*)b;
 #pragma unroll
       for (int i = 0; i < LB / 2; ++i) {
-        const int it = tid + i * 256, nc = it % NC, kp = it / NC;
+        int nc, kp;
+        kmajor_item(tid + i * 256, nc, kp);
         const int k = 2 * kp, ch = k / VEC, kin = k % VEC;
         const uint4 q0 = rb[2 * i], q1 = rb[2 * i + 1];
+        const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w}, w1[4] = {q1.x, q1.y, q1.z, q1.w};
         if constexpr (VEC == 8) {
-          const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w}, w1[4] = {q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int row = nc * 8 + e;
             const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
             const uint32_t hi = (e & 1) ? (w1[e >> 1] & 0xffff0000u) : (w1[e >> 1] << 16);
-            *(uint32_t*)(bb + (row * 8 + (ch ^ (row & 7))) * 16 + kin * 2) = lo | hi;
+            *(uint32_t*)(bb + (row * KCH + (ch ^ swz(row))) * 16 + kin * 2) = lo | hi;
           }
         } else {
-          const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w}, w1[4] = {q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = nc * 4 + e;
-            *(uint2*)(bb + (row * 8 + (ch ^ (row & 7))) * 16 + kin * 4) = make_uint2(w0[e], w1[e]);
+            *(uint2*)(bb + (row * KCH + (ch ^ swz(row))) * 16 + kin * 4) = make_uint2(w0[e], w1[e]);
           }
         }
       }
     }
   };
   auto compute = [&](int s) {
-    const uint4* a = sA + s * BM * 8;
-    const uint4* b = sB + s * BN * 8;
+    const uint4* a = sA + s * BM * KCH;
+    const uint4* b = sB + s * BN * KCH;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KCH / 2; ++ks) {
       const int ch = ks * 2 + (lane >> 5);
       uint4 fa[MI], fb[NI];
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int row = wm * WM + i * 32 + (lane & 31);
-        fa[i] = a[row * 8 + (ch ^ (row & 7))];
+        fa[i] = a[row * KCH + (ch ^ swz(row))];
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int row = wn * WN + j * 32 + (lane & 31);
-        fb[j] = b[row * 8 + (ch ^ (row & 7))];
+        fb[j] = b[row * KCH + (ch ^ swz(row))];
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -131,17 +139,27 @@ __global__ __launch_bounds__(256) void k_gemm(const Op op) {
     }
   };
 
+  // Two register sets: the loads for stage it+1 were issued two iterations
+  // earlier, so each global load has two compute phases to land.
   const int nk = (tc.ke - tc.kb + BK - 1) / BK;
-  if (nk > 0) {
-    gload(tc.kb);
-    sstore(0);
+  uint4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+  auto body = [&](int it, uint4* ra, uint4* rb) {  // ra/rb hold the loads of stage it+1
+    compute(it & 1);
+    if (it + 1 < nk) {
+      sstore((it + 1) & 1, ra, rb);
+      if (it + 3 < nk) gload(tc.kb + (it + 3) * BK, ra, rb);
+    }
     __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      const int s = it & 1;
-      if (it + 1 < nk) gload(tc.kb + (it + 1) * BK);
-      compute(s);
-      if (it + 1 < nk) sstore(s ^ 1);
-      __syncthreads();
+  };
+  if (nk > 0) {
+    gload(tc.kb, ra0, rb0);
+    if (nk > 1) gload(tc.kb + BK, ra1, rb1);
+    sstore(0, ra0, rb0);
+    if (nk > 2) gload(tc.kb + 2 * BK, ra0, rb0);
+    __syncthreads();
+    for (int it = 0; it < nk; it += 2) {
+      body(it, ra1, rb1);
+      if (it + 1 < nk) body(it + 1, ra0, rb0);
     }
   }
 #pragma unroll
@@ -315,10 +333,12 @@ struct DwOp {
   }
 };
 
+constexpr int kGemmKch = 8;  // 16-byte chunks per row per stage (128-byte rows)
+
 template <typename T, int BM, int BN, class Op>
 static hipError_t run_gemm(const char* name, const Op& op, int grid, hipStream_t st) {
-  constexpr int lds = 2 * (BM + BN) * 8 * 16;
-  auto kern = k_gemm<T, BM, BN, Op>;
+  constexpr int lds = 2 * (BM + BN) * kGemmKch * 16;
+  auto kern = k_gemm<T, BM, BN, kGemmKch, Op>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   if (grid == 0) return hipSuccess;
@@ -348,6 +368,7 @@ static hipError_t gemm_forward_t(const deft_plan& p, const void* wt, const void*
 
 hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
                                hipStream_t st) {
+  if (p.gemm_dl) return dl_gemm_forward(p, wt, cols, b, y, st);
   return p.d.dtype == DEFT_BF16 ? gemm_forward_t<bf16_t>(p, wt, cols, b, y, st)
                                 : gemm_forward_t<float>(p, wt, cols, b, y, st);
 }
@@ -388,10 +409,12 @@ hipError_t gemm_dw_t(const deft_plan& p, const void* dy, const void* cols, float
 
 hipError_t launch_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
                             hipStream_t st) {
+  if (p.gemm_dl) return dl_gemm_dcol(p, w2, dy, dcol, maxbits, st);
   return p.d.dtype == DEFT_BF16 ? gemm_dcol_t<bf16_t>(p, w2, dy, dcol, maxbits, st)
                                 : gemm_dcol_t<float>(p, w2, dy, dcol, maxbits, st);
 }
 hipError_t launch_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* dwpart, hipStream_t st) {
+  if (p.gemm_dl) return dl_gemm_dw(p, dy, cols, dwpart, st);
   return p.d.dtype == DEFT_BF16 ? gemm_dw_t<bf16_t>(p, dy, cols, dwpart, st)
                                 : gemm_dw_t<float>(p, dy, cols, dwpart, st);
 }

@@ -165,7 +165,14 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   const size_t nchunks = p.chunk_b ? (size_t)(s.cg / p.chunk_b) : 1;
   p.ws_maxbits = p.ws_doffp + nchunks * P * s.oc * 4;
   o = align256(p.ws_maxbits + 16);
-  p.ws_dwpart = o; o = align256(o + (size_t)d.n * d.c_out * s.ck * 4);
+  p.gemm_dl = deft::gemm_dl_supported(p) ? 1 : 0;
+  if (p.gemm_dl) {
+    deft::gemm_dl_dw_split(p, &p.dw_splits, &p.dw_kper);
+  } else {
+    p.dw_splits = d.n;
+    p.dw_kper = s.ho * s.wo;
+  }
+  p.ws_dwpart = o; o = align256(o + (size_t)p.dw_splits * d.c_out * s.ck * 4);
   p.ws_dwoffpart = o; o = align256(o + (size_t)d.n * p.woff_bands * s.oc * s.ck * 4);
   p.ws_biaspart = o; o = align256(o + (size_t)(d.c_out + s.oc) * d.n * 4);
   p.ws_train_end = o;
@@ -315,6 +322,8 @@ int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
   info->bwd_tile_h = p->btile_h;
   info->bwd_tile_w = p->btile_w;
   info->bwd_chunk = p->chunk_b;
+  info->gemm_direct = p->gemm_dl;
+  info->dw_splits = p->dw_splits;
   return DEFT_OK;
 }
 

@@ -29,6 +29,9 @@ struct deft_plan {
   int chunk_b, lb_dx, lb_dc, lb_cnt, lb_total;
   int woff_bands;              // row bands of the offset-weight backward
   size_t ws_list, ws_doffp, ws_maxbits, ws_dwpart, ws_dwoffpart, ws_biaspart;
+  // bf16 GEMMs with direct global-to-LDS staging (else the generic kernel)
+  int gemm_dl;
+  int dw_splits, dw_kper;      // dW partials: pixel ranges of dw_kper (per image on the generic path)
 };
 
 namespace deft {
@@ -63,6 +66,14 @@ hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off
 
 hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b,
                                void* y, hipStream_t s);
+// direct-staging bf16 GEMMs (deft_gemm_dl.hip)
+bool gemm_dl_supported(const deft_plan& p);
+void gemm_dl_dw_split(const deft_plan& p, int* splits, int* kper);
+hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
+                           hipStream_t st);
+hipError_t dl_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
+                        hipStream_t st);
+hipError_t dl_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* part, hipStream_t st);
 
 struct BackwardArgs {
   const void* x;

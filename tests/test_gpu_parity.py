@@ -274,6 +274,31 @@ def test_backward_matches_oracle_small(case, dtype):
         assert e <= tol, k
 
 
+@pytest.mark.parametrize("case", [
+    dict(n=3, c_in=48, c_out=40, h=12, w=10),             # ragged tiles in m, n and k; dW splits cross images
+    dict(n=2, c_in=16, c_out=8, h=8, w=8),                # single partial tile everywhere
+    dict(n=2, c_in=32, c_out=264, h=8, w=6, groups=2),    # c_out over one 256-wide tile
+    dict(n=1, c_in=32, c_out=16, h=16, w=16, stride=2),   # Ho*Wo = 64
+])
+def test_backward_bf16_direct_gemm(case):
+    """Shapes that take the direct global-to-LDS GEMMs (bf16, Ho*Wo and c_out
+    multiples of 8), with partial tiles on every side."""
+    base = dict(n=2, c_in=32, c_out=24, h=10, w=11)
+    base.update(case)
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype="bf16", train=True, **base)
+    say("backward bf16 direct gemm", case)
+    inp, layer, y, off, g = run_backward(wl)
+    assert layer.info["gemm_direct"] == 1
+    s = shape_of(wl)
+    y_ref, _ = oracle.forward(s, inp["x"], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+    assert rel(host(y), y_ref) <= TOL["bf16"]
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL["bf16"], k
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["train_bf16_n16_c256_56x56_s1", "train_bf16_n16_c256_56x56_s2"])
 def test_training_step_full_size(name):
