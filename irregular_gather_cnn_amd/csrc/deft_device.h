@@ -148,18 +148,82 @@ __device__ __forceinline__ int fdiv(int x, FastDiv f) {
 
 template <typename T> __device__ __forceinline__ T zero_elem() { return T(0); }
 
-// Copies channels [c0, c0+nc) of image n of x [N][Cin][H][W] over input rows
-// [ry0, ry0+RH) and columns [rx0, rx0+RW) into LDS as [row][col][channel]
-// with pixel stride pstr (elements); locations outside the image are zero.
-// drw/drh divide by RW/RH.  Called by all 256 threads of the workgroup.
+// Staging of an input region into LDS as [row][col][channel] (pixel stride
+// pstr elements), zero outside the image.  bf16 input with an even width is
+// read as aligned 2-pixel words, 8 channels per thread, and written as two
+// 16-byte channel vectors; other inputs go element by element.
+struct StageGeom {
+  int pairs;       // 1: 2-pixel path
+  int xa;          // first (even) column of the 2-pixel grid
+  int npairs;      // 2-pixel words per row
+  FastDiv div;     // divides by npairs (2-pixel path) or by RW (elementwise)
+};
 template <typename T>
-__device__ __forceinline__ void stage_region_hwc(T* dst, const T* __restrict__ x, int Cin, int H, int W,
-                                                 int n, int c0, int nc, int ry0, int rx0, int RH, int RW,
-                                                 FastDiv drw, FastDiv drh, int pstr) {
-  const int total = nc * RH * RW;
+__device__ __forceinline__ StageGeom stage_geom(int W, int rx0, int RW, size_t image_elems) {
+  StageGeom g;
+  // 2-pixel path: bf16, even width, 32-bit offsets within one image
+  g.pairs = (sizeof(T) == 2 && (W & 1) == 0 && image_elems < 0x7fffffffu) ? 1 : 0;
+  g.xa = rx0 & ~1;
+  g.npairs = (rx0 + RW - g.xa + 1) >> 1;
+  g.div = make_fastdiv(g.pairs ? (g.npairs > 0 ? g.npairs : 1) : (RW > 0 ? RW : 1));
+  return g;
+}
+// Channels [c0, c0+nc) (nc a multiple of 8) of image n of x [N][Cin][H][W],
+// rows [ry0, ry0+RH), columns [rx0, rx0+RW).  drh divides by RH.  Called by
+// all 256 threads of the workgroup.
+template <typename T>
+__device__ __forceinline__ void stage_region(T* dst, const T* __restrict__ x, int Cin, int H, int W, int n, int c0,
+                                             int nc, int ry0, int rx0, int RH, int RW, FastDiv drh,
+                                             const StageGeom& g, int pstr) {
   const T* xb = x + ((size_t)n * Cin + c0) * H * W;
+  if (sizeof(T) == 2 && g.pairs) {
+    // items in batches of kU per thread: all loads of a batch are in flight
+    // together; offsets are 32-bit within the image's channel slab
+    constexpr int kU = 4;
+    const uint32_t* xw = (const uint32_t*)xb;
+    const int hw2 = (H * W) >> 1;
+    const int total = (nc >> 3) * RH * g.npairs;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 256 * kU) {
+      uint32_t w[kU][8];
+      int dofs[kU], rcs[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e = e0 + u * 256;
+        const int ec = e < total ? e : 0;
+        const int r = fdiv(ec, g.div);
+        const int xp = ec - r * g.npairs;
+        const int oct = fdiv(r, drh);
+        const int ry = r - oct * RH;
+        const int y = ry0 + ry, xx = g.xa + 2 * xp;
+        const bool in = e < total && (unsigned)y < (unsigned)H && (unsigned)xx < (unsigned)W;
+        const int wofs = ((oct * 8 * H + y) * W + xx) >> 1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[u][k] = in ? xw[wofs + k * hw2] : 0u;
+        rcs[u] = e < total ? xx - rx0 : -2;
+        dofs[u] = (ry * RW + (xx - rx0)) * pstr + oct * 8;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int rc = rcs[u];
+        if (rc >= 0 && rc < RW) {
+          uint4 q;
+          q.x = (w[u][0] & 0xffffu) | (w[u][1] << 16); q.y = (w[u][2] & 0xffffu) | (w[u][3] << 16);
+          q.z = (w[u][4] & 0xffffu) | (w[u][5] << 16); q.w = (w[u][6] & 0xffffu) | (w[u][7] << 16);
+          *(uint4*)(dst + dofs[u]) = q;
+        }
+        if (rc + 1 >= 0 && rc + 1 < RW) {
+          uint4 q;
+          q.x = (w[u][0] >> 16) | (w[u][1] & 0xffff0000u); q.y = (w[u][2] >> 16) | (w[u][3] & 0xffff0000u);
+          q.z = (w[u][4] >> 16) | (w[u][5] & 0xffff0000u); q.w = (w[u][6] >> 16) | (w[u][7] & 0xffff0000u);
+          *(uint4*)(dst + dofs[u] + pstr) = q;
+        }
+      }
+    }
+    return;
+  }
+  const int total = nc * RH * RW;
   for (int e = threadIdx.x; e < total; e += 256) {
-    const int r1 = fdiv(e, drw);
+    const int r1 = fdiv(e, g.div);
     const int rx = e - r1 * RW;
     const int c = fdiv(r1, drh);
     const int ry = r1 - c * RH;
@@ -167,6 +231,100 @@ __device__ __forceinline__ void stage_region_hwc(T* dst, const T* __restrict__ x
     T v = zero_elem<T>();
     if ((unsigned)y < (unsigned)H && (unsigned)xx < (unsigned)W) v = xb[((size_t)c * H + y) * W + xx];
     dst[(ry * RW + rx) * pstr + c] = v;
+  }
+}
+
+// The 2-pixel staging split into a load half (global words into registers)
+// and a store half (registers into LDS), so a kernel can keep the next
+// chunk's loads in flight while it computes on the current one.  A thread
+// holds up to NI items (one item: 8 channels x 2 pixels).
+template <int NI>
+struct PairStage {
+  uint32_t w[NI][8];
+};
+struct PairGeom {
+  int ry0, rx0, RH, RW, xa, npairs, pstr, total, H, W, hw2;
+  FastDiv dnp, drh;
+};
+// nc channels per chunk; usable when the 2-pixel path applies and the whole
+// region fits the registers of one pass.
+__device__ __forceinline__ PairGeom pair_geom(int H, int W, int nc, int ry0, int rx0, int RH, int RW, int pstr) {
+  PairGeom g;
+  g.ry0 = ry0; g.rx0 = rx0; g.RH = RH; g.RW = RW; g.pstr = pstr; g.H = H; g.W = W;
+  g.xa = rx0 & ~1;
+  g.npairs = (rx0 + RW - g.xa + 1) >> 1;
+  g.total = RH > 0 ? (nc >> 3) * RH * g.npairs : 0;
+  g.hw2 = (H * W) >> 1;
+  g.dnp = make_fastdiv(g.npairs > 0 ? g.npairs : 1);
+  g.drh = make_fastdiv(RH > 0 ? RH : 1);
+  return g;
+}
+__device__ __forceinline__ void pair_item(const PairGeom& g, int e, int& oct, int& ry, int& xx) {
+  const int r = fdiv(e, g.dnp);
+  const int xp = e - r * g.npairs;
+  oct = fdiv(r, g.drh);
+  ry = r - oct * g.RH;
+  xx = g.xa + 2 * xp;
+}
+// Buffer descriptor (gfx9 layout): 48-bit base, stride 0, `bytes` records;
+// loads at offsets at or beyond it return zero.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  rsrc_t r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)(uint32_t)(a >> 32);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+// ximg: buffer over one image; c0: first channel of the chunk.  Words outside
+// the image read as zero through the buffer range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <int NI>
+__device__ __forceinline__ void pair_load(PairStage<NI>& s, const PairGeom& g, const __amdgpu_buffer_rsrc_t ximg,
+                                          int c0) {
+  const int plane = g.H * g.W * 2;  // bytes per channel
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int e = threadIdx.x + u * 256;
+    if (e < g.total) {
+      int oct, ry, xx;
+      pair_item(g, e, oct, ry, xx);
+      const int y = g.ry0 + ry;
+      const bool in = (unsigned)y < (unsigned)g.H && (unsigned)xx < (unsigned)g.W;
+      const int voff = in ? (((c0 + oct * 8) * g.H + y) * g.W + xx) * 2 : (int)0x80000000;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s.w[u][k] = __builtin_amdgcn_raw_buffer_load_b32(ximg, voff, k * plane, 0);
+    }
+  }
+}
+template <int NI>
+__device__ __forceinline__ void pair_store(const PairStage<NI>& s, const PairGeom& g, bf16_t* dst) {
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int e = threadIdx.x + u * 256;
+    if (e < g.total) {
+      int oct, ry, xx;
+      pair_item(g, e, oct, ry, xx);
+      const int rc = xx - g.rx0;
+      bf16_t* d = dst + (ry * g.RW + rc) * g.pstr + oct * 8;
+      const uint32_t* w = s.w[u];
+      if (rc >= 0 && rc < g.RW) {
+        uint4 q;
+        q.x = (w[0] & 0xffffu) | (w[1] << 16); q.y = (w[2] & 0xffffu) | (w[3] << 16);
+        q.z = (w[4] & 0xffffu) | (w[5] << 16); q.w = (w[6] & 0xffffu) | (w[7] << 16);
+        *(uint4*)d = q;
+      }
+      if (rc + 1 >= 0 && rc + 1 < g.RW) {
+        uint4 q;
+        q.x = (w[0] >> 16) | (w[1] & 0xffff0000u); q.y = (w[2] >> 16) | (w[3] & 0xffff0000u);
+        q.z = (w[4] >> 16) | (w[5] & 0xffff0000u); q.w = (w[6] >> 16) | (w[7] & 0xffff0000u);
+        *(uint4*)(d + g.pstr) = q;
+      }
+    }
   }
 }
 

@@ -42,19 +42,6 @@ constexpr int kOOB = (int)0x80000000;
 typedef __attribute__((address_space(3))) void lds_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-// Buffer descriptor (gfx9 layout): 48-bit base, stride 0, `bytes` records
-// (loads at offsets beyond it return zero), default data format.
-typedef int rsrc_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  rsrc_t r;
-  r.x = (int)(uint32_t)a;
-  r.y = (int)(uint32_t)(a >> 32);
-  r.z = (int)bytes;
-  r.w = 0x00020000;
-  return r;
-}
-
 // 16 bytes per lane from the buffer straight into LDS at dst + 16*lane.
 // Written as inline assembly so the compiler does not order every later LDS
 // read behind these loads; completion is awaited explicitly (wait_vm).

@@ -140,7 +140,7 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   p.lds_region = 0;
   p.lds_off = align16(region);
   p.lds_info = p.lds_off + align16(ocw * pt * 4);
-  p.lds_total = p.lds_info + p.gw * s.taps * pt * 16;
+  p.lds_total = p.lds_info + align16(p.gw * s.taps * pt * 8) + p.gw * s.taps * pt * 16;  // tap table + weights
   if (p.lds_total > kMaxLds) return false;
   p.num_btiles = 0; p.list_cap = 0; p.woff_bands = 1;
   if (!layout_backward(p)) p.chunk_b = 0;
@@ -192,9 +192,10 @@ double miss_fraction(const uint32_t* hist, int len, int halo) {
 
 // Planner: pick (tile, halo, chunk) minimising a byte-cost estimate of the
 // fused kernel: the columns it must write, the input staged into LDS (served
-// mostly from L2, weighted down), and the taps outside the halo, each of which
+// mostly from L2, weighted down), the taps outside the halo, each of which
 // reads four corners per channel from global memory uncoalesced (weighted up),
-// divided by the fraction of the machine the launch keeps busy.
+// and a fixed cost per channel-chunk pass, divided by the fraction of the
+// machine the launch keeps busy.
 int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len) {
   const Shape s = shape_of(d);
   static const int tiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}, {4, 4}, {2, 16}, {16, 2}, {2, 8}, {1, 16}};
@@ -213,12 +214,16 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
         const double pt = (double)t[0] * t[1];
         const double per_tile_stage = (double)p.reg_h * p.reg_w * s.cg + (double)p.foot_h * p.foot_w * d.c_in;
         const double stage_bytes = (double)p.num_wg * per_tile_stage * s.esz;
-        const double miss_bytes = miss * samples * 4.0 * s.esz * 8.0;
+        // a missed tap costs its uncoalesced reads here and again in the backward
+        const double miss_bytes = miss * samples * 4.0 * s.esz * 32.0;
         const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
         const double slots = (double)kNumCUs * occ;
         const double waves = std::ceil(p.num_wg / slots);
         const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
-        double cost = (col_bytes + 0.25 * stage_bytes + miss_bytes) / std::max(busy, 0.05);
+        // each channel-chunk pass of a workgroup pays a staging round trip and
+        // two barriers, about as much as moving 16 KB
+        const double passes = (double)p.num_wg * p.gw * (s.cg / chunk) + (double)p.num_wg * (d.c_in / p.chunk_a);
+        double cost = (col_bytes + 0.25 * stage_bytes + miss_bytes + passes * 16384.0) / std::max(busy, 0.05);
         if (p.lds_total > kTargetLds) cost *= 1.15;
         if (pt < 32) cost *= 1.1;  // phase-A MFMA blocks half empty
         if (cost < best_cost * 0.999) {

@@ -26,7 +26,7 @@ struct SampleParams {
   int TH, TW, halo, CC, CA, GW, gsplit, tiles_h, tiles_w, num_wg;
   int FH, FW, pstr, pstr_a, lognv;
   int lds_region, lds_off, lds_info;
-  FastDiv div_tw, div_k2, div_fw, div_fh;
+  FastDiv div_tw, div_k2, div_fh;
   const void* x;
   const void* woff_p;
   const void* b_off;
@@ -36,7 +36,7 @@ struct SampleParams {
 };
 
 template <typename T, bool FUSED, int MB>
-__global__ __launch_bounds__(256) void k_sample(const SampleParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sample(const SampleParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int VEC = Elem<T>::VEC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -52,10 +52,31 @@ __global__ __launch_bounds__(256) void k_sample(const SampleParams p) {
   const int ocw = 2 * p.GW * p.K2;
   const int obase = 2 * g0 * p.K2;
   float* off_l = (float*)(smem + p.lds_off);   // [ocw][PT]
-  int4* info = (int4*)(smem + p.lds_info);     // [GW][K2][PT]
+  int2* tab = (int2*)(smem + p.lds_info);                            // [GW][PT][K2]
+  float4* wts = (float4*)(smem + p.lds_info + ((p.GW * PT * p.K2 * 8 + 15) & ~15));  // [GW][PT][K2]
   T* xr = (T*)(smem + p.lds_region);
   const T* __restrict__ x = (const T*)p.x;
   const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
+
+  // ---- halo region of this tile (clipped to rows/cols -1..H, -1..W) ----
+  const int fha = (thn - 1) * p.SH + (p.KH - 1) * p.DH + 1;
+  const int fwa = (twn - 1) * p.SW + (p.KW - 1) * p.DW + 1;
+  const int ry0 = max(fy0 - p.halo, -1), ry1 = min(fy0 + fha + p.halo, p.H);
+  const int rx0 = max(fx0 - p.halo, -1), rx1 = min(fx0 + fwa + p.halo, p.W);
+  int RH = ry1 - ry0 + 1, RW = rx1 - rx0 + 1;
+  if (RH <= 0 || RW <= 0) { RH = 0; RW = 0; }
+
+  // Input staging: bf16 with an even width goes through registers so the next
+  // chunk's loads overlap the current chunk's compute (kItemsA / kItemsB
+  // items of 8 channels x 2 pixels per thread for the footprint / halo
+  // chunks); larger regions and other inputs are staged synchronously.
+  constexpr int kItemsA = 3, kItemsB = 8;
+  const size_t img_elems = (size_t)p.Cin * p.H * p.W;
+  const bool pairs_ok = sizeof(T) == 2 && (p.W & 1) == 0 && img_elems < 0x3ffffff0u;
+  const PairGeom gb = pair_geom(p.H, p.W, p.CC, ry0, rx0, RH, RW, p.pstr);
+  const bool pipeB = pairs_ok && RH > 0 && gb.total <= 256 * kItemsB;
+  const __amdgpu_buffer_rsrc_t ximg = make_brsrc(x + (size_t)n * img_elems, pairs_ok ? (uint32_t)(img_elems * 2) : 0u);
+  PairStage<kItemsB> st;
 
   if constexpr (FUSED) {
     // ---- phase A: offsets of this tile on the MFMA units ----
@@ -68,40 +89,76 @@ __global__ __launch_bounds__(256) void k_sample(const SampleParams p) {
         for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     const int nkc = p.CA / (2 * VEC);
     const int npairs = p.K2 * nkc;
+    const int myp = (npairs - wave + 3) >> 2;  // this wave's (tap, k-chunk) pairs: wave, wave+4, ...
     const bool nb1 = PT > 32;
     const T* __restrict__ wp = (const T*)p.woff_p;
-    int pixb[2], pixoff[2];
+    int pixb[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       int pix = nb * 32 + (lane & 31);
       if (pix >= PT) pix = 0;
       const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
       pixb[nb] = ty * p.SH * p.FW + tx * p.SW;  // footprint pixel of tap (0,0)
-      pixoff[nb] = pix;
     }
-    (void)pixoff;
+    const StageGeom sga = stage_geom<T>(p.W, fx0, p.FW, img_elems);
+    const PairGeom ga = pair_geom(p.H, p.W, p.CA, fy0, fx0, p.FH, p.FW, p.pstr_a);
+    const bool pipeA = pairs_ok && ga.total <= 256 * kItemsA;
+    PairStage<kItemsA> sa;
+    if (pipeA) pair_load(sa, ga, ximg, 0);
+    // Weight fragments of this wave, a batch of kWB pairs at a time; the
+    // first batch of the next chunk is loaded while this chunk computes.
+    constexpr int kWB = 9 / MB;
+    uint4 wa[kWB][MB], wn[kWB][MB];
+    auto load_w = [&](uint4 (&dst)[kWB][MB], int c0, int j0) {
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        const int j = j0 + jj;
+        if (j < myp) {
+          const int pi = wave + 4 * j;
+          const int t = pi / nkc, kc = pi - t * nkc;
+          const int cl = kc * 2 * VEC + (lane >> 5) * VEC;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int o = obase + mb * 32 + (lane & 31);
+            dst[jj][mb] = *(const uint4*)(wp + ((size_t)o * p.K2 + t) * p.Cin + c0 + cl);
+          }
+        }
+      }
+    };
+    load_w(wa, 0, 0);
     for (int c0 = 0; c0 < p.Cin; c0 += p.CA) {
       __syncthreads();
-      stage_region_hwc<T>(xr, x, p.Cin, p.H, p.W, n, c0, p.CA, fy0, fx0, p.FH, p.FW, p.div_fw, p.div_fh, p.pstr_a);
+      if (pipeA) pair_store(sa, ga, (bf16_t*)xr);
+      else stage_region<T>(xr, x, p.Cin, p.H, p.W, n, c0, p.CA, fy0, fx0, p.FH, p.FW, p.div_fh, sga, p.pstr_a);
       __syncthreads();
-      for (int pi = wave; pi < npairs; pi += 4) {
-        const int t = pi / nkc, kc = pi - t * nkc;
-        const int ti = t / p.KW, tj = t - ti * p.KW;
-        const int cl = kc * 2 * VEC + (lane >> 5) * VEC;
-        uint4 a[MB];
+      const bool more = c0 + p.CA < p.Cin;
+      if (pipeA && more) pair_load(sa, ga, ximg, c0 + p.CA);
+      if (more) load_w(wn, c0 + p.CA, 0);
+      for (int j0 = 0; j0 < myp; j0 += kWB) {
+        if (j0 > 0) load_w(wa, c0, j0);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int o = obase + mb * 32 + (lane & 31);
-          a[mb] = *(const uint4*)(wp + ((size_t)o * p.K2 + t) * p.Cin + c0 + cl);
+        for (int jj = 0; jj < kWB; ++jj) {
+          const int j = j0 + jj;
+          if (j >= myp) break;
+          const int pi = wave + 4 * j;
+          const int t = pi / nkc, kc = pi - t * nkc;
+          const int ti = t / p.KW, tj = t - ti * p.KW;
+          const int cl = kc * 2 * VEC + (lane >> 5) * VEC;
+          const int toff = ti * p.DH * p.FW + tj * p.DW;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (nb == 1 && !nb1) break;
+            const uint4 bq = *(const uint4*)(xr + (size_t)(pixb[nb] + toff) * p.pstr_a + cl);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][nb], wa[jj][mb], bq, T());
+          }
         }
-        const int toff = ti * p.DH * p.FW + tj * p.DW;
+      }
+      if (more) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if (nb == 1 && !nb1) break;
-          const uint4 b = *(const uint4*)(xr + (size_t)(pixb[nb] + toff) * p.pstr_a + cl);
+        for (int jj = 0; jj < kWB; ++jj)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][nb], a[mb], b, T());
-        }
+          for (int mb = 0; mb < MB; ++mb) wa[jj][mb] = wn[jj][mb];
       }
     }
     __syncthreads();
@@ -140,23 +197,25 @@ __global__ __launch_bounds__(256) void k_sample(const SampleParams p) {
     }
   }
 
-  // ---- halo region of this tile (clipped to rows/cols -1..H, -1..W) ----
-  const int fha = (thn - 1) * p.SH + (p.KH - 1) * p.DH + 1;
-  const int fwa = (twn - 1) * p.SW + (p.KW - 1) * p.DW + 1;
-  const int ry0 = max(fy0 - p.halo, -1), ry1 = min(fy0 + fha + p.halo, p.H);
-  const int rx0 = max(fx0 - p.halo, -1), rx1 = min(fx0 + fwa + p.halo, p.W);
-  int RH = ry1 - ry0 + 1, RW = rx1 - rx0 + 1;
-  if (RH <= 0 || RW <= 0) { RH = 0; RW = 0; }
+  if (pipeB) pair_load(st, gb, ximg, g0 * p.Cg);  // first halo chunk, in flight during the index stage
   __syncthreads();
 
-  // ---- tap index stage: once per (group, tap, pixel) ----
+  // ---- tap index stage: once per (group, pixel, tap) ----
+  // tab[e] = {corner (y0, x0) as an element offset into the staged region,
+  // or -2 fully outside, <= -3 corner outside the halo (then
+  // -3 - ((y0+1)*(W+1) + (x0+1))); column offset of the tap relative to the
+  // tile's first column row, -1 for pixels outside the tile}; wts[e] = the
+  // four bilinear weights.  e = (group*PT + pixel)*K2 + tap.
+  const int nent = PT * p.K2;
+  const int rwp = RW * p.pstr;
   {
-    const int nidx = p.GW * p.K2 * PT;
+    const int nidx = p.GW * nent;
     for (int e = tid; e < nidx; e += 256) {
-      const int gt = e / PT, pix = e - gt * PT;
-      const int gl = fdiv(gt, p.div_k2), t = gt - gl * p.K2;
+      const int r = fdiv(e, p.div_k2), t = e - r * p.K2;
+      const int gl = r / PT, pix = r - gl * PT;
       const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-      int4 inf = make_int4(-2, 0, 0, 0);
+      int2 tb = make_int2(0, -1);
+      float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
       if (ty < thn && tx < twn) {
         const int ti = t / p.KW, tj = t - ti * p.KW;
         const int by = (oh0 + ty) * p.SH - p.PH + ti * p.DH;
@@ -164,75 +223,108 @@ __global__ __launch_bounds__(256) void k_sample(const SampleParams p) {
         const float dy = off_l[(2 * (gl * p.K2 + t)) * PT + pix];
         const float dx = off_l[(2 * (gl * p.K2 + t) + 1) * PT + pix];
         const TapIndex ix = tap_index(by, bx, dy, dx, p.H, p.W);
-        if (!ix.outside) {
+        tb.y = (ty * p.Wo + tx) * p.Ck + t * p.Cin;
+        if (ix.outside) {
+          tb.x = -2;
+        } else {
           const bool in = ix.y0 >= ry0 && ix.y0 + 1 <= ry1 && ix.x0 >= rx0 && ix.x0 + 1 <= rx1 && RH > 0;
-          inf.x = in ? (ix.y0 - ry0) * RW + (ix.x0 - rx0) : -1;
-          inf.y = (int)(((uint32_t)ix.y0 << 16) | ((uint32_t)ix.x0 & 0xffffu));
-          inf.z = __float_as_int(ix.ly);
-          inf.w = __float_as_int(ix.lx);
+          tb.x = in ? ((ix.y0 - ry0) * RW + (ix.x0 - rx0)) * p.pstr : -3 - ((ix.y0 + 1) * (p.W + 1) + (ix.x0 + 1));
+          float w[4];
+          tap_weights(ix, w);
+          wv = make_float4(w[0], w[1], w[2], w[3]);
         }
       }
-      info[e] = inf;
+      tab[e] = tb;
+      wts[e] = wv;
     }
   }
 
   // ---- phase B: stage chunk + halo, blend four corners, write columns ----
-  const FastDiv drw = make_fastdiv(RW > 0 ? RW : 1), drh = make_fastdiv(RH > 0 ? RH : 1);
-  T* __restrict__ cols = (T*)p.cols;
+  // Each thread keeps one 8-channel slice v of the chunk and walks the
+  // (pixel, tap) entries; the nv threads of an entry write its chunk as one
+  // contiguous run of the column row.
+  const FastDiv drh = make_fastdiv(RH > 0 ? RH : 1);
+  const StageGeom sg = stage_geom<T>(p.W, rx0, RW, img_elems);
+  T* __restrict__ colt = (T*)p.cols + ((size_t)n * p.Ho * p.Wo + (size_t)oh0 * p.Wo + ow0) * p.Ck;
   const int nv = p.CC >> 3;
-  const int nitems = PT * p.K2 * nv;
+  const int v = tid & (nv - 1), e0 = tid >> p.lognv, estep = 256 >> p.lognv;
   const size_t HW = (size_t)p.H * p.W;
   for (int gl = 0; gl < p.GW; ++gl) {
     const int g = g0 + gl;
+    const int2* tabg = tab + gl * nent;
+    const float4* wtsg = wts + gl * nent;
     for (int c0 = 0; c0 < p.Cg; c0 += p.CC) {
       const int cglob = g * p.Cg + c0;
       __syncthreads();
-      if (RH > 0) stage_region_hwc<T>(xr, x, p.Cin, p.H, p.W, n, cglob, p.CC, ry0, rx0, RH, RW, drw, drh, p.pstr);
+      if (pipeB) pair_store(st, gb, (bf16_t*)xr);
+      else if (RH > 0) stage_region<T>(xr, x, p.Cin, p.H, p.W, n, cglob, p.CC, ry0, rx0, RH, RW, drh, sg, p.pstr);
       __syncthreads();
-      for (int it = tid; it < nitems; it += 256) {
-        const int v = it & (nv - 1);
-        const int rest = it >> p.lognv;
-        const int pix = fdiv(rest, p.div_k2), t = rest - pix * p.K2;
-        const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-        if (ty >= thn || tx >= twn) continue;
-        const int4 inf = info[(gl * p.K2 + t) * PT + pix];
+      if (pipeB) {
+        // next halo chunk: same group, next channels, else the next group
+        const int cn = c0 + p.CC < p.Cg ? cglob + p.CC : (gl + 1 < p.GW ? (g + 1) * p.Cg : -1);
+        if (cn >= 0) pair_load(st, gb, ximg, cn);
+      }
+      const T* xv = xr + v * 8;
+      T* colv = colt + cglob + v * 8;
+      // Every entry is blended from the staged region; entries that are fully
+      // outside or whose
+      // corner lies beyond the halo read corner 0 and are rewritten below by
+      // the same thread.
+      constexpr int kE = 1;  // entries per step (registers: the next chunk's loads are live here)
+      for (int e = e0; e < nent; e += kE * estep) {
+        int2 tb[kE];
+        float w[kE][4];
+#pragma unroll
+        for (int u = 0; u < kE; ++u) {
+          const int eu = e + u * estep;
+          const int ec = eu < nent ? eu : e;
+          tb[u] = tabg[ec];
+          if (eu >= nent) tb[u].y = -1;
+          const float4 wq = wtsg[ec];
+          w[u][0] = wq.x; w[u][1] = wq.y; w[u][2] = wq.z; w[u][3] = wq.w;
+        }
+        float o8[kE][8];
+#pragma unroll
+        for (int u = 0; u < kE; ++u) {
+          const T* b0 = xv + max(tb[u].x, 0);
+          float f00[8], f01[8], f10[8], f11[8];
+          lds_read8(b0, f00);
+          lds_read8(b0 + p.pstr, f01);
+          lds_read8(b0 + rwp, f10);
+          lds_read8(b0 + rwp + p.pstr, f11);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o8[u][c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
+        }
+#pragma unroll
+        for (int u = 0; u < kE; ++u)
+          if (tb[u].y >= 0) store8(colv + tb[u].y, o8[u]);
+      }
+      // fully outside taps (zero) and corners beyond the halo (global reads)
+      for (int e = e0; e < nent; e += estep) {
+        const int2 tb = tabg[e];
+        if (tb.x >= 0 || tb.y < 0) continue;
         float o8[8];
-        if (inf.x == -2) {
+        if (tb.x == -2) {
 #pragma unroll
           for (int c = 0; c < 8; ++c) o8[c] = 0.f;
         } else {
-          TapIndex ix;
-          ix.outside = false;
-          ix.ly = __int_as_float(inf.z);
-          ix.lx = __int_as_float(inf.w);
-          float w[4];
-          tap_weights(ix, w);
-          if (inf.x >= 0) {
-            const T* b0 = xr + (size_t)inf.x * p.pstr + v * 8;
-            float f00[8], f01[8], f10[8], f11[8];
-            lds_read8(b0, f00);
-            lds_read8(b0 + p.pstr, f01);
-            lds_read8(b0 + (size_t)RW * p.pstr, f10);
-            lds_read8(b0 + (size_t)(RW + 1) * p.pstr, f11);
+          const float4 wq = wtsg[e];
+          const float w[4] = {wq.x, wq.y, wq.z, wq.w};
+          const int m = -3 - tb.x;
+          const int yy = m / (p.W + 1), y0 = yy - 1, x0 = m - yy * (p.W + 1) - 1;
+          const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
+          const T* base = x + ((size_t)n * p.Cin + cglob + v * 8) * HW;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) o8[c] = blend4(w, f00[c], f01[c], f10[c], f11[c]);
-          } else {
-            const int y0 = inf.y >> 16, x0 = (int)(short)(inf.y & 0xffff);
-            const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
-            const T* base = x + ((size_t)n * p.Cin + cglob + v * 8) * HW;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const T* pl = base + c * HW;
-              const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
-              const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
-              const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
-              const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
-              o8[c] = blend4(w, v00, v01, v10, v11);
-            }
+          for (int c = 0; c < 8; ++c) {
+            const T* pl = base + c * HW;
+            const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
+            const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
+            const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
+            const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
+            o8[c] = blend4(w, v00, v01, v10, v11);
           }
         }
-        const size_t q = (size_t)n * p.Ho * p.Wo + (size_t)(oh0 + ty) * p.Wo + (ow0 + tx);
-        store8(cols + q * p.Ck + (size_t)t * p.Cin + cglob + v * 8, o8);
+        store8(colv + tb.y, o8);
       }
     }
   }
@@ -346,7 +438,6 @@ static SampleParams make_params(const deft_plan& p, const SampleArgs& a) {
   s.lds_region = p.lds_region; s.lds_off = p.lds_off; s.lds_info = p.lds_info;
   s.div_tw = make_fastdiv(p.tile_w);
   s.div_k2 = make_fastdiv(p.taps);
-  s.div_fw = make_fastdiv(p.foot_w);
   s.div_fh = make_fastdiv(p.foot_h);
   s.x = a.x; s.woff_p = a.woff_p; s.b_off = a.b_off; s.off_in = a.off_in; s.off_out = a.off_out;
   s.cols = a.cols;
