@@ -25,6 +25,8 @@
 //                     reduction of all partials to dW, dW_off, db, db_off.
 // Global atomics are avoided on every hot path: on gfx950 they run far below
 // the bandwidth of plain stores.
+#include <type_traits>
+
 #include "deft_device.h"
 #include "deft_internal.h"
 
@@ -147,16 +149,21 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const int L = *cnt;
 
   // ---- per channel chunk: stage, scatter, dOffset, write the core ----
-  // dX is accumulated in 64-bit fixed point with integer LDS atomics (fast
-  // on this LDS, unlike float atomics; exact, so the sum is independent of
-  // the order of the atomics).  Scale 2^S: every contribution |w*g| <= max|g|
-  // < 2^(e+1) and a (pixel, channel) receives at most list_cap of them, so
-  // |sum| * 2^S < 2^63 for S = 61 - capbits - e; one contribution is split as
-  // hi*2^32 + lo with |hi| < 2^30.
+  // dX is accumulated in fixed point with integer LDS atomics (fast on this
+  // LDS, unlike float atomics; integer sums do not depend on the order of the
+  // atomics).  Every contribution |w*g| <= max|g| < 2^e and a (pixel,
+  // channel) receives at most list_cap < 2^capbits of them.  fp32: 64-bit
+  // accumulators, scale 2^S with S = 61 - capbits - e, a contribution split
+  // as hi*2^32 + lo with |hi| < 2^30, exact to 2^-S.  bf16: 32-bit
+  // accumulators, S = 30 - capbits - e, each contribution rounded to the
+  // nearest multiple of 2^-S (relative to the sum of the contributions'
+  // magnitudes the error stays below 2^-(30-capbits), far inside bf16's).
+  constexpr bool kWide = sizeof(T) == 4;
+  typedef typename std::conditional<kWide, unsigned long long, uint32_t>::type acc_t;
   const uint32_t gb = *p.maxbits;
   const int e = max((int)((gb >> 23) & 255u) - 126, -100);
-  const int S = 61 - p.capbits - e;
-  const float sc = ldexpf(1.0f, S - 32);
+  const int S = (kWide ? 61 : 30) - p.capbits - e;
+  const float sc = ldexpf(1.0f, kWide ? S - 32 : S);
   const double inv = ldexp(1.0, -S);
   // Each wave walks blocks of BLK list entries: the block's dCol rows are
   // copied into a wave-private LDS buffer with 16-byte loads (the next
@@ -170,27 +177,18 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const bool act = c < p.CC;
   const size_t HW = (size_t)p.H * p.W;
   T* dst = (T*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;
-  unsigned long long* dxl = (unsigned long long*)(smem + p.lds_dx);  // [CH*CW][CC]
+  acc_t* dxl = (acc_t*)(smem + p.lds_dx);  // [CH*CW][CC]
   const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
   const int epi = 64 / lpe;    // rows per load instruction
   const size_t pstride = (size_t)p.N * p.Oc * HoWo;
+  const FastDiv drh = make_fastdiv(p.CH + 2);
+  const StageGeom sg = stage_geom<T>(p.W, X0 - 1, XW, (size_t)p.Cin * HW);
   for (int c0 = 0; c0 < p.Cg; c0 += p.CC) {
     const int cglob = g * p.Cg + c0;
     float* doffp = p.doffp + (size_t)(c0 / p.CC) * pstride + ((size_t)n * p.Oc + obase) * HoWo;
     __syncthreads();
-    {
-      const int np = (p.CH + 2) * XW;
-      for (int k = tid; k < np * p.CC; k += 256) {
-        const int cc = k / np, r = k - cc * np;
-        const int ry = r / XW, rx = r - ry * XW;
-        const int y = Y0 - 1 + ry, xx = X0 - 1 + rx;
-        T v = zero_elem<T>();
-        if ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
-          v = x[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)y * p.W + xx];
-        xl[r * p.xstr + cc] = v;
-      }
-      for (int k = tid; k < p.CH * p.CW * p.CC; k += 256) dxl[k] = 0ull;
-    }
+    stage_region<T>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
+    for (int k = tid; k < p.CH * p.CW * p.CC; k += 256) dxl[k] = 0;
     __syncthreads();
     int eb = wave * BLK;
     int4 my = make_int4(0, 0, 0, 0);
@@ -233,15 +231,19 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
         tap_weights(ix, w);
         if (act) {
           const float gcv = Elem<T>::to_f32(dst[r * p.dcstr + c]);
-          unsigned long long* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
+          acc_t* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             if (cm & (1u << qq)) {
               const float xv = gcv * (w[qq] * sc);
-              const float fh = floorf(xv);
-              const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
-              const unsigned long long v64 = ((unsigned long long)(uint32_t)(int)fh << 32) | lo;
-              atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, v64);
+              if constexpr (kWide) {
+                const float fh = floorf(xv);
+                const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
+                const unsigned long long v64 = ((unsigned long long)(uint32_t)(int)fh << 32) | lo;
+                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, v64);
+              } else {
+                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, (uint32_t)(int)rintf(xv));
+              }
             }
           }
         }
@@ -286,8 +288,9 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     for (int k = tid; k < p.CC * chn * cwn; k += 256) {
       const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
       const int y = r / cwn, xx = r - y * cwn;
-      const long long sv = (long long)dxl[(y * p.CW + xx) * p.CC + cc];
-      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = (float)((double)sv * inv);
+      const acc_t a = dxl[(y * p.CW + xx) * p.CC + cc];
+      const double sv = kWide ? (double)(long long)a : (double)(int)(uint32_t)a;
+      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = (float)(sv * inv);
     }
   }
 }
@@ -702,7 +705,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     int cb = 0;
     while ((1 << cb) < p.list_cap + 1) ++cb;
     b.capbits = cb;
-    b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 2 : 1);
+    b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
     b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
     b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
     b.lists = lists;

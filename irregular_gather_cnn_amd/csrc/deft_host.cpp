@@ -86,9 +86,9 @@ bool layout_backward(deft_plan& p) {
   while (cb > 16 && s.cg % cb) cb /= 2;
   if (s.cg % cb) return false;
   const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
-  const int xstr = cb + (d.dtype == DEFT_BF16 ? 2 : 1);
+  const int xstr = cb + vec;
   const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
-  const int ldx = align16(ch * cw * cb * 8);  // 64-bit fixed-point dX of the core
+  const int ldx = align16(ch * cw * cb * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core
   const int ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
   const int total = lx + ldx + ldc + 16 + 4 * 49 * 4;  // + list counter and per-tap tables
   if (total > kMaxLds) return false;
