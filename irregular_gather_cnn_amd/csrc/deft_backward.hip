@@ -2,17 +2,18 @@
 //
 // The DefT explainer page speaks of training time only ("The argument in one
 // glance", "This paper's idea"), so the backward is the exact derivative of
-// the forward.  dCol = W^T dY and the per-image partials of dW = dY Col run
-// on the MFMA GEMMs (deft_gemm.hip); this file holds
-//   k_sample_bwd   -- per core tile of input pixels: lists the (output pixel,
-//                     tap) pairs whose corners touch the core within the
-//                     halo, then per channel chunk (lanes = channels)
-//                     scatters dCol x bilinear weight into an fp32 LDS copy
-//                     of the core (64 consecutive addresses per LDS atomic,
-//                     no collisions) and writes the core's dX once with plain
-//                     stores; the unique owner of each pair reduces
-//                     dOffset = sum over the group's channels of dCol x the
-//                     corner differences.
+// the forward.  dCol = W^T dY and the pixel-range partials of dW = dY Col
+// run on the MFMA GEMMs (deft_gemm.hip, deft_gemm_dl.hip); this file holds
+//   k_sample_bwd   -- per (core tile of input pixels, offset group, channel
+//                     chunk): lists the (output pixel, tap) pairs whose
+//                     corners touch the core within the halo, then (lanes =
+//                     channels) scatters dCol x bilinear weight into a
+//                     fixed-point LDS copy of the core with integer LDS
+//                     atomics (64 consecutive addresses per atomic, order-
+//                     independent sums) and writes the core's dX once with
+//                     plain stores; the unique owner of each pair reduces
+//                     dOffset = the chunk's sum of dCol x the corner
+//                     differences into that chunk's partial.
 //   k_sample_bwd_miss -- the rare taps beyond the halo: dOffset from global
 //                     memory, dX added with global atomics.
 //   k_woff_bwd     -- per (image, 32-channel slice, band of output rows):
@@ -46,7 +47,7 @@ struct BwdParams {
   const uint32_t* maxbits;  // max |dcol| as fp32 bits
   float* dxs;    // [N][Cin][H][W] fp32: the sampling part of dX
   float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials, zeroed beforehand
-  int4* lists;   // [num_wg][list_cap]
+  int4* lists;   // [num_wg][list_cap]: each workgroup's own list
 };
 
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
@@ -57,8 +58,12 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // one workgroup per (core tile, offset group, channel chunk): the chunks
+  // of one core are neighbours in the XCD-aware order and share its offsets
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
-  const int tile = lw / p.G, g = lw - tile * p.G;
+  const int nchunks = p.Cg / p.CC;
+  const int tg = lw / nchunks, chunk = lw - tg * nchunks;
+  const int tile = tg / p.G, g = tg - tile * p.G;
   const int tpi = p.bt_h * p.bt_w;
   const int n = tile / tpi, trem = tile - n * tpi;
   const int Y0 = (trem / p.bt_w) * p.CH, X0 = (trem % p.bt_w) * p.CW;
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const size_t pstride = (size_t)p.N * p.Oc * HoWo;
   const FastDiv drh = make_fastdiv(p.CH + 2);
   const StageGeom sg = stage_geom<T>(p.W, X0 - 1, XW, (size_t)p.Cin * HW);
-  for (int c0 = 0; c0 < p.Cg; c0 += p.CC) {
+  {
+    const int c0 = chunk * p.CC;
     const int cglob = g * p.Cg + c0;
     float* doffp = p.doffp + (size_t)(c0 / p.CC) * pstride + ((size_t)n * p.Oc + obase) * HoWo;
     __syncthreads();
@@ -218,34 +224,46 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
-      // scatter: lanes = channels, one entry at a time
-      for (int r = 0; r < nb; ++r) {
-        const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
-        const uint32_t cm = (info >> 9) & 15u;
-        const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
-        TapIndex ix;
-        ix.outside = false;
-        ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
-        ix.lx = __int_as_float(__builtin_amdgcn_readlane(cur.w, r));
-        float w[4];
-        tap_weights(ix, w);
-        if (act) {
-          const float gcv = Elem<T>::to_f32(dst[r * p.dcstr + c]);
-          acc_t* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
+      // scatter: lanes = channels, two entries per step (independent
+      // instruction streams for the scheduler)
+      for (int r0 = 0; r0 < nb; r0 += 2) {
+        acc_t* dd[2];
+        uint32_t cms[2];
+        float wsc[2][4], gcv[2];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            if (cm & (1u << qq)) {
-              const float xv = gcv * (w[qq] * sc);
-              if constexpr (kWide) {
-                const float fh = floorf(xv);
-                const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
-                const unsigned long long v64 = ((unsigned long long)(uint32_t)(int)fh << 32) | lo;
-                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, v64);
-              } else {
-                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC, (uint32_t)(int)rintf(xv));
+        for (int u = 0; u < 2; ++u) {
+          const int r = min(r0 + u, nb - 1);
+          const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
+          cms[u] = (r0 + u < nb) ? (info >> 9) & 15u : 0u;
+          const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+          TapIndex ix;
+          ix.outside = false;
+          ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
+          ix.lx = __int_as_float(__builtin_amdgcn_readlane(cur.w, r));
+          float w[4];
+          tap_weights(ix, w);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) wsc[u][qq] = w[qq] * sc;
+          dd[u] = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
+          gcv[u] = act ? Elem<T>::to_f32(dst[r * p.dcstr + c]) : 0.f;
+        }
+        if (act) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              if (cms[u] & (1u << qq)) {
+                const float xv = gcv[u] * wsc[u][qq];
+                acc_t* da = dd[u] + ((qq >> 1) * p.CW + (qq & 1)) * p.CC;
+                if constexpr (kWide) {
+                  const float fh = floorf(xv);
+                  const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
+                  atomicAdd(da, ((unsigned long long)(uint32_t)(int)fh << 32) | lo);
+                } else {
+                  atomicAdd(da, (uint32_t)(int)rintf(xv));
+                }
               }
             }
-          }
         }
       }
       // dOffset of the block's owned entries: lanes = entries (lane & 31);
@@ -266,12 +284,18 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
           const T* b2 = b0 + XW * p.xstr;
           const T* b3 = b2 + p.xstr;
           const int hc = p.CC >> 1;
-          for (int cc = half * hc; cc < (half + 1) * hc; ++cc) {
-            const float gv = Elem<T>::to_f32(drow[cc]);
-            const float v00 = Elem<T>::to_f32(b0[cc]), v01 = Elem<T>::to_f32(b1[cc]);
-            const float v10 = Elem<T>::to_f32(b2[cc]), v11 = Elem<T>::to_f32(b3[cc]);
-            gy = __builtin_fmaf(gv, hx * (v10 - v00) + lx * (v11 - v01), gy);
-            gx = __builtin_fmaf(gv, hy * (v01 - v00) + ly * (v11 - v10), gx);
+          for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
+            float gv[8], v00[8], v01[8], v10[8], v11[8];
+            lds_read8(drow + cc, gv);
+            lds_read8(b0 + cc, v00);
+            lds_read8(b1 + cc, v01);
+            lds_read8(b2 + cc, v10);
+            lds_read8(b3 + cc, v11);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              gy = __builtin_fmaf(gv[k], hx * (v10[k] - v00[k]) + lx * (v11[k] - v01[k]), gy);
+              gx = __builtin_fmaf(gv[k], hy * (v01[k] - v00[k]) + ly * (v11[k] - v10[k]), gx);
+            }
           }
         }
         gy += __shfl_xor(gy, 32);
@@ -701,7 +725,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
     b.CC = p.chunk_b;
     b.dcstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
-    b.num_wg = p.num_btiles * d.offset_groups; b.list_cap = p.list_cap;
+    b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;
     int cb = 0;
     while ((1 << cb) < p.list_cap + 1) ++cb;
     b.capbits = cb;
