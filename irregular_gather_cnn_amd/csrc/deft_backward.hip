@@ -413,31 +413,75 @@ __global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part
 // ([o][pixel], dtype); wave w owns taps tg+w, tg+w+4, tg+w+8.
 struct WoffParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc;
-  int o0, orows, slices, bands, band_rows, num_wg, WoP, XS, DLS;
+  int o0, orows, slices, bands, band_rows, num_wg, WoP, XR, XS, XL, DLS;
+  bool vec_x;  // x rows staged as aligned 16-byte pieces (bf16, W % 8 == 0, PW <= 8)
   const void* x;
   const float* doff;
   float* part;  // [N*bands][Oc][K2][Cin]
 };
 
+// dW_off partial of one (image, 32-channel slice, band of output rows): a
+// GEMM with rows = offset channels, columns = (tap, channel), depth = the
+// band's output pixels.  The band's input rows ([ch][row][XS], column XL is
+// x = 0) and its dOffset rows ([o][row][DLS], bf16) are staged once; the
+// taps then read their shifted windows from LDS.
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int KC = 2 * VEC;  // pixels per k-chunk
   extern __shared__ __align__(16) unsigned char smem[];
-  T* xs = (T*)smem;                                                        // [32][KH][XS]
-  T* dl = (T*)(smem + ((32 * p.KH * p.XS * (int)sizeof(T) + 15) & ~15));  // [MB*32][DLS]
+  T* xs = (T*)smem;                                                                  // [32][XR][XS]
+  T* dl = (T*)(smem + ((32 * p.XR * p.XS * (int)sizeof(T) + 15) & ~15));           // [MB*32][band_rows][DLS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
   const int per_img = p.slices * p.bands;
   const int n = lw / per_img, r = lw - n * per_img;
   const int band = r / p.slices, cs = r - band * p.slices;
-  const int ho0 = band * p.band_rows, ho1 = min(p.Ho, ho0 + p.band_rows);
+  const int ho0 = band * p.band_rows, nrows = min(p.Ho, ho0 + p.band_rows) - ho0;
   const int HoWo = p.Ho * p.Wo;
   const int cl = lane & 31, half = lane >> 5;
   const int c = cs * 32 + cl;
   const T* __restrict__ x = (const T*)p.x;
   const float* __restrict__ doff = p.doff + (size_t)n * p.Oc * HoWo;
-  const int xrow = p.KH * p.XS;
+  const int y0 = ho0 * p.SH - p.PH;  // first input row of the band
+  // ---- stage the band's input rows and dOffset rows ----
+  if (p.vec_x) {
+    const int pieces = p.XS >> 3, tot = 32 * p.XR * pieces;
+    for (int e = tid; e < tot; e += 256) {
+      const int cc = e / (p.XR * pieces), rr = e - cc * (p.XR * pieces);
+      const int ry = rr / pieces, pc = rr - ry * pieces;
+      const int y = y0 + ry, xx = pc * 8 - p.XL;
+      const int ch = cs * 32 + cc;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ch < p.Cin && (unsigned)y < (unsigned)p.H && xx >= 0 && xx < p.W)
+        v = *(const uint4*)(x + (((size_t)n * p.Cin + ch) * p.H + y) * p.W + xx);
+      *(uint4*)(xs + (cc * p.XR + ry) * p.XS + pc * 8) = v;
+    }
+  } else {
+    const int tot = 32 * p.XR * p.XS;
+    for (int e = tid; e < tot; e += 256) {
+      const int cc = e / (p.XR * p.XS), rr = e - cc * (p.XR * p.XS);
+      const int ry = rr / p.XS, xi = rr - ry * p.XS;
+      const int y = y0 + ry, xx = xi - p.XL;
+      const int ch = cs * 32 + cc;
+      T v = zero_elem<T>();
+      if (ch < p.Cin && (unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
+        v = x[(((size_t)n * p.Cin + ch) * p.H + y) * p.W + xx];
+      xs[e] = v;
+    }
+  }
+  {
+    const int tot = MB * 32 * p.band_rows * p.DLS;
+    for (int e = tid; e < tot; e += 256) {
+      const int o = e / (p.band_rows * p.DLS), rr = e - o * (p.band_rows * p.DLS);
+      const int ry = rr / p.DLS, wo = rr - ry * p.DLS;
+      float v = 0.f;
+      if (o < p.orows && ry < nrows && wo < p.Wo) v = doff[(size_t)(p.o0 + o) * HoWo + (size_t)(ho0 + ry) * p.Wo + wo];
+      dl[e] = Elem<T>::from_f32(v);
+    }
+  }
+  __syncthreads();
+  // ---- taps in groups of 12 (three per wave) ----
   for (int tg = 0; tg < p.K2; tg += 12) {
     f32x16_t acc[MB][3];
 #pragma unroll
@@ -446,39 +490,21 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
       for (int j = 0; j < 3; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[mb][j][q] = 0.f;
-    for (int ho = ho0; ho < ho1; ++ho) {
-      __syncthreads();
-      for (int e = tid; e < 32 * xrow; e += 256) {
-        const int cc = e / xrow, rr = e - cc * xrow;
-        const int i = rr / p.XS, xi = rr - i * p.XS;
-        const int y = ho * p.SH - p.PH + i * p.DH, xx = xi - p.PW;
-        const int ch = cs * 32 + cc;
-        T v = zero_elem<T>();
-        if (ch < p.Cin && (unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W)
-          v = x[(((size_t)n * p.Cin + ch) * p.H + y) * p.W + xx];
-        xs[e] = v;
-      }
-      for (int e = tid; e < MB * 32 * p.DLS; e += 256) {
-        const int o = e / p.DLS, wo = e - o * p.DLS;
-        float v = 0.f;
-        if (o < p.orows && wo < p.Wo) v = doff[(size_t)(p.o0 + o) * HoWo + (size_t)ho * p.Wo + wo];
-        dl[e] = Elem<T>::from_f32(v);
-      }
-      __syncthreads();
+    for (int ry = 0; ry < nrows; ++ry) {
       for (int kc = 0; kc < p.WoP; kc += KC) {
         const int w0 = kc + half * VEC;
         uint4 a[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) a[mb] = *(const uint4*)(dl + (mb * 32 + cl) * p.DLS + w0);
+        for (int mb = 0; mb < MB; ++mb) a[mb] = *(const uint4*)(dl + ((mb * 32 + cl) * p.band_rows + ry) * p.DLS + w0);
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
           const int t = tg + wave + 4 * j;
           if (t >= p.K2) break;
           const int ti = t / p.KW, tj = t - ti * p.KW;
-          const T* src = xs + (cl * p.KH + ti) * p.XS + tj * p.DW + w0 * p.SH;
+          const T* src = xs + (cl * p.XR + ry * p.SH + ti * p.DH) * p.XS + p.XL - p.PW + tj * p.DW + w0 * p.SW;
           T v[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = src[e * p.SH];
+          for (int e = 0; e < VEC; ++e) v[e] = src[e * p.SW];
           const uint4 b = *(const uint4*)v;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][j], a[mb], b, T());
@@ -760,14 +786,20 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     w.num_wg = d.n * w.slices * w.bands;
     const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
     w.WoP = (p.wo + kc - 1) / kc * kc;
-    w.XS = (w.WoP - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;
+    w.XR = (w.band_rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
+    // staged row: columns [-XL, XS - XL) of x; XL = 8 keeps x = 0 16-byte aligned
+    const int span = (w.WoP - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;  // from x = -PW
+    w.vec_x = d.dtype == DEFT_BF16 && d.w % 8 == 0 && d.pad_w <= 8;
+    w.XL = w.vec_x ? 8 : d.pad_w;
+    w.XS = w.XL - d.pad_w + span;
+    if (w.vec_x) w.XS = (w.XS + 7) / 8 * 8;
     w.DLS = w.WoP + (d.dtype == DEFT_BF16 ? 8 : 4);
     w.x = a.x; w.doff = doff; w.part = dwoffpart;
     for (int o0 = 0; o0 < p.oc && w.num_wg; o0 += 96) {
       w.o0 = o0;
       w.orows = p.oc - o0 < 96 ? p.oc - o0 : 96;
       const int mb = (w.orows + 31) / 32;
-      const int lds = ((32 * d.kh * w.XS * (int)sizeof(T) + 15) & ~15) + mb * 32 * w.DLS * (int)sizeof(T);
+      const int lds = ((32 * w.XR * w.XS * (int)sizeof(T) + 15) & ~15) + mb * 32 * w.band_rows * w.DLS * (int)sizeof(T);
       if (mb == 1) {
         e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e == hipSuccess)

@@ -102,10 +102,25 @@ bool layout_backward(deft_plan& p) {
   const int wh = (p.btile_h + 2 * p.halo + 1 + d.stride_h - 1) / d.stride_h + 1;
   const int ww = (p.btile_w + 2 * p.halo + 1 + d.stride_w - 1) / d.stride_w + 1;
   p.list_cap = s.taps * std::min(wh, s.ho) * std::min(ww, s.wo);
-  // offset-weight backward: enough (image, channel slice, row band) workgroups
+  // offset-weight backward: (image, channel slice, row band) workgroups; a
+  // band's rows are staged at once, so bands are as tall as two workgroups
+  // per CU allow, and numerous enough to fill the chip
   const int slices = (d.c_in + 31) / 32;
+  const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
+  const int wop = (s.wo + kc - 1) / kc * kc;
+  const int span = (wop - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;
+  const int xs = ((8 + span + 7) / 8) * 8;  // bound on the staged row length
+  const int mbw = std::min(3, (s.oc + 31) / 32);
+  auto woff_lds = [&](int rows) {
+    const int xr = (rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
+    return align16(32 * xr * xs * s.esz) + mbw * 32 * rows * (wop + vec) * s.esz;
+  };
   int bands = 1;
-  while ((double)d.n * slices * bands < 512 && bands * 2 <= s.ho) bands *= 2;
+  while (bands < s.ho) {
+    const int rows = (s.ho + bands - 1) / bands;
+    if (woff_lds(rows) <= kMaxLds / 2 && (double)d.n * slices * bands >= 512) break;
+    ++bands;
+  }
   p.woff_bands = bands;
   return true;
 }
