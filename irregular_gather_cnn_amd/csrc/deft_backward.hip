@@ -536,6 +536,7 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
 struct DxParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc, KKP, KKC;
   int pix_blocks, cblocks, num_wg;
+  FastDiv div_w, div_sh, div_sw;
   const void* wofft;  // [Cin][KKP]
   const float* doff;
   const float* dxs;   // sampling part of dX, fp32
@@ -565,24 +566,39 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
   const int crow = c0 + (lane & 31);
+  int4* kinfo = (int4*)(smem + ((64 * bstr * (int)sizeof(T) + 15) & ~15));  // [KKC]
   for (int kb = 0; kb < p.KKP; kb += p.KKC) {
     const int len = min(p.KKC, p.KKP - kb);
     __syncthreads();
-    for (int e = tid; e < 64 * len; e += 256) {
-      const int pix = e / len, kl = e - pix * len, kk = kb + kl;
-      float v = 0.f;
-      const int q = pix0 + pix;
-      if (kk < p.Oc * p.K2 && q < HW) {
+    // per depth index kk = o*K2 + tap: dOffset plane and the tap's shift
+    for (int kl = tid; kl < len; kl += 256) {
+      const int kk = kb + kl;
+      int4 ki = make_int4(-1, 0, 0, 0);
+      if (kk < p.Oc * p.K2) {
         const int o = kk / p.K2, t = kk - o * p.K2;
         const int ti = t / p.KW, tj = t - ti * p.KW;
-        const int y = q / p.W, xx = q - y * p.W;
-        const int ny = y + p.PH - ti * p.DH, nx = xx + p.PW - tj * p.DW;
-        if (ny >= 0 && nx >= 0 && ny % p.SH == 0 && nx % p.SW == 0) {
-          const int ho = ny / p.SH, wo = nx / p.SW;
-          if (ho < p.Ho && wo < p.Wo) v = doff[(size_t)o * HoWo + (size_t)ho * p.Wo + wo];
-        }
+        ki = make_int4(o * HoWo, p.PH - ti * p.DH, p.PW - tj * p.DW, 0);
       }
-      bt[pix * bstr + kl] = Elem<T>::from_f32(v);
+      kinfo[kl] = ki;
+    }
+    __syncthreads();
+    // B tile: dOffset at the output pixel whose tap lands on the input pixel
+    for (int pix = wave; pix < 64; pix += 4) {
+      const int q = pix0 + pix;
+      const int y = fdiv(q, p.div_w), xx = q - y * p.W;
+      for (int kl = lane; kl < len; kl += 64) {
+        const int4 ki = kinfo[kl];
+        float v = 0.f;
+        const int ny = y + ki.y, nx = xx + ki.z;
+        if (ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
+          int ho = ny, wo = nx;
+          bool ok = true;
+          if (p.SH != 1) { ho = fdiv(ny, p.div_sh); ok = ho * p.SH == ny; }
+          if (p.SW != 1) { wo = fdiv(nx, p.div_sw); ok = ok && wo * p.SW == nx; }
+          if (ok && ho < p.Ho && wo < p.Wo) v = doff[(size_t)ki.x + (size_t)ho * p.Wo + wo];
+        }
+        bt[pix * bstr + kl] = Elem<T>::from_f32(v);
+      }
     }
     __syncthreads();
     if (active) {
@@ -688,8 +704,17 @@ __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ 
       const float* src = first ? dwpart : dwoffpart;
       const size_t stride = first ? n1 : n2;
       const int cnt = first ? ndw : nwp;
+      // loads eight partials ahead, adds them in ascending z
       float s = 0.f;
-      for (int z = 0; z < cnt; ++z) s += src[(size_t)z * stride + f];
+      int z = 0;
+      for (; z + 8 <= cnt; z += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(z + u) * stride + f];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; z < cnt; ++z) s += src[(size_t)z * stride + f];
       (first ? dw : dwoff)[(o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
     } else {
       const int ch = (int)(e - n1 - n2);
@@ -829,7 +854,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     q.cblocks = (d.c_in + 127) / 128;
     q.num_wg = d.n * q.pix_blocks * q.cblocks;
     q.wofft = wofft; q.doff = doff; q.dxs = dxs; q.dx = a.dx;
-    const int lds = 64 * (q.KKC + (d.dtype == DEFT_BF16 ? 8 : 4)) * (int)sizeof(T);
+    q.div_w = make_fastdiv(d.w); q.div_sh = make_fastdiv(d.stride_h); q.div_sw = make_fastdiv(d.stride_w);
+    const int lds = ((64 * (q.KKC + (d.dtype == DEFT_BF16 ? 8 : 4)) * (int)sizeof(T) + 15) & ~15) + q.KKC * 16;
     auto kern = k_dx_final<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
