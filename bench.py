@@ -172,7 +172,13 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(b)
+    # HBM traffic from the committed rocprofv3 counter summary of this
+    # workload, if the dominant kernel's sources still match it
     roof["traffic"] = None
+    from irregular_gather_cnn_amd import profiling
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % wl.name))
+    if dom in tr and tr[dom][1] == profiling.source_hash(dom):
+        roof["traffic"] = tr[dom][0]
 
     total_flop = sum(f for k, (b_, f) in work.items())
     gflops = total_flop / (ms_step * 1e-3) / 1e9

@@ -1,0 +1,186 @@
+"""rocprofv3 summaries for the benchmark: per-kernel durations and HBM traffic.
+
+Two kinds of text summaries live under ``profiles/``:
+
+* kernel statistics of ``rocprofv3 --kernel-trace --stats`` (the
+  ``*_kernel_stats.csv`` the tool writes), one row per kernel;
+* HBM traffic per dispatch from two ``rocprofv3 --pmc`` runs (``FETCH_SIZE``,
+  then ``WRITE_SIZE``, in KiB per dispatch).  Those counters do not read the
+  bytes one-to-one, so each is scaled by what it reads for a plain device copy
+  of known size that the same run performs (``bench.py --calib-copy-mib``).
+  Every traffic row records a hash of the kernel's sources, so a reader can
+  tell whether the kernel changed after the counters were taken.
+
+Usage (after the rocprofv3 runs, on any machine)::
+
+    python -m irregular_gather_cnn_amd.profiling stats STATS_CSV OUT_MD "COMMAND"
+    python -m irregular_gather_cnn_amd.profiling traffic FETCH_DIR WRITE_DIR COPY_MIB OUT_MD "COMMANDS"
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CSRC = os.path.join(_HERE, "csrc")
+
+# benchmark name of a launch -> (pattern of the kernel symbol, source files of the kernel)
+KERNELS = {
+    "fused_offset_sample": (r"k_sample<[^>]*, true", ["deft_sample.hip", "deft_device.h"]),
+    "gemm_forward": (r"k_gemm_dl<.*DlFwd|k_gemm<.*FwdOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "gemm_dw": (r"k_gemm_dl<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "sample_backward": (r"k_sample_bwd<", ["deft_backward.hip", "deft_device.h"]),
+    "sample_backward_miss": (r"k_sample_bwd_miss<", ["deft_backward.hip", "deft_device.h"]),
+    "offset_weight_backward": (r"k_woff_bwd<", ["deft_backward.hip", "deft_device.h"]),
+    "dx_final": (r"k_dx_final<", ["deft_backward.hip", "deft_device.h"]),
+}
+
+
+def source_hash(bench_name: str) -> str:
+    """sha256 (first 16 hex digits) over the kernel's source files."""
+    h = hashlib.sha256()
+    for f in KERNELS[bench_name][1]:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bench_name_of(symbol: str):
+    s = symbol.replace("(anonymous namespace)::", "")
+    for name, (pat, _) in KERNELS.items():
+        if name == "sample_backward" and "k_sample_bwd_miss" in s:
+            continue
+        if re.search(pat, s):
+            return name
+    return None
+
+
+def _rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under %s" % d)
+    out = []
+    for f in files:
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel symbol, grid size, value summed over dimensions)}"""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Dispatch_Id"]
+        sym, grid, v = acc.get(k, (r["Kernel_Name"], int(r["Grid_Size"]), 0.0))
+        acc[k] = (sym, grid, v + float(r["Counter_Value"]))
+    return acc
+
+
+def counter_scale(disp, copy_bytes):
+    """Bytes per counted KiB, from the largest plain copy dispatch of the run."""
+    copies = [(v, g) for (s, g, v) in disp.values() if "copyBuffer" in s]
+    if not copies:
+        raise ValueError("no copy dispatch in the counter run")
+    v = max(copies)[0]
+    return copy_bytes / (v * 1024.0), v
+
+
+def traffic_table(fetch_dir, write_dir, copy_mib):
+    copy_bytes = copy_mib * (1 << 20)
+    f = _per_dispatch(_rows(fetch_dir), "FETCH_SIZE")
+    w = _per_dispatch(_rows(write_dir), "WRITE_SIZE")
+    fs, fcopy = counter_scale(f, copy_bytes)
+    ws, wcopy = counter_scale(w, copy_bytes)
+    per = defaultdict(lambda: [[], []])
+    for disp, idx in ((f, 0), (w, 1)):
+        for sym, grid, v in disp.values():
+            name = bench_name_of(sym)
+            if name:
+                per[name][idx].append(v)
+    table = {}
+    for name, (fv, wv) in per.items():
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        table[name] = dict(fetch_kib=fk, write_kib=wk, fetch_bytes=fk * 1024 * fs, write_bytes=wk * 1024 * ws,
+                           traffic=fk * 1024 * fs + wk * 1024 * ws, dispatches=len(fv), src=source_hash(name))
+    return table, dict(fetch_scale=fs, write_scale=ws, copy_fetch_kib=fcopy, copy_write_kib=wcopy,
+                       copy_bytes=copy_bytes)
+
+
+def write_traffic_md(path, table, calib, commands):
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (from the repository root, on the GPU machine):", "", "```"] + commands + ["```", "",
+             "Calibration: a plain device copy of %d bytes reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per "
+             "dispatch, so one counted KiB is %.4f bytes fetched and %.4f bytes written."
+             % (calib["copy_bytes"], calib["copy_fetch_kib"], calib["copy_write_kib"], calib["fetch_scale"],
+                calib["write_scale"]), "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB | traffic bytes "
+             "| source hash |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name in sorted(table):
+        t = table[name]
+        lines.append("| %s | %d | %.1f | %.1f | %.2f | %.2f | %d | %s |" % (
+            name, t["dispatches"], t["fetch_kib"], t["write_kib"], t["fetch_bytes"] / 1e6, t["write_bytes"] / 1e6,
+            int(t["traffic"]), t["src"]))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def read_traffic(path):
+    """{kernel: (traffic bytes per dispatch, source hash)} from a summary written above."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"\|\s*(\w+)\s*\|\s*\d+\s*\|[^|]*\|[^|]*\|[^|]*\|[^|]*\|\s*(\d+)\s*\|\s*(\w+)\s*\|", line)
+            if m:
+                out[m.group(1)] = (int(m.group(2)), m.group(3))
+    return out
+
+
+def write_stats_md(stats_csv, path, command):
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = ["# Kernel statistics (rocprofv3 --kernel-trace --stats)", "", "Command (from the repository root):", "",
+             "```", command, "```", "",
+             "| kernel | bench name | calls | total ms | average us | min us | max us | share % |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or ""
+        calls = int(float(r.get("Calls", 0)))
+        tot = float(r.get("TotalDurationNs", 0)) / 1e6
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))[:70]
+        lines.append("| `%s` | %s | %d | %.3f | %.1f | %.1f | %.1f | %.2f |" % (
+            short, bench_name_of(name) or "", calls, tot, avg, mn, mx, pct))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def main(argv):
+    if len(argv) >= 4 and argv[0] == "stats":
+        write_stats_md(argv[1], argv[2], argv[3])
+    elif len(argv) >= 6 and argv[0] == "traffic":
+        table, calib = traffic_table(argv[1], argv[2], int(argv[3]))
+        write_traffic_md(argv[4], table, calib, argv[5].split("\n"))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
