@@ -51,6 +51,12 @@ struct BwdParams {
 };
 
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+// float -> int32 rounded to nearest (halves up), one instruction
+__device__ __forceinline__ int cvt_rpi(float x) {
+  int r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }
 
 // Corner q of a tap: (y0 + (q >> 1), x0 + (q & 1)), the order of tap_weights.
@@ -83,9 +89,10 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   // can touch it).  The per-tap rectangles are flattened into one index space
   // and evaluated four per thread per step, loads first.
   int* rlo_h = cnt + 4;          // per tap: first output row / column of the
-  int* rlo_w = rlo_h + 48;        // candidate rectangle, its width, and the
-  int* rnw = rlo_w + 48;          // prefix sum of the rectangle sizes
-  int* rstart = rnw + 48;
+  int* rlo_w = rlo_h + 48;        // candidate rectangle, its width (as a
+  int* rnw = rlo_w + 48;          // divisor), and the prefix sum of the
+  int* rstart = rnw + 48;         // rectangle sizes
+  uint32_t* rdiv = (uint32_t*)(rstart + 49);  // [48][2] FastDiv of the widths
   if (tid < p.K2) {
     const int t = tid;
     const int ti = t / p.KW, tj = t - ti * p.KW;
@@ -95,6 +102,8 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     const int wo_hi = min(p.Wo - 1, floor_div(X0 + cwn - 1 + p.halo + p.PW - tj * p.DW, p.SW));
     const int nh = max(0, ho_hi - ho_lo + 1), nw = max(0, wo_hi - wo_lo + 1);
     rlo_h[t] = ho_lo; rlo_w[t] = wo_lo; rnw[t] = nw > 0 ? nw : 1;
+    const FastDiv fd = make_fastdiv(nw > 0 ? nw : 1);
+    rdiv[2 * t] = fd.m; rdiv[2 * t + 1] = fd.s;
     rstart[t + 1] = nh * nw;
   }
   if (tid == 0) *cnt = 0;
@@ -107,19 +116,22 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const int ncand = rstart[p.K2];
   for (int e0 = tid; e0 < ncand; e0 += 4 * 256) {
     float dyv[4], dxv[4];
-    int tt[4], pp[4];
+    int tt[4], pp[4], hh[4], ww[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * 256;
       tt[u] = -1;
       dyv[u] = dxv[u] = 0.f;
-      pp[u] = 0;
+      pp[u] = hh[u] = ww[u] = 0;
       if (e < ncand) {
         int t = 0;
         while (e >= rstart[t + 1]) ++t;
         const int k = e - rstart[t];
-        const int ho = rlo_h[t] + k / rnw[t], wo = rlo_w[t] + k % rnw[t];
+        const FastDiv fd{rdiv[2 * t], rdiv[2 * t + 1]};
+        const int kr = fdiv(k, fd);
+        const int ho = rlo_h[t] + kr, wo = rlo_w[t] + (k - kr * rnw[t]);
         tt[u] = t;
+        hh[u] = ho; ww[u] = wo;
         pp[u] = ho * p.Wo + wo;
         dyv[u] = offn[(size_t)(2 * t) * HoWo + pp[u]];
         dxv[u] = offn[(size_t)(2 * t + 1) * HoWo + pp[u]];
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
       const int t = tt[u];
       if (t < 0) continue;
       const int ti = t / p.KW, tj = t - ti * p.KW;
-      const int ho = pp[u] / p.Wo, wo = pp[u] - ho * p.Wo;
+      const int ho = hh[u], wo = ww[u];
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
       const TapIndex ix = tap_index(by, bx, dyv[u], dxv[u], p.H, p.W);
       if (ix.outside) continue;
@@ -182,7 +194,8 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const bool act = c < p.CC;
   const size_t HW = (size_t)p.H * p.W;
   T* dst = (T*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;
-  acc_t* dxl = (acc_t*)(smem + p.lds_dx);  // [CH*CW][CC]
+  acc_t* dxl = (acc_t*)(smem + p.lds_dx);  // [CH*CW][CC], then one spill slot per lane
+  acc_t* spill = dxl + p.CH * p.CW * p.CC + lane;
   const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
   const int epi = 64 / lpe;    // rows per load instruction
   const size_t pstride = (size_t)p.N * p.Oc * HoWo;
@@ -224,17 +237,15 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
-      // scatter: lanes = channels, two entries per step (independent
-      // instruction streams for the scheduler)
-      for (int r0 = 0; r0 < nb; r0 += 2) {
-        acc_t* dd[2];
-        uint32_t cms[2];
-        float wsc[2][4], gcv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = min(r0 + u, nb - 1);
+      // scatter: lanes = channels.  bf16: eight entries per step, their dCol
+      // values read from LDS together; every corner issues its atomic, and
+      // corners outside the core add into a per-lane spill slot (lanes beyond
+      // the chunk add zero), so the step has no branches.
+      const int nbs = __builtin_amdgcn_readfirstlane(nb);
+      if constexpr (kWide) {
+        for (int r = 0; r < nbs; ++r) {
           const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
-          cms[u] = (r0 + u < nb) ? (info >> 9) & 15u : 0u;
+          const uint32_t cm = (info >> 9) & 15u;
           const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
           TapIndex ix;
           ix.outside = false;
@@ -242,28 +253,48 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
           ix.lx = __int_as_float(__builtin_amdgcn_readlane(cur.w, r));
           float w[4];
           tap_weights(ix, w);
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) wsc[u][qq] = w[qq] * sc;
-          dd[u] = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
-          gcv[u] = act ? Elem<T>::to_f32(dst[r * p.dcstr + c]) : 0.f;
-        }
-        if (act) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
+          if (act) {
+            const float gs = Elem<T>::to_f32(dst[r * p.dcstr + c]) * sc;
+            acc_t* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-              if (cms[u] & (1u << qq)) {
-                const float xv = gcv[u] * wsc[u][qq];
-                acc_t* da = dd[u] + ((qq >> 1) * p.CW + (qq & 1)) * p.CC;
-                if constexpr (kWide) {
-                  const float fh = floorf(xv);
-                  const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
-                  atomicAdd(da, ((unsigned long long)(uint32_t)(int)fh << 32) | lo);
-                } else {
-                  atomicAdd(da, (uint32_t)(int)rintf(xv));
-                }
+              if (cm & (1u << qq)) {
+                const float xv = gs * w[qq];
+                const float fh = floorf(xv);
+                const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
+                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC,
+                          ((unsigned long long)(uint32_t)(int)fh << 32) | lo);
               }
             }
+          }
+        }
+      } else {
+        const int cr = min(c, p.CC - 1);
+        const float scl = act ? sc : 0.f;
+        for (int r0 = 0; r0 < nbs; r0 += 8) {
+          float gs[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) gs[u] = Elem<T>::to_f32(dst[min(r0 + u, nbs - 1) * p.dcstr + cr]) * scl;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r = r0 + u;
+            if (r >= nbs) break;
+            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
+            const uint32_t cm = (info >> 9) & 15u;
+            const int cy = (info >> 16) & 255, cx = info >> 24;
+            TapIndex ix;
+            ix.outside = false;
+            ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
+            ix.lx = __int_as_float(__builtin_amdgcn_readlane(cur.w, r));
+            float w[4];
+            tap_weights(ix, w);
+            acc_t* d0 = dxl + ((cy - 1) * p.CW + (cx - 1)) * p.CC + c;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              acc_t* da = ((cm >> qq) & 1u) ? d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC : spill;
+              atomicAdd(da, (uint32_t)cvt_rpi(gs[u] * w[qq]));
+            }
+          }
         }
       }
       // dOffset of the block's owned entries: lanes = entries (lane & 31);

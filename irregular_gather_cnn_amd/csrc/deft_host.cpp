@@ -88,9 +88,9 @@ bool layout_backward(deft_plan& p) {
   const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
   const int xstr = cb + vec;
   const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
-  const int ldx = align16(ch * cw * cb * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core
+  const int ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core + spill slots
   const int ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
-  const int total = lx + ldx + ldc + 16 + 4 * 49 * 4;  // + list counter and per-tap tables
+  const int total = lx + ldx + ldc + 16 + 4 * 49 * 4 + 48 * 8;  // + list counter and per-tap tables
   if (total > kMaxLds) return false;
   p.btile_h = ch; p.btile_w = cw;
   p.btiles_h = (d.h + ch - 1) / ch; p.btiles_w = (d.w + cw - 1) / cw;
