@@ -47,7 +47,9 @@ struct BwdParams {
   const uint32_t* maxbits;  // max |dcol| as fp32 bits
   float* dxs;    // [N][Cin][H][W] fp32: the sampling part of dX
   float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials, zeroed beforehand
-  int4* lists;   // [num_wg][list_cap]: each workgroup's own list
+  int4* lists;   // [num_tg][list_cap]: one list per (core, group)
+  int* counts;   // [num_tg]: entries in each list
+  int num_tg;    // cores x groups
 };
 
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
@@ -59,16 +61,13 @@ __device__ __forceinline__ int cvt_rpi(float x) {
 }
 __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }
 
-// Corner q of a tap: (y0 + (q >> 1), x0 + (q & 1)), the order of tap_weights.
-template <typename T>
-__global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // one workgroup per (core tile, offset group, channel chunk): the chunks
-  // of one core are neighbours in the XCD-aware order and share its offsets
-  const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
-  const int nchunks = p.Cg / p.CC;
-  const int tg = lw / nchunks, chunk = lw - tg * nchunks;
+// The (output pixel, tap) pairs whose corners touch one core tile of input
+// pixels (for one offset group), written to that core's list; shared by the
+// core's channel-chunk workgroups of k_sample_bwd.
+__global__ __launch_bounds__(256) void k_sample_bwd_list(const BwdParams p) {
+  __shared__ int tabs[4 + 48 * 3 + 49 + 96];
+  const int tid = threadIdx.x;
+  const int tg = xcd_swizzle(blockIdx.x, p.num_tg);
   const int tile = tg / p.G, g = tg - tile * p.G;
   const int tpi = p.bt_h * p.bt_w;
   const int n = tile / tpi, trem = tile - n * tpi;
@@ -76,12 +75,9 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
   const int obase = 2 * g * p.K2;
   const int HoWo = p.Ho * p.Wo;
-  T* xl = (T*)smem;  // [(CH+2)*(CW+2)][xstr]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
-  int* cnt = (int*)(smem + p.lds_cnt);
-  int4* list = p.lists + (size_t)lw * p.list_cap;
+  int* cnt = tabs;
+  int4* list = p.lists + (size_t)tg * p.list_cap;
   const float* __restrict__ offn = p.off + ((size_t)n * p.Oc + obase) * HoWo;
-  const T* __restrict__ x = (const T*)p.x;
-  const T* __restrict__ dcol = (const T*)p.dcol;
 
   // ---- the pairs touching this core ----
   // Candidates: for every tap, the output pixels whose tap grid point lies
@@ -163,7 +159,33 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     }
   }
   __syncthreads();
-  const int L = *cnt;
+  __syncthreads();
+  if (tid == 0) p.counts[tg] = *cnt;
+}
+
+// Corner q of a tap: (y0 + (q >> 1), x0 + (q & 1)), the order of tap_weights.
+template <typename T>
+__global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // one workgroup per (core tile, offset group, channel chunk): the chunks
+  // of one core are neighbours in the XCD-aware order and share its offsets
+  const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
+  const int nchunks = p.Cg / p.CC;
+  const int tg = lw / nchunks, chunk = lw - tg * nchunks;
+  const int tile = tg / p.G, g = tg - tile * p.G;
+  const int tpi = p.bt_h * p.bt_w;
+  const int n = tile / tpi, trem = tile - n * tpi;
+  const int Y0 = (trem / p.bt_w) * p.CH, X0 = (trem % p.bt_w) * p.CW;
+  const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
+  const int obase = 2 * g * p.K2;
+  const int HoWo = p.Ho * p.Wo;
+  T* xl = (T*)smem;  // [(CH+2)*(CW+2)][xstr]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
+  const int4* list = p.lists + (size_t)tg * p.list_cap;
+  const T* __restrict__ x = (const T*)p.x;
+  const T* __restrict__ dcol = (const T*)p.dcol;
+
+  const int L = p.counts[tg];
 
   // ---- per channel chunk: stage, scatter, dOffset, write the core ----
   // dX is accumulated in fixed point with integer LDS atomics (fast on this
@@ -815,6 +837,11 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
     b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
     b.lists = lists;
+    b.num_tg = p.num_btiles * d.offset_groups;
+    b.counts = (int*)(ws + p.ws_lcount);
+    if (b.num_tg) DEFT_LAUNCH("sample_backward_list", k_sample_bwd_list, dim3(b.num_tg), dim3(256), 0, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     auto kern = k_sample_bwd<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
     if (e != hipSuccess) return e;

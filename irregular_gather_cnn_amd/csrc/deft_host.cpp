@@ -173,7 +173,8 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   p.ws_dx32 = o; o = align256(o + (size_t)d.n * d.c_in * d.h * d.w * 4);
   p.ws_doff = o; o = align256(o + P * s.oc * 4);
   p.ws_list = o;
-  o = align256(o + (size_t)p.num_btiles * d.offset_groups * (p.chunk_b ? s.cg / p.chunk_b : 1) * p.list_cap * 16);
+  o = align256(o + (size_t)p.num_btiles * d.offset_groups * p.list_cap * 16);
+  p.ws_lcount = o; o = align256(o + (size_t)p.num_btiles * d.offset_groups * 4);
   // dOffset partials (one per backward channel chunk) followed by one word
   // for max |dCol|; both zeroed by the backward's prep kernel
   p.ws_doffp = o;

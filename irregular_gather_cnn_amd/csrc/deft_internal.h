@@ -28,7 +28,7 @@ struct deft_plan {
   int btile_h, btile_w, btiles_h, btiles_w, num_btiles, list_cap;
   int chunk_b, lb_dx, lb_dc, lb_cnt, lb_total;
   int woff_bands;              // row bands of the offset-weight backward
-  size_t ws_list, ws_doffp, ws_maxbits, ws_dwpart, ws_dwoffpart, ws_biaspart;
+  size_t ws_list, ws_lcount, ws_doffp, ws_maxbits, ws_dwpart, ws_dwoffpart, ws_biaspart;
   // bf16 GEMMs with direct global-to-LDS staging (else the generic kernel)
   int gemm_dl;
   int dw_splits, dw_kper;      // dW partials: pixel ranges of dw_kper (per image on the generic path)
