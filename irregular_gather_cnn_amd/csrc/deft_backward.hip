@@ -467,7 +467,6 @@ __global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part
 struct WoffParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc;
   int o0, orows, slices, bands, band_rows, num_wg, WoP, XR, XS, XL, DLS;
-  bool vec_x;  // x rows staged as aligned 16-byte pieces (bf16, W % 8 == 0, PW <= 8)
   const void* x;
   const float* doff;
   float* part;  // [N*bands][Oc][K2][Cin]
@@ -483,7 +482,7 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int KC = 2 * VEC;  // pixels per k-chunk
   extern __shared__ __align__(16) unsigned char smem[];
-  T* xs = (T*)smem;                                                                  // [32][XR][XS]
+  T* xs = (T*)smem;  // bf16: [XR][XS][32]; fp32: [32][XR][XS]
   T* dl = (T*)(smem + ((32 * p.XR * p.XS * (int)sizeof(T) + 15) & ~15));           // [MB*32][band_rows][DLS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
@@ -498,18 +497,14 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   const float* __restrict__ doff = p.doff + (size_t)n * p.Oc * HoWo;
   const int y0 = ho0 * p.SH - p.PH;  // first input row of the band
   // ---- stage the band's input rows and dOffset rows ----
-  if (p.vec_x) {
-    const int pieces = p.XS >> 3, tot = 32 * p.XR * pieces;
-    for (int e = tid; e < tot; e += 256) {
-      const int cc = e / (p.XR * pieces), rr = e - cc * (p.XR * pieces);
-      const int ry = rr / pieces, pc = rr - ry * pieces;
-      const int y = y0 + ry, xx = pc * 8 - p.XL;
-      const int ch = cs * 32 + cc;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ch < p.Cin && (unsigned)y < (unsigned)p.H && xx >= 0 && xx < p.W)
-        v = *(const uint4*)(x + (((size_t)n * p.Cin + ch) * p.H + y) * p.W + xx);
-      *(uint4*)(xs + (cc * p.XR + ry) * p.XS + pc * 8) = v;
-    }
+  // bf16: x as [row][pixel][32 channels] (pixel = x + PW), read as MFMA
+  // fragments with transposed LDS reads; fp32: [channel][row][XS].
+  constexpr bool kHwc = sizeof(T) == 2;
+  if constexpr (kHwc) {
+    const int nc = min(32, p.Cin - cs * 32);
+    const FastDiv drh = make_fastdiv(p.XR);
+    const StageGeom sg = stage_geom<T>(p.W, -p.PW, p.XS, (size_t)p.Cin * p.H * p.W);
+    stage_region<T>(xs, x, p.Cin, p.H, p.W, n, cs * 32, nc, y0, -p.PW, p.XR, p.XS, drh, sg, 32);
   } else {
     const int tot = 32 * p.XR * p.XS;
     for (int e = tid; e < tot; e += 256) {
@@ -554,11 +549,29 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
           const int t = tg + wave + 4 * j;
           if (t >= p.K2) break;
           const int ti = t / p.KW, tj = t - ti * p.KW;
-          const T* src = xs + (cl * p.XR + ry * p.SH + ti * p.DH) * p.XS + p.XL - p.PW + tj * p.DW + w0 * p.SW;
-          T v[VEC];
+          uint4 b;
+          if constexpr (kHwc) {
+            // lane: channel n = lane % 32, pixels kc + 8*(lane/32) + 0..7, as
+            // two transposed reads of 4 pixel rows x 4 channels per 16 lanes
+            const int g4 = lane >> 4, j4 = lane & 15;
+            const T* rowb = xs + (size_t)(ry * p.SH + ti * p.DH) * p.XS * 32 + 16 * (g4 & 1) + 4 * (j4 & 3);
+            uint2 hh[2];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = src[e * p.SW];
-          const uint4 b = *(const uint4*)v;
+            for (int h = 0; h < 2; ++h) {
+              const int wo = kc + 8 * (g4 >> 1) + 4 * h + (j4 >> 2);
+              const bf16_t* a16 = (const bf16_t*)(rowb + (size_t)(wo * p.SW + tj * p.DW) * 32);
+              typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+              hh[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                    (__attribute__((address_space(3))) bf16x4_t*)a16));
+            }
+            b = make_uint4(hh[0].x, hh[0].y, hh[1].x, hh[1].y);
+          } else {
+            const T* src = xs + (cl * p.XR + ry * p.SH + ti * p.DH) * p.XS + p.XL - p.PW + tj * p.DW + w0 * p.SW;
+            T v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = src[e * p.SW];
+            b = *(const uint4*)v;
+          }
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][j], a[mb], b, T());
         }
@@ -872,10 +885,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     w.XR = (w.band_rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
     // staged row: columns [-XL, XS - XL) of x; XL = 8 keeps x = 0 16-byte aligned
     const int span = (w.WoP - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;  // from x = -PW
-    w.vec_x = d.dtype == DEFT_BF16 && d.w % 8 == 0 && d.pad_w <= 8;
-    w.XL = w.vec_x ? 8 : d.pad_w;
-    w.XS = w.XL - d.pad_w + span;
-    if (w.vec_x) w.XS = (w.XS + 7) / 8 * 8;
+    w.XL = d.pad_w;
+    w.XS = span;  // pixels per staged row, from x = -PW
     w.DLS = w.WoP + (d.dtype == DEFT_BF16 ? 8 : 4);
     w.x = a.x; w.doff = doff; w.part = dwoffpart;
     for (int o0 = 0; o0 < p.oc && w.num_wg; o0 += 96) {
