@@ -632,6 +632,18 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
   const int crow = c0 + (lane & 31);
+  // the sampling part of dX for this lane's outputs, loaded up front so the
+  // loads overlap the dOffset tile and the MFMAs
+  float sv[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = pix0 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int r2 = 0; r2 < 16; ++r2) {
+      const int cc = c0 + acc_row(lane, r2);
+      sv[j][r2] = (active && q < HW && cc < p.Cin) ? p.dxs[((size_t)n * p.Cin + cc) * HW + q] : 0.f;
+    }
+  }
   int4* kinfo = (int4*)(smem + ((64 * bstr * (int)sizeof(T) + 15) & ~15));  // [KKC]
   for (int kb = 0; kb < p.KKP; kb += p.KKC) {
     const int len = min(p.KKC, p.KKP - kb);
@@ -691,7 +703,7 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
       const int cc = c0 + acc_row(lane, r2);
       if (cc < p.Cin) {
         const size_t idx = ((size_t)n * p.Cin + cc) * HW + q;
-        dx[idx] = Elem<T>::from_f32(acc[j][r2] + p.dxs[idx]);
+        dx[idx] = Elem<T>::from_f32(acc[j][r2] + sv[j][r2]);
       }
     }
   }
