@@ -88,6 +88,9 @@ typedef struct deft_plan_info {
                              loads (bf16, Ho*Wo and c_out multiples of 8, operands under
                              2 GiB); 0: register-staged generic GEMM */
   int dw_splits;          /* pixel ranges the dW GEMM is split into (one fp32 partial each) */
+  int gather_direct;      /* 1: the forward gathers corners from a channel-minor copy of x held
+                             in the caches (no LDS halo; halo then bounds only the backward's
+                             candidate window); 0: LDS tile + halo */
 } deft_plan_info;
 
 /* Checks the descriptor alone.  Pure host function. */
@@ -107,8 +110,10 @@ int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len
                      deft_plan** out);
 
 /* Plan with a forced tile (tile_h*tile_w <= 64), halo (0..32) and channel
- * chunk (multiple of 16 dividing Cin/G, at most 64; 0 = largest that fits).
- * DEFT_ERR_PLAN if its LDS does not fit; deft_backward returns DEFT_ERR_PLAN
+ * chunk (multiple of 16 dividing Cin/G, at most 64; 0 = largest that fits;
+ * -1 = direct gather: the forward reads the corners from a channel-minor copy
+ * of x instead of an LDS halo, bf16 only, Cin/(8G) a power of two <= 256).
+ * DEFT_ERR_PLAN if its LDS does not fit or the direct gather is unsupported; deft_backward returns DEFT_ERR_PLAN
  * for a forced plan whose backward tile does not fit even with 8 channels.
  * Forward results (offsets, columns, y) are bit-identical across plans; the
  * backward's atomically accumulated sums (dx, dw, dw_off) and the per-chunk

@@ -278,6 +278,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   r.w = 0x00020000;
   return r;
 }
+constexpr int kOOB = (int)0x80000000;  // buffer offset past any range: loads return zero
+
+typedef __attribute__((address_space(3))) void lds_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from the buffer straight into LDS at dst + 16*lane.
+// Written as inline assembly so the compiler does not order every later LDS
+// read behind these loads; completion is awaited explicitly (wait_vm).
+__device__ __forceinline__ void load_lds16(const rsrc_t r, unsigned char* dst, int voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_t*)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ximg: buffer over one image; c0: first channel of the chunk.  Words outside
 // the image read as zero through the buffer range check.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_brsrc(const void* p, uint32_t bytes) {

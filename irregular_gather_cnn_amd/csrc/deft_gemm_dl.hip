@@ -37,28 +37,9 @@ constexpr int kEpiStride = kWave * 2 + 16;                 // bytes per transpos
 constexpr int kLdsEpi = 4 * kWave * kEpiStride;            // 136 KB
 constexpr int kLds = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
 constexpr int kPerWave = kTile * kBK * 2 / 1024 / 4;      // 1 KB loads per wave per operand per stage
-constexpr int kOOB = (int)0x80000000;
-
-typedef __attribute__((address_space(3))) void lds_t;
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
-// 16 bytes per lane from the buffer straight into LDS at dst + 16*lane.
-// Written as inline assembly so the compiler does not order every later LDS
-// read behind these loads; completion is awaited explicitly (wait_vm).
-__device__ __forceinline__ void load_lds16(const rsrc_t r, unsigned char* dst, int voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_t*)dst);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-               : "memory");
-}
-
 __device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
   const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
   return __builtin_bit_cast(uint2, v);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Row-form swizzle (64-byte rows, 4 chunks): 16 consecutive rows reading the

@@ -125,11 +125,26 @@ bool layout_backward(deft_plan& p) {
   return true;
 }
 
-// Fills every derived field of a plan for the given tile / halo / chunk.
-// Returns false if the LDS does not fit.
-bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
+// The direct-gather forward (corners from a channel-minor copy of x) needs
+// bf16, at most 9 taps (one block of offset channels, at most three units
+// per wave and chunk), a power-of-two number of 8-channel slices per group
+// (at most 256) and byte offsets below 2^31 within one image's copy.
+bool direct_ok(const deft_desc& d) {
+  const Shape s = shape_of(d);
+  const int nv = s.cg / 8;
+  return d.dtype == DEFT_BF16 && d.c_in % 16 == 0 && s.taps <= 9 && nv >= 1 && nv <= 256 &&
+         (nv & (nv - 1)) == 0 && ((size_t)d.h * d.w + 1) * d.c_in < 0x40000000u;
+}
+
+// Fills every derived field of a plan for the given tile / halo / chunk
+// (direct: the forward gathers from the channel-minor copy; the halo then
+// only bounds the backward's candidate window).  Returns false if the LDS
+// does not fit.
+bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct = false) {
   const deft_desc& d = p.d;
   const Shape s = shape_of(d);
+  if (direct && !direct_ok(d)) return false;
+  p.direct = direct ? 1 : 0;
   p.ho = s.ho; p.wo = s.wo; p.taps = s.taps; p.oc = s.oc; p.cg = s.cg; p.ck = s.ck;
   p.tile_h = th; p.tile_w = tw; p.halo = halo; p.chunk = chunk;
   p.chunk_a = d.c_in % 64 == 0 ? 64 : (d.c_in % 32 == 0 ? 32 : 16);
@@ -153,9 +168,22 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   const int region = std::max({p.foot_h * p.foot_w * p.pstr_a * s.esz, p.reg_h * p.reg_w * p.pstr * s.esz,
                                4 * ocw * pt * 4});
   p.lds_region = 0;
-  p.lds_off = align16(region);
-  p.lds_info = p.lds_off + align16(ocw * pt * 4);
-  p.lds_total = p.lds_info + align16(p.gw * s.taps * pt * 8) + p.gw * s.taps * pt * 16;  // tap table + weights
+  p.stage_d = 0;
+  if (direct) {
+    // offsets, then one region shared in turn by the double-buffered
+    // footprint staging (256 * stage_d 16-byte slots per buffer), the
+    // phase-A partial sums and the tap table (int4) + weights (float4)
+    p.stage_d = (p.foot_h * p.foot_w * (p.chunk_a / 8) + 255) / 256;
+    if (p.stage_d > 7) return false;
+    p.lds_off = 0;
+    p.lds_info = align16(ocw * pt * 4);
+    p.lds_region = p.lds_info;
+    p.lds_total = p.lds_info + std::max({4 * ocw * pt * 4, 32 * s.taps * pt, 2 * p.stage_d * 4096});
+  } else {
+    p.lds_off = align16(region);
+    p.lds_info = p.lds_off + align16(ocw * pt * 4);
+    p.lds_total = p.lds_info + align16(p.gw * s.taps * pt * 8) + p.gw * s.taps * pt * 16;  // tap table + weights
+  }
   if (p.lds_total > kMaxLds) return false;
   p.num_btiles = 0; p.list_cap = 0; p.woff_bands = 1;
   if (!layout_backward(p)) p.chunk_b = 0;
@@ -164,8 +192,11 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk) {
   p.kk_pad = (s.oc * s.taps + 15) / 16 * 16;
   size_t o = 0;
   p.ws_wt = o; o = align256(o + (size_t)d.c_out * s.ck * s.esz);
-  p.ws_woff = o; o = align256(o + (size_t)p.oc_pad * s.ck * s.esz);
+  p.ws_woff = o;
+  o = align256(o + (size_t)std::max(p.oc_pad, 32 * d.offset_groups) * s.ck * s.esz);  // rows or fragments
   p.ws_cols = o; o = align256(o + P * s.ck * s.esz);
+  p.ws_xh = o;
+  if (direct) o = align256(o + (size_t)d.n * ((size_t)d.h * d.w + 1) * d.c_in * s.esz);
   p.ws_fwd_end = o;
   p.ws_w2 = o; o = align256(o + (size_t)s.ck * d.c_out * s.esz);
   p.ws_wofft = o; o = align256(o + (size_t)d.c_in * p.kk_pad * s.esz);
@@ -309,13 +340,16 @@ int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo
   if (v) return v;
   const Shape s = shape_of(*d);
   if (tile_h < 1 || tile_w < 1 || tile_h * tile_w > 64 || halo < 0 || halo > 32) return DEFT_ERR_PLAN;
-  if (chunk != 0 && (chunk < 16 || chunk > 64 || chunk % 16 || s.cg % chunk)) return DEFT_ERR_PLAN;
+  if (chunk != 0 && chunk != -1 && (chunk < 16 || chunk > 64 || chunk % 16 || s.cg % chunk)) return DEFT_ERR_PLAN;
+  if (chunk == -1 && !direct_ok(*d)) return DEFT_ERR_PLAN;
   deft_plan* p = new (std::nothrow) deft_plan();
   if (!p) return DEFT_ERR_UNSUPPORTED;
   p->d = *d;
   p->num_btiles = 0;
   bool ok = false;
-  if (chunk != 0) {
+  if (chunk == -1) {
+    ok = layout_plan(*p, tile_h, tile_w, halo, s.cg, true);
+  } else if (chunk != 0) {
     ok = layout_plan(*p, tile_h, tile_w, halo, chunk);
   } else {
     for (int c = 64; c >= 16 && !ok; c /= 2)
@@ -344,6 +378,7 @@ int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
   info->bwd_tile_w = p->btile_w;
   info->bwd_chunk = p->chunk_b;
   info->gemm_direct = p->gemm_dl;
+  info->gather_direct = p->direct;
   info->dw_splits = p->dw_splits;
   return DEFT_OK;
 }
@@ -374,6 +409,7 @@ int deft_forward(const deft_plan* p, const void* x, const void* w_off, const voi
   deft::SampleArgs a;
   a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_in = nullptr; a.off_out = offsets_out;
   a.cols = ws + p->ws_cols;
+  a.xh = ws + p->ws_xh;
   e = deft::launch_sample(*p, true, a, st);
   if (e != hipSuccess) return hip_fail(e);
   e = deft::launch_gemm_forward(*p, ws + p->ws_wt, ws + p->ws_cols, b, y, st);
@@ -422,6 +458,18 @@ int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, v
   if (p->d.n == 0) return DEFT_OK;
   deft::SampleArgs a;
   a.x = x; a.woff_p = nullptr; a.b_off = nullptr; a.off_in = offsets; a.off_out = nullptr; a.cols = cols;
+  if (p->direct) {
+    // sampling from given offsets always uses the LDS tile + halo kernel
+    // (it has no workspace for the channel-minor copy)
+    deft_plan q{};
+    q.d = p->d;
+    bool ok = false;
+    for (int c = 64; c >= 16 && !ok; c /= 2)
+      if (p->cg % c == 0) ok = layout_plan(q, p->tile_h, p->tile_w, p->halo, c);
+    if (!ok) return DEFT_ERR_PLAN;
+    const hipError_t e = deft::launch_sample(q, false, a, (hipStream_t)stream);
+    return e == hipSuccess ? DEFT_OK : hip_fail(e);
+  }
   const hipError_t e = deft::launch_sample(*p, false, a, (hipStream_t)stream);
   return e == hipSuccess ? DEFT_OK : hip_fail(e);
 }

@@ -17,10 +17,12 @@ struct deft_plan {
   int reg_h, reg_w;            // largest halo region (input pixels)
   int pstr, pstr_a;            // LDS pixel strides (elements)
   int lds_region, lds_off, lds_info, lds_total;  // byte offsets / total
+  int direct;
+  int stage_d;  // direct: footprint-staging loads per wave per channel chunk                  // 1: corners gathered from a channel-minor copy of x (no LDS halo)
   int oc_pad;                  // rows of the prepared offset-conv weight
   double est_miss;
   // workspace layout (byte offsets, 256-aligned)
-  size_t ws_wt, ws_woff, ws_cols, ws_fwd_end;
+  size_t ws_wt, ws_woff, ws_cols, ws_xh, ws_fwd_end;
   size_t ws_w2, ws_dcol, ws_dx32, ws_doff, ws_wofft, ws_train_end;
   int kk_pad;                  // padded (o, tap) depth of the transposed offset conv
   // sampling backward: each workgroup owns a core tile of input pixels
@@ -54,6 +56,7 @@ struct SampleArgs {
   const float* off_in;     // unfused: offsets to sample from
   float* off_out;          // nullable
   void* cols;              // [N*Ho*Wo][taps][Cin]
+  void* xh;                // direct gather: channel-minor copy of x (workspace)
 };
 
 hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt,

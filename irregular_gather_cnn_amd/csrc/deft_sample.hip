@@ -33,6 +33,34 @@ struct SampleParams {
   const float* off_in;
   float* off_out;
   void* cols;
+  const bf16_t* xh;  // direct path: x channel-minor [N][H*W+1][Cin], pixel H*W = 0
+  int nv_log;        // direct path: log2(Cg / 8)
+  int stage_d;       // direct path: footprint-staging loads per wave per chunk
+  FastDiv div_fw;
+};
+
+// Phase-A work split.  The offset convolution's depth (taps x input
+// channels) is cut into units of one tap x one chunk of CA channels, unit
+// u = chunk * K2 + tap, and wave w takes units w, w + 4, w + 8, ...  Inside a
+// unit the depth goes in k-steps of one MFMA; at step s lane half h holds the
+// VEC channels chunk * CA + h * CA / 2 + s * VEC (the A and B operands use the
+// same assignment), so over a unit each lane reads one contiguous run of CA/2
+// channels of its pixel or offset channel: whole cache lines per wave.  Steps
+// go in batches of up to four.  Both sampling kernels use this walk, so they
+// accumulate identical products in identical order (bit-identical offsets).
+struct UnitWalk {
+  int c, t, kb;  // chunk, tap, first k-step of the batch
+  __device__ __forceinline__ void start(int wave, int K2) {
+    c = 0; t = wave; kb = 0;
+    while (t >= K2) { t -= K2; ++c; }
+  }
+  __device__ __forceinline__ void next(int K2, int nks) {
+    kb += 4;
+    if (kb >= nks) {
+      kb = 0; t += 4;
+      while (t >= K2) { t -= K2; ++c; }
+    }
+  }
 };
 
 template <typename T, bool FUSED, int MB>
@@ -87,9 +115,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-    const int nkc = p.CA / (2 * VEC);
-    const int npairs = p.K2 * nkc;
-    const int myp = (npairs - wave + 3) >> 2;  // this wave's (tap, k-chunk) pairs: wave, wave+4, ...
+    const int nks = p.CA / (2 * VEC), nch = p.Cin / p.CA;
+    const int hoff = (lane >> 5) * (p.CA / 2);
     const bool nb1 = PT > 32;
     const T* __restrict__ wp = (const T*)p.woff_p;
     int pixb[2];
@@ -105,60 +132,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const bool pipeA = pairs_ok && ga.total <= 256 * kItemsA;
     PairStage<kItemsA> sa;
     if (pipeA) pair_load(sa, ga, ximg, 0);
-    // Weight fragments of this wave, a batch of kWB pairs at a time; the
-    // first batch of the next chunk is loaded while this chunk computes.
-    constexpr int kWB = 9 / MB;
-    uint4 wa[kWB][MB], wn[kWB][MB];
-    auto load_w = [&](uint4 (&dst)[kWB][MB], int c0, int j0) {
+    // Weight fragments of one batch of k-steps; the next batch's are loaded
+    // while this one computes.
+    uint4 wa[4][MB], wn[4][MB];
+    auto load_w = [&](uint4 (&dst)[4][MB], const UnitWalk& u) {
 #pragma unroll
-      for (int jj = 0; jj < kWB; ++jj) {
-        const int j = j0 + jj;
-        if (j < myp) {
-          const int pi = wave + 4 * j;
-          const int t = pi / nkc, kc = pi - t * nkc;
-          const int cl = kc * 2 * VEC + (lane >> 5) * VEC;
+      for (int k = 0; k < 4; ++k) {
+        if (u.kb + k < nks) {
+          const int cl = u.c * p.CA + hoff + (u.kb + k) * VEC;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const int o = obase + mb * 32 + (lane & 31);
-            dst[jj][mb] = *(const uint4*)(wp + ((size_t)o * p.K2 + t) * p.Cin + c0 + cl);
+            dst[k][mb] = *(const uint4*)(wp + ((size_t)o * p.K2 + u.t) * p.Cin + cl);
           }
         }
       }
     };
-    load_w(wa, 0, 0);
-    for (int c0 = 0; c0 < p.Cin; c0 += p.CA) {
+    UnitWalk uw;
+    uw.start(wave, p.K2);
+    if (uw.c < nch) load_w(wa, uw);
+    for (int c = 0; c < nch; ++c) {
+      const int c0 = c * p.CA;
       __syncthreads();
       if (pipeA) pair_store(sa, ga, (bf16_t*)xr);
       else stage_region<T>(xr, x, p.Cin, p.H, p.W, n, c0, p.CA, fy0, fx0, p.FH, p.FW, p.div_fh, sga, p.pstr_a);
       __syncthreads();
-      const bool more = c0 + p.CA < p.Cin;
-      if (pipeA && more) pair_load(sa, ga, ximg, c0 + p.CA);
-      if (more) load_w(wn, c0 + p.CA, 0);
-      for (int j0 = 0; j0 < myp; j0 += kWB) {
-        if (j0 > 0) load_w(wa, c0, j0);
+      if (pipeA && c + 1 < nch) pair_load(sa, ga, ximg, c0 + p.CA);
+      while (uw.c == c) {
+        UnitWalk un = uw;
+        un.next(p.K2, nks);
+        if (un.c < nch) load_w(wn, un);
+        const int ti = uw.t / p.KW, tj = uw.t - ti * p.KW;
+        const int toff = ti * p.DH * p.FW + tj * p.DW;
 #pragma unroll
-        for (int jj = 0; jj < kWB; ++jj) {
-          const int j = j0 + jj;
-          if (j >= myp) break;
-          const int pi = wave + 4 * j;
-          const int t = pi / nkc, kc = pi - t * nkc;
-          const int ti = t / p.KW, tj = t - ti * p.KW;
-          const int cl = kc * 2 * VEC + (lane >> 5) * VEC;
-          const int toff = ti * p.DH * p.FW + tj * p.DW;
+        for (int k = 0; k < 4; ++k) {
+          if (uw.kb + k >= nks) break;
+          const int cl = hoff + (uw.kb + k) * VEC;
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
             if (nb == 1 && !nb1) break;
             const uint4 bq = *(const uint4*)(xr + (size_t)(pixb[nb] + toff) * p.pstr_a + cl);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][nb], wa[jj][mb], bq, T());
+            for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][nb], wa[k][mb], bq, T());
           }
         }
-      }
-      if (more) {
 #pragma unroll
-        for (int jj = 0; jj < kWB; ++jj)
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) wa[jj][mb] = wn[jj][mb];
+          for (int mb = 0; mb < MB; ++mb) wa[k][mb] = wn[k][mb];
+        uw = un;
       }
     }
     __syncthreads();
@@ -331,6 +353,281 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // ---------------------------------------------------------------------------
+// Direct-gather variant (bf16): the corners are read straight from a
+// channel-minor copy of the input (one 16-byte load = 8 channels of one
+// corner), which stays resident in the L2s and the 256 MB Infinity Cache; no
+// input staging, no halo, no chunk loop and no barriers in the blend.  The
+// offset conv reads its MFMA operand fragments from the same copy.  Out-of-
+// image corners read the copy's extra zero pixel, so fully outside taps blend
+// to zero without a special case.
+template <int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_direct(const SampleParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
+  const int tile = lw / p.gsplit, gs = lw - tile * p.gsplit;
+  const int tpi = p.tiles_h * p.tiles_w;
+  const int n = tile / tpi, trem = tile - n * tpi;
+  const int tyi = trem / p.tiles_w, txi = trem - tyi * p.tiles_w;
+  const int oh0 = tyi * p.TH, ow0 = txi * p.TW;
+  const int thn = min(p.TH, p.Ho - oh0), twn = min(p.TW, p.Wo - ow0);
+  const int PT = p.TH * p.TW;
+  const int g = gs;  // one offset group per workgroup
+  const int ocw = 2 * p.K2;
+  const int obase = 2 * g * p.K2;
+  const int HW = p.H * p.W;
+  float* off_l = (float*)(smem + p.lds_off);                                  // [ocw][PT]
+  int4* tab = (int4*)(smem + p.lds_info);                                     // [PT][K2]
+  float4* wts = (float4*)(smem + p.lds_info + PT * p.K2 * 16);                // [PT][K2]
+  const bf16_t* __restrict__ xn = p.xh + (size_t)n * (HW + 1) * p.Cin;
+  const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
+
+  // ---- phase A: offsets of this tile, operand fragments from the copy ----
+  {
+    f32x16_t acc[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+    // Same unit walk as the LDS-staged kernel (bit-identical offsets); a
+    // unit here is one batch (CA <= 64 channels: at most four k-steps).  The
+    // tile's footprint, one chunk of CA channels at a time, is copied from
+    // the channel-minor input into LDS by direct buffer-to-LDS loads (whole
+    // 16-byte pieces of contiguous pixel rows), double buffered; 16-byte
+    // piece q of footprint pixel P sits in slot P * nq + (q ^ (P % nq)), so
+    // the 32 pixels of an operand read hit distinct banks.  The weights come
+    // in fragment order: one 1 KB contiguous load per k-step.
+    const int nks = p.CA / 16, nch = p.Cin / p.CA, nq = p.CA / 8;
+    const int nslot = p.FH * p.FW * nq;
+    const int D = p.stage_d;
+    unsigned char* stg = smem + p.lds_region;  // [2][D * 256 slots][16 B]
+    const rsrc_t xr = make_rsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * 2));
+    const bool nb1 = PT > 32;
+    const bf16_t* __restrict__ wf = (const bf16_t*)p.woff_p + (size_t)g * p.K2 * p.Cin * 32 + lane * 8;
+    int pixb[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      int pix = nb * 32 + (lane & 31);
+      if (pix >= PT) pix = 0;
+      const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
+      pixb[nb] = ty * p.SH * p.FW + tx * p.SW;  // footprint pixel of tap (0,0)
+    }
+    auto issue = [&](int c, int buf) {
+      unsigned char* b = stg + buf * (D * 4096);
+      for (int i = 0; i < D; ++i) {
+        const int s0 = (i * 4 + wave) * 64, sl = s0 + lane;
+        int voff = kOOB;
+        if (sl < nslot) {
+          const int P = sl / nq, q = (sl - P * nq) ^ (P & (nq - 1));
+          const int fy = fdiv(P, p.div_fw), fx = P - fy * p.FW;
+          const int y = fy0 + fy, xx = fx0 + fx;
+          const int pix = ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) ? y * p.W + xx : HW;
+          voff = (pix * p.Cin + c * p.CA + q * 8) * 2;
+        }
+        load_lds16(xr, b + s0 * 16, voff);
+      }
+    };
+    UnitWalk uw;
+    uw.start(wave, p.K2);
+    issue(0, 0);
+    for (int c = 0; c < nch; ++c) {
+      wait_vm<0>();     // this wave's pieces of chunk c have landed
+      __syncthreads();  // everyone's have; everyone is done with chunk c - 1
+      // weights of this wave's units in chunk c (at most three: K2 <= 9)
+      uint4 wa[3][4];
+      int tl[3], nu = 0;
+      {
+        UnitWalk w = uw;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          if (w.c == c) {
+            tl[u] = w.t; nu = u + 1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(w.t * nch + c) * nks + k) * 512);
+            w.next(p.K2, nks);
+          }
+        }
+        uw = w;
+      }
+      if (c + 1 < nch) {
+        issue(c + 1, (c + 1) & 1);
+        switch (D) {  // weights landed, next chunk's pieces still in flight
+          case 1: wait_vm<1>(); break;
+          case 2: wait_vm<2>(); break;
+          case 3: wait_vm<3>(); break;
+          case 4: wait_vm<4>(); break;
+          case 5: wait_vm<5>(); break;
+          case 6: wait_vm<6>(); break;
+          case 7: wait_vm<7>(); break;
+          default: wait_vm<0>(); break;
+        }
+      } else {
+        wait_vm<0>();
+      }
+      const unsigned char* b = stg + (c & 1) * (D * 4096);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        if (u >= nu) break;
+        const int ti = tl[u] / p.KW, tj = tl[u] - ti * p.KW;
+        const int toff = ti * p.DH * p.FW + tj * p.DW;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (k >= nks) break;
+          const int q = (lane >> 5) * (nq >> 1) + k;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (nb == 1 && !nb1) break;
+            const int P = pixb[nb] + toff;
+            const uint4 bq = *(const uint4*)(b + (P * nq + (q ^ (P & (nq - 1)))) * 16);
+            mfma_chunk(acc[0][nb], wa[u][k], bq, bf16_t());
+          }
+        }
+      }
+    }
+    __syncthreads();  // the partial sums below reuse the staging buffers
+    float* part = (float*)(smem + p.lds_region);  // [4][ocw][PT]
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mb * 32 + acc_row(lane, r), col = nb * 32 + (lane & 31);
+          if (row < ocw && col < PT) part[(wave * ocw + row) * PT + col] = acc[mb][nb][r];
+        }
+    __syncthreads();
+    const int tot = ocw * PT;
+    for (int e = tid; e < tot; e += 256) {
+      const int o = e / PT, pix = e - o * PT;
+      float v = part[e] + part[tot + e];
+      v += part[2 * tot + e];
+      v += part[3 * tot + e];
+      if (p.b_off) v += bf16_to_f32(((const bf16_t*)p.b_off)[obase + o]);
+      off_l[e] = v;
+      const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
+      if (p.off_out && ty < thn && tx < twn)
+        p.off_out[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx] = v;
+    }
+    __syncthreads();
+  }
+
+  // ---- tap index stage: corner pixel, corner mask, column offset, weights ----
+  const int nent = PT * p.K2;
+  for (int e = tid; e < nent; e += 256) {
+    const int pix = fdiv(e, p.div_k2), t = e - pix * p.K2;
+    const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
+    int4 tb = make_int4(0, 0, -1, 0);
+    float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ty < thn && tx < twn) {
+      const int ti = t / p.KW, tj = t - ti * p.KW;
+      const int by = (oh0 + ty) * p.SH - p.PH + ti * p.DH;
+      const int bx = (ow0 + tx) * p.SW - p.PW + tj * p.DW;
+      const float dy = off_l[(2 * t) * PT + pix];
+      const float dx = off_l[(2 * t + 1) * PT + pix];
+      const TapIndex ix = tap_index(by, bx, dy, dx, p.H, p.W);
+      tb.z = (ty * p.Wo + tx) * p.Ck + t * p.Cin;
+      if (!ix.outside) {
+        tb.x = ix.y0 * p.W + ix.x0;
+        tb.y = (int)corner_mask(ix, p.H, p.W);
+        float w[4];
+        tap_weights(ix, w);
+        wv = make_float4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    tab[e] = tb;
+    wts[e] = wv;
+  }
+  __syncthreads();
+
+  // ---- phase B: every (pixel, tap) x 8 channels, corners from the copy ----
+  const int nvm = (1 << p.nv_log) - 1;
+  const int v = tid & nvm, e0 = tid >> p.nv_log, estep = 256 >> p.nv_log;
+  const int cofs = g * p.Cg + v * 8;
+  const bf16_t* __restrict__ xc = xn + cofs;
+  bf16_t* __restrict__ colt = (bf16_t*)p.cols + ((size_t)n * p.Ho * p.Wo + (size_t)oh0 * p.Wo + ow0) * p.Ck + cofs;
+  const int cw1 = p.Cin, cwW = p.W * p.Cin, zero = HW * p.Cin;
+  for (int e = e0; e < nent; e += 2 * estep) {
+    int4 tb[2];
+    float w[2][4];
+    uint4 q[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int eu = e + u * estep;
+      tb[u] = eu < nent ? tab[eu] : make_int4(0, 0, -1, 0);
+      const float4 wq = wts[eu < nent ? eu : e];
+      w[u][0] = wq.x; w[u][1] = wq.y; w[u][2] = wq.z; w[u][3] = wq.w;
+      const int b = tb[u].x * p.Cin, m = tb[u].y;
+      const int a0 = (m & 1) ? b : zero, a1 = (m & 2) ? b + cw1 : zero;
+      const int a2 = (m & 4) ? b + cwW : zero, a3 = (m & 8) ? b + cwW + cw1 : zero;
+      q[u][0] = *(const uint4*)(xc + a0);
+      q[u][1] = *(const uint4*)(xc + a1);
+      q[u][2] = *(const uint4*)(xc + a2);
+      q[u][3] = *(const uint4*)(xc + a3);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (tb[u].z < 0) continue;
+      float f00[8], f01[8], f10[8], f11[8], o8[8];
+      unpack8(q[u][0], f00);
+      unpack8(q[u][1], f01);
+      unpack8(q[u][2], f10);
+      unpack8(q[u][3], f11);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o8[c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
+      store8(colt + tb[u].z, o8);
+    }
+  }
+}
+
+// x [N][Cin][H*W] -> xh [N][H*W+1][Cin] (bf16), pixel H*W of every image zero.
+// Each lane moves an 8 x 8 block (8 channels x 8 pixels): eight 16-byte loads
+// along the pixels, a register transpose with byte permutes, eight 16-byte
+// stores along the channels.  A wave covers 64 pixels x 64 channels, so both
+// the loads and the stores come in whole 128-byte runs.
+__global__ __launch_bounds__(256) void k_x_channel_minor(const bf16_t* __restrict__ x, bf16_t* __restrict__ xh,
+                                                         int Cin, int HW, int pgroups, int cgroups, int total_waves) {
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= total_waves) return;
+  const int cgi = wv % cgroups, r = wv / cgroups;
+  const int pgi = r % pgroups, n = r / pgroups;
+  const int c = cgi * 64 + (lane & 7) * 8;
+  const int p0 = pgi * 64 + (lane >> 3) * 8;
+  if (c >= Cin || p0 > HW) return;
+  const bf16_t* src = x + ((size_t)n * Cin + c) * HW;
+  uint4 rv[8];
+  if ((HW & 7) == 0 && p0 + 8 <= HW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rv[k] = *(const uint4*)(src + (size_t)k * HW + p0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = p0 + i < HW ? (uint32_t)src[(size_t)k * HW + p0 + i] : 0u;
+      rv[k] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+    }
+  }
+  bf16_t* dst = xh + ((size_t)n * (HW + 1) + p0) * Cin + c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // pixel i sits in dword i/2 of every channel's word, low half for even i
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    auto dw = [&](const uint4& q) { return (i >> 1) == 0 ? q.x : (i >> 1) == 1 ? q.y : (i >> 1) == 2 ? q.z : q.w; };
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(dw(rv[1]), dw(rv[0]), sel);
+    o.y = __builtin_amdgcn_perm(dw(rv[3]), dw(rv[2]), sel);
+    o.z = __builtin_amdgcn_perm(dw(rv[5]), dw(rv[4]), sel);
+    o.w = __builtin_amdgcn_perm(dw(rv[7]), dw(rv[6]), sel);
+    if (p0 + i <= HW) *(uint4*)(dst + (size_t)i * Cin) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tap index / corner mask on its own (same tap_index as the fused kernel).
 struct IndexParams {
   int N, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, G, K2, Oc;
@@ -398,11 +695,19 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
 // Weight preparation: main weight [Cout][Cin][K] -> [Cout][K][Cin] (the
 // column order) and offset-conv weight [Oc][Cin][K] -> [oc_pad][K][Cin],
 // rows >= Oc zero.
+// Weights of the main conv -> Wt [Cout][taps][Cin]; offset-conv weights ->
+// rows [OcP][taps][Cin] (LDS-staged sampling kernel), or with CA > 0 the
+// direct kernel's fragment order: per group, tap, chunk of CA channels and
+// k-step, the 64 lanes' 16-byte A operands back to back (lane L: offset
+// channel L % 32 of the group, zero past 2 * taps; channels
+// chunk * CA + (L / 32) * CA / 2 + step * 8 ... + 7).
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, const T* __restrict__ w_off,
                                                       T* wt, T* woff_p, int Cout, int Cin, int K2, int Oc,
-                                                      int OcP) {
-  const size_t n1 = (size_t)Cout * K2 * Cin, n2 = (size_t)OcP * K2 * Cin;
+                                                      int OcP, int G, int CA) {
+  const size_t n1 = (size_t)Cout * K2 * Cin;
+  const size_t n2 = CA > 0 ? (size_t)G * K2 * Cin * 32 : (size_t)OcP * K2 * Cin;
+  const int nks = CA / 16, nch = CA > 0 ? Cin / CA : 1;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * 256) {
     if (e < n1) {
       const int c = (int)(e % Cin);
@@ -410,6 +715,17 @@ __global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, c
       const int t = (int)(r % K2);
       const int co = (int)(r / K2);
       wt[e] = w[((size_t)co * Cin + c) * K2 + t];
+    } else if (CA > 0) {
+      const size_t f = e - n1;
+      const int e8 = (int)(f & 7), L = (int)((f >> 3) & 63);
+      size_t r = f >> 9;
+      const int k = (int)(r % nks); r /= nks;
+      const int ch = (int)(r % nch); r /= nch;
+      const int t = (int)(r % K2);
+      const int g = (int)(r / K2);
+      const int ol = L & 31;
+      const int c = ch * CA + (L >> 5) * (CA / 2) + k * 8 + e8;
+      woff_p[f] = ol < 2 * K2 ? w_off[((size_t)(2 * g * K2 + ol) * Cin + c) * K2 + t] : zero_elem<T>();
     } else {
       const size_t f = e - n1;
       const int c = (int)(f % Cin);
@@ -439,6 +755,10 @@ static SampleParams make_params(const deft_plan& p, const SampleArgs& a) {
   s.div_tw = make_fastdiv(p.tile_w);
   s.div_k2 = make_fastdiv(p.taps);
   s.div_fh = make_fastdiv(p.foot_h);
+  s.div_fw = make_fastdiv(p.foot_w);
+  s.stage_d = p.stage_d;
+  s.xh = nullptr;
+  s.nv_log = 0;
   s.x = a.x; s.woff_p = a.woff_p; s.b_off = a.b_off; s.off_in = a.off_in; s.off_out = a.off_out;
   s.cols = a.cols;
   return s;
@@ -464,9 +784,34 @@ static hipError_t launch_sample_dt(const deft_plan& p, bool fused, const SampleP
   }
 }
 
+template <int MB>
+static hipError_t launch_direct_t(const deft_plan& p, const SampleParams& s, hipStream_t st) {
+  auto kern = k_sample_direct<MB>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
+  if (e != hipSuccess) return e;
+  DEFT_LAUNCH("fused_offset_sample", kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hipStream_t st) {
-  const SampleParams s = make_params(p, a);
+  SampleParams s = make_params(p, a);
   if (p.num_wg == 0) return hipSuccess;
+  if (p.direct && fused) {
+    // channel-minor copy of x with a zero pixel per image, then the gather
+    const int HW = p.d.h * p.d.w;
+    const int pgroups = (HW + 1 + 63) / 64, cgroups = (p.d.c_in + 63) / 64;
+    const int waves = p.d.n * pgroups * cgroups;
+    DEFT_LAUNCH("x_channel_minor", k_x_channel_minor, dim3((waves + 3) / 4), dim3(256), 0, st,
+                (const bf16_t*)a.x, (bf16_t*)a.xh, p.d.c_in, HW, pgroups, cgroups, waves);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    s.xh = (const bf16_t*)a.xh;
+    int l = 0;
+    while ((1 << l) < p.cg / 8) ++l;
+    s.nv_log = l;
+    if (p.mblocks != 1) return hipErrorInvalidValue;
+    return launch_direct_t<1>(p, s, st);
+  }
   return p.d.dtype == DEFT_BF16 ? launch_sample_dt<bf16_t>(p, fused, s, st)
                                 : launch_sample_dt<float>(p, fused, s, st);
 }
@@ -510,17 +855,19 @@ hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off
 hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt,
                                void* woff_p, hipStream_t st) {
   const deft_desc& d = p.d;
-  const size_t total = (size_t)(d.c_out + p.oc_pad) * p.taps * d.c_in;
+  const int ca = p.direct ? p.chunk_a : 0;
+  const size_t total = (size_t)d.c_out * p.taps * d.c_in +
+                       (ca ? (size_t)d.offset_groups * p.taps * d.c_in * 32 : (size_t)p.oc_pad * p.taps * d.c_in);
   unsigned g = grid_for(total);
   if (g > 4096) g = 4096;
   if (d.dtype == DEFT_BF16)
     DEFT_LAUNCH("prep_forward", k_prep_forward<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)w,
                        (const bf16_t*)w_off, (bf16_t*)wt, (bf16_t*)woff_p, d.c_out, d.c_in, p.taps, p.oc,
-                       p.oc_pad);
+                       p.oc_pad, d.offset_groups, ca);
   else
     DEFT_LAUNCH("prep_forward", k_prep_forward<float>, dim3(g), dim3(256), 0, st, (const float*)w,
                        (const float*)w_off, (float*)wt, (float*)woff_p, d.c_out, d.c_in, p.taps, p.oc,
-                       p.oc_pad);
+                       p.oc_pad, d.offset_groups, ca);
   return hipGetLastError();
 }
 
