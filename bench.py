@@ -20,6 +20,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA
 
 
+FORWARD_KERNELS = ("prep_forward", "x_channel_minor", "fused_offset_sample", "gemm_forward")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -36,6 +39,7 @@ def kernel_work(wl):
     gemm_flop = 2.0 * wl.c_out * ck * P
     off_flop = 2.0 * wl.oc * ck * P
     return {
+        "x_channel_minor": (2 * x * esz, 0.0),
         "fused_offset_sample": (x * esz + cols + wl.oc * ck * esz + (offs if wl.train else 0), off_flop),
         "gemm_forward": (cols + wl.c_out * ck * esz + P * wl.c_out * esz, gemm_flop),
         "gemm_dcol": (P * wl.c_out * esz + wl.c_out * ck * esz + cols, gemm_flop),
@@ -155,10 +159,9 @@ def main():
         kernels[name] = rec
     for name, rec in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"]):
         log("  %-24s %s" % (name, rec))
-    fwd_ms = sum(kernels[k]["ms_per_step"] for k in ("prep_forward", "fused_offset_sample", "gemm_forward")
-                 if k in kernels)
+    fwd_ms = sum(kernels[k]["ms_per_step"] for k in FORWARD_KERNELS if k in kernels)
     bwd_ms = sum(r["ms_per_step"] for k, r in kernels.items()
-                 if k not in ("prep_forward", "fused_offset_sample", "gemm_forward"))
+                 if k not in FORWARD_KERNELS)
 
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
     b, f = work[dom]
@@ -210,8 +213,8 @@ def main():
         "config": {"workload": wl.name, "n": wl.n, "c_in": wl.c_in, "c_out": wl.c_out, "h": wl.h, "w": wl.w,
                    "kernel": [wl.kh, wl.kw], "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil,
                    "offset_groups": wl.groups, "offset_std_px": wl.offset_std,
-                   "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk", "bwd_tile_h", "bwd_tile_w",
-                                                 "bwd_chunk")}},
+                   "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h",
+                                                 "bwd_tile_w", "bwd_chunk")}},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),

@@ -282,7 +282,37 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
       }
     }
   }
-  return found ? DEFT_OK : DEFT_ERR_UNSUPPORTED;
+  if (!found) return DEFT_ERR_UNSUPPORTED;
+  // Direct gather where supported: the halo chosen above still bounds the
+  // backward's candidate window; the tile only sets the forward's launch
+  // shape (every workgroup pays a fixed cost for its offset weights and
+  // staging round trips, about as much as writing 64 KB of columns).
+  if (direct_ok(d)) {
+    static const int dtiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}};
+    double dbest = 1e300;
+    deft_plan bd;
+    bool dfound = false;
+    for (auto& t : dtiles) {
+      deft_plan p;
+      p.d = d;
+      if (!layout_plan(p, t[0], t[1], best.halo, s.cg, true) || p.chunk_b == 0) continue;
+      const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
+      const double slots = (double)kNumCUs * occ;
+      const double waves = std::ceil(p.num_wg / slots);
+      const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
+      const double cost = (col_bytes + (double)p.num_wg * 65536.0) / std::max(busy, 0.05);
+      if (cost < dbest * 0.999) {
+        dbest = cost;
+        bd = p;
+        dfound = true;
+      }
+    }
+    if (dfound) {
+      bd.est_miss = best.est_miss;
+      best = bd;
+    }
+  }
+  return DEFT_OK;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

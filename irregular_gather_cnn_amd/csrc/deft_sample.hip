@@ -430,63 +430,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         load_lds16(xr, b + s0 * 16, voff);
       }
     };
+    // Weights of this wave's units of one chunk (at most three: K2 <= 9);
+    // unit u of chunk c + 1 is loaded into wa[u] as soon as unit u of chunk
+    // c has been multiplied, so its latency hides behind the rest.
+    uint4 wa[3][4];
+    int tl[3], nu = 0;
     UnitWalk uw;
     uw.start(wave, p.K2);
-    issue(0, 0);
-    for (int c = 0; c < nch; ++c) {
-      wait_vm<0>();     // this wave's pieces of chunk c have landed
-      __syncthreads();  // everyone's have; everyone is done with chunk c - 1
-      // weights of this wave's units in chunk c (at most three: K2 <= 9)
-      uint4 wa[3][4];
-      int tl[3], nu = 0;
-      {
-        UnitWalk w = uw;
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          if (w.c == c) {
-            tl[u] = w.t; nu = u + 1;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(w.t * nch + c) * nks + k) * 512);
-            w.next(p.K2, nks);
-          }
-        }
-        uw = w;
-      }
-      if (c + 1 < nch) {
-        issue(c + 1, (c + 1) & 1);
-        switch (D) {  // weights landed, next chunk's pieces still in flight
-          case 1: wait_vm<1>(); break;
-          case 2: wait_vm<2>(); break;
-          case 3: wait_vm<3>(); break;
-          case 4: wait_vm<4>(); break;
-          case 5: wait_vm<5>(); break;
-          case 6: wait_vm<6>(); break;
-          case 7: wait_vm<7>(); break;
-          default: wait_vm<0>(); break;
-        }
-      } else {
-        wait_vm<0>();
-      }
-      const unsigned char* b = stg + (c & 1) * (D * 4096);
+    auto fetch = [&](int c) {  // walks uw over chunk c's units, loading their weights
+      nu = 0;
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        if (u >= nu) break;
-        const int ti = tl[u] / p.KW, tj = tl[u] - ti * p.KW;
-        const int toff = ti * p.DH * p.FW + tj * p.DW;
+        if (uw.c == c) {
+          tl[u] = uw.t; nu = u + 1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (k >= nks) break;
-          const int q = (lane >> 5) * (nq >> 1) + k;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            if (nb == 1 && !nb1) break;
-            const int P = pixb[nb] + toff;
-            const uint4 bq = *(const uint4*)(b + (P * nq + (q ^ (P & (nq - 1)))) * 16);
-            mfma_chunk(acc[0][nb], wa[u][k], bq, bf16_t());
-          }
+          for (int k = 0; k < 4; ++k)
+            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(uw.t * nch + c) * nks + k) * 512);
+          uw.next(p.K2, nks);
         }
       }
+    };
+    issue(0, 0);
+    fetch(0);
+    for (int c = 0; c < nch; ++c) {
+      wait_vm<0>();     // this wave's pieces of chunk c and its weights have landed
+      __syncthreads();  // everyone's have; everyone is done with chunk c - 1
+      if (c + 1 < nch) issue(c + 1, (c + 1) & 1);
+      const unsigned char* b = stg + (c & 1) * (D * 4096);
+      const int nuc = nu;
+      int tlc[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) tlc[u] = tl[u];
+      // next chunk's units (same count pattern; loaded per unit below)
+      UnitWalk un = uw;
+      int tn[3], nn = 0;
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (un.c == c + 1) { tn[u] = un.t; nn = u + 1; un.next(p.K2, nks); }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        if (u < nuc) {
+          const int ti = tlc[u] / p.KW, tj = tlc[u] - ti * p.KW;
+          const int toff = ti * p.DH * p.FW + tj * p.DW;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (k >= nks) break;
+            const int q = (lane >> 5) * (nq >> 1) + k;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              if (nb == 1 && !nb1) break;
+              const int P = pixb[nb] + toff;
+              const uint4 bq = *(const uint4*)(b + (P * nq + (q ^ (P & (nq - 1)))) * 16);
+              mfma_chunk(acc[0][nb], wa[u][k], bq, bf16_t());
+            }
+          }
+        }
+        if (u < nn) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(tn[u] * nch + c + 1) * nks + k) * 512);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) tl[u] = tn[u];
+      nu = nn;
+      uw = un;
     }
     __syncthreads();  // the partial sums below reuse the staging buffers
     float* part = (float*)(smem + p.lds_region);  // [4][ocw][PT]

@@ -31,7 +31,8 @@ _CSRC = os.path.join(_HERE, "csrc")
 
 # benchmark name of a launch -> (pattern of the kernel symbol, source files of the kernel)
 KERNELS = {
-    "fused_offset_sample": (r"k_sample<[^>]*, true", ["deft_sample.hip", "deft_device.h"]),
+    "x_channel_minor": (r"k_x_channel_minor", ["deft_sample.hip"]),
+    "fused_offset_sample": (r"k_sample<[^>]*, true|k_sample_direct<", ["deft_sample.hip", "deft_device.h"]),
     "gemm_forward": (r"k_gemm_dl<.*DlFwd|k_gemm<.*FwdOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dw": (r"k_gemm_dl<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
