@@ -60,6 +60,15 @@ __device__ __forceinline__ int cvt_rpi(float x) {
   return r;
 }
 __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }
+// acc + sum over the eight bf16 pairs of a and b (products exact in fp32)
+__device__ __forceinline__ float dot2_bf16(const uint4 a, const uint4 b, float acc) {
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.x), __builtin_bit_cast(b2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.y), __builtin_bit_cast(b2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.z), __builtin_bit_cast(b2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.w), __builtin_bit_cast(b2_t, b.w), acc, false);
+  return acc;
+}
 
 // The (output pixel, tap) pairs whose corners touch one core tile of input
 // pixels (for one offset group), written to that core's list; shared by the
@@ -337,18 +346,36 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
           const T* b2 = b0 + XW * p.xstr;
           const T* b3 = b2 + p.xstr;
           const int hc = p.CC >> 1;
-          for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
-            float gv[8], v00[8], v01[8], v10[8], v11[8];
-            lds_read8(drow + cc, gv);
-            lds_read8(b0 + cc, v00);
-            lds_read8(b1 + cc, v01);
-            lds_read8(b2 + cc, v10);
-            lds_read8(b3 + cc, v11);
+          if constexpr (kWide) {
+            for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
+              float gv[8], v00[8], v01[8], v10[8], v11[8];
+              lds_read8(drow + cc, gv);
+              lds_read8(b0 + cc, v00);
+              lds_read8(b1 + cc, v01);
+              lds_read8(b2 + cc, v10);
+              lds_read8(b3 + cc, v11);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              gy = __builtin_fmaf(gv[k], hx * (v10[k] - v00[k]) + lx * (v11[k] - v01[k]), gy);
-              gx = __builtin_fmaf(gv[k], hy * (v01[k] - v00[k]) + ly * (v11[k] - v10[k]), gx);
+              for (int k = 0; k < 8; ++k) {
+                gy = __builtin_fmaf(gv[k], hx * (v10[k] - v00[k]) + lx * (v11[k] - v01[k]), gy);
+                gx = __builtin_fmaf(gv[k], hy * (v01[k] - v00[k]) + ly * (v11[k] - v10[k]), gx);
+              }
             }
+          } else {
+            // bf16: the four corner dot products D_q = sum_c dCol_c x_q,c on
+            // the packed two-channel dot instruction (products exact in fp32),
+            // then gy = hx (D10 - D00) + lx (D11 - D01), gx likewise
+            float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
+            for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
+              const uint4 gq = *(const uint4*)(drow + cc);
+              const uint4 q00 = *(const uint4*)(b0 + cc), q01 = *(const uint4*)(b1 + cc);
+              const uint4 q10 = *(const uint4*)(b2 + cc), q11 = *(const uint4*)(b3 + cc);
+              d00 = dot2_bf16(gq, q00, d00);
+              d01 = dot2_bf16(gq, q01, d01);
+              d10 = dot2_bf16(gq, q10, d10);
+              d11 = dot2_bf16(gq, q11, d11);
+            }
+            gy = hx * (d10 - d00) + lx * (d11 - d01);
+            gx = hy * (d01 - d00) + ly * (d11 - d10);
           }
         }
         gy += __shfl_xor(gy, 32);
