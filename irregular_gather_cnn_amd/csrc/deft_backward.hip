@@ -70,6 +70,70 @@ __device__ __forceinline__ float dot2_bf16(const uint4 a, const uint4 b, float a
   return acc;
 }
 
+// dOffset of a block's owned entries (each (pixel, tap) pair has exactly one
+// owner core): lanes = entries (lane & 31), the two lane halves take the two
+// halves of the chunk's channels; dst holds the entries' dCol rows, xl the
+// staged input region around the core.
+template <typename T>
+__device__ __forceinline__ void doffset_owned(const int4 cur, int nb, int lane, const T* dst, int dcstr, const T* xl,
+                                              int xstr, int XW, int CC, int HoWo, float* doffp) {
+  constexpr bool kWide = sizeof(T) == 4;
+  const int r = lane & 31, half = lane >> 5;
+  const int ex = __shfl(cur.x, r), ey = __shfl(cur.y, r), ez = __shfl(cur.z, r), ew = __shfl(cur.w, r);
+  const uint32_t info = (uint32_t)ey;
+  const bool own = r < nb && ((info >> 8) & 1u);
+  float gy = 0.f, gx = 0.f;
+  if (own) {
+    const int cy = (info >> 16) & 255, cx = info >> 24;
+    const float ly = __int_as_float(ez), lx = __int_as_float(ew);
+    const float hy = 1.0f - ly, hx = 1.0f - lx;
+    const T* drow = dst + r * dcstr;
+    const T* b0 = xl + (cy * XW + cx) * xstr;
+    const T* b1 = b0 + xstr;
+    const T* b2 = b0 + XW * xstr;
+    const T* b3 = b2 + xstr;
+    const int hc = CC >> 1;
+    if constexpr (kWide) {
+      for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
+        float gv[8], v00[8], v01[8], v10[8], v11[8];
+        lds_read8(drow + cc, gv);
+        lds_read8(b0 + cc, v00);
+        lds_read8(b1 + cc, v01);
+        lds_read8(b2 + cc, v10);
+        lds_read8(b3 + cc, v11);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          gy = __builtin_fmaf(gv[k], hx * (v10[k] - v00[k]) + lx * (v11[k] - v01[k]), gy);
+          gx = __builtin_fmaf(gv[k], hy * (v01[k] - v00[k]) + ly * (v11[k] - v10[k]), gx);
+        }
+      }
+    } else {
+      // bf16: the four corner dot products D_q = sum_c dCol_c x_q,c on
+      // the packed two-channel dot instruction (products exact in fp32),
+      // then gy = hx (D10 - D00) + lx (D11 - D01), gx likewise
+      float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
+      for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
+        const uint4 gq = *(const uint4*)(drow + cc);
+        const uint4 q00 = *(const uint4*)(b0 + cc), q01 = *(const uint4*)(b1 + cc);
+        const uint4 q10 = *(const uint4*)(b2 + cc), q11 = *(const uint4*)(b3 + cc);
+        d00 = dot2_bf16(gq, q00, d00);
+        d01 = dot2_bf16(gq, q01, d01);
+        d10 = dot2_bf16(gq, q10, d10);
+        d11 = dot2_bf16(gq, q11, d11);
+      }
+      gy = hx * (d10 - d00) + lx * (d11 - d01);
+      gx = hy * (d01 - d00) + ly * (d11 - d10);
+    }
+  }
+  gy += __shfl_xor(gy, 32);
+  gx += __shfl_xor(gx, 32);
+  if (own && half == 0) {
+    const int t = info & 255;
+    doffp[(size_t)(2 * t) * HoWo + ex] = gy;
+    doffp[(size_t)(2 * t + 1) * HoWo + ex] = gx;
+  }
+}
+
 // The (output pixel, tap) pairs whose corners touch one core tile of input
 // pixels (for one offset group), written to that core's list; shared by the
 // core's channel-chunk workgroups of k_sample_bwd.
@@ -328,64 +392,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
           }
         }
       }
-      // dOffset of the block's owned entries: lanes = entries (lane & 31);
-      // the two lane halves take the two halves of the chunk's channels
-      {
-        const int r = lane & 31, half = lane >> 5;
-        const int ex = __shfl(cur.x, r), ey = __shfl(cur.y, r), ez = __shfl(cur.z, r), ew = __shfl(cur.w, r);
-        const uint32_t info = (uint32_t)ey;
-        const bool own = r < nb && ((info >> 8) & 1u);
-        float gy = 0.f, gx = 0.f;
-        if (own) {
-          const int cy = (info >> 16) & 255, cx = info >> 24;
-          const float ly = __int_as_float(ez), lx = __int_as_float(ew);
-          const float hy = 1.0f - ly, hx = 1.0f - lx;
-          const T* drow = dst + r * p.dcstr;
-          const T* b0 = xl + (cy * XW + cx) * p.xstr;
-          const T* b1 = b0 + p.xstr;
-          const T* b2 = b0 + XW * p.xstr;
-          const T* b3 = b2 + p.xstr;
-          const int hc = p.CC >> 1;
-          if constexpr (kWide) {
-            for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
-              float gv[8], v00[8], v01[8], v10[8], v11[8];
-              lds_read8(drow + cc, gv);
-              lds_read8(b0 + cc, v00);
-              lds_read8(b1 + cc, v01);
-              lds_read8(b2 + cc, v10);
-              lds_read8(b3 + cc, v11);
-#pragma unroll
-              for (int k = 0; k < 8; ++k) {
-                gy = __builtin_fmaf(gv[k], hx * (v10[k] - v00[k]) + lx * (v11[k] - v01[k]), gy);
-                gx = __builtin_fmaf(gv[k], hy * (v01[k] - v00[k]) + ly * (v11[k] - v10[k]), gx);
-              }
-            }
-          } else {
-            // bf16: the four corner dot products D_q = sum_c dCol_c x_q,c on
-            // the packed two-channel dot instruction (products exact in fp32),
-            // then gy = hx (D10 - D00) + lx (D11 - D01), gx likewise
-            float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
-            for (int cc = half * hc; cc < (half + 1) * hc; cc += 8) {
-              const uint4 gq = *(const uint4*)(drow + cc);
-              const uint4 q00 = *(const uint4*)(b0 + cc), q01 = *(const uint4*)(b1 + cc);
-              const uint4 q10 = *(const uint4*)(b2 + cc), q11 = *(const uint4*)(b3 + cc);
-              d00 = dot2_bf16(gq, q00, d00);
-              d01 = dot2_bf16(gq, q01, d01);
-              d10 = dot2_bf16(gq, q10, d10);
-              d11 = dot2_bf16(gq, q11, d11);
-            }
-            gy = hx * (d10 - d00) + lx * (d11 - d01);
-            gx = hy * (d01 - d00) + ly * (d11 - d10);
-          }
-        }
-        gy += __shfl_xor(gy, 32);
-        gx += __shfl_xor(gx, 32);
-        if (own && half == 0) {
-          const int t = info & 255;
-          doffp[(size_t)(2 * t) * HoWo + ex] = gy;
-          doffp[(size_t)(2 * t + 1) * HoWo + ex] = gx;
-        }
-      }
+      doffset_owned<T>(cur, nb, lane, dst, p.dcstr, xl, p.xstr, XW, p.CC, HoWo, doffp);
       __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
@@ -396,6 +403,186 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
       const double sv = kWide ? (double)(long long)a : (double)(int)(uint32_t)a;
       p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = (float)(sv * inv);
     }
+  }
+}
+
+// bf16 sampling backward with the scatter on the MFMA units.  Per block of 32
+// list entries a wave forms, 16 entries at a time, the sparse matrix of
+// bilinear weights A [core pixel][entry] in LDS (each entry puts its weights
+// on at most four pixels; the fp32 weight split as bf16 hi + lo, two MFMAs,
+// so the weights keep 16 significant bits) and multiplies it with the
+// entries' dCol rows B [entry][channel] (read as fragments with transposed
+// LDS reads): dX_core += A B in fp32 registers.  The four waves take every
+// fourth block; their partial sums are added in a fixed order at the end.
+// No atomics; dOffset as in the other variant.  Needs a core of at most 64
+// pixels and a chunk of 32 or 64 channels.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sample_bwd_mf(const BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
+  const int nchunks = p.Cg / p.CC;
+  const int tg = lw / nchunks, chunk = lw - tg * nchunks;
+  const int tile = tg / p.G, g = tg - tile * p.G;
+  const int tpi = p.bt_h * p.bt_w;
+  const int n = tile / tpi, trem = tile - n * tpi;
+  const int Y0 = (trem / p.bt_w) * p.CH, X0 = (trem % p.bt_w) * p.CW;
+  const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
+  const int obase = 2 * g * p.K2;
+  const int HoWo = p.Ho * p.Wo;
+  bf16_t* xl = (bf16_t*)smem;  // [(CH+2)*(CW+2)][xstr]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
+  const int4* list = p.lists + (size_t)tg * p.list_cap;
+  const bf16_t* __restrict__ x = (const bf16_t*)p.x;
+  const bf16_t* __restrict__ dcol = (const bf16_t*)p.dcol;
+  const int L = p.counts[tg];
+
+  constexpr int BLK = 32, VEC = 8, KQ = BLK / VEC;
+  const int XW = p.CW + 2;
+  const int PX = p.CH * p.CW;
+  const bool mb1 = PX > 32, nb1 = p.CC > 32;
+  const size_t HW = (size_t)p.H * p.W;
+  bf16_t* dst = (bf16_t*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;  // [BLK][dcstr]
+  unsigned char* at = smem + p.lds_dx + wave * 4096;  // A hi [64][16], then A lo [64][16] (32-byte rows)
+  const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
+  const int epi = 64 / lpe;    // rows per load instruction
+  const size_t pstride = (size_t)p.N * p.Oc * HoWo;
+  const FastDiv drh = make_fastdiv(p.CH + 2);
+  const StageGeom sg = stage_geom<bf16_t>(p.W, X0 - 1, XW, (size_t)p.Cin * HW);
+  const int c0 = chunk * p.CC;
+  const int cglob = g * p.Cg + c0;
+  float* doffp = p.doffp + (size_t)chunk * pstride + ((size_t)n * p.Oc + obase) * HoWo;
+  stage_region<bf16_t>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
+  __syncthreads();
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  int4 my = make_int4(0, 0, 0, 0);
+  uint4 q[KQ];
+  auto load_block = [&](int b0) {
+    const int nb = min(BLK, L - b0);
+    my = lane < nb ? list[b0 + lane] : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      const int r = k * epi + lane / lpe, v = lane % lpe;
+      const int pix = __shfl(my.x, r & 63), t = __shfl(my.y, r & 63) & 255;
+      q[k] = make_uint4(0, 0, 0, 0);
+      if (k * epi < BLK && r < nb)
+        q[k] = *(const uint4*)(dcol + ((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cglob + v * VEC);
+    }
+  };
+  int eb = wave * BLK;
+  if (eb < L) load_block(eb);
+  for (; eb < L; eb += 4 * BLK) {
+    const int nb = min(BLK, L - eb);
+    // rows past the block's entries are written too (as zeros): the MFMA
+    // reads all 32 rows, and stale LDS must not meet a zero weight as NaN
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      const int r = k * epi + lane / lpe, v = lane % lpe;
+      if (k * epi < BLK && r < BLK) *(uint4*)(dst + r * p.dcstr + v * VEC) = q[k];
+    }
+    const int4 cur = my;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
+    const int nbs = __builtin_amdgcn_readfirstlane(nb);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks * 16 >= nbs) break;
+      // the weight matrix of entries ks*16 .. ks*16+15: zero, then each
+      // (entry, corner) lane writes its weight at (corner pixel, entry)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(uint4*)(at + (i * 64 + lane) * 16) = make_uint4(0, 0, 0, 0);
+      {
+        const int j = lane & 15, qc = lane >> 4, e = ks * 16 + j;
+        const uint32_t info = (uint32_t)__shfl(cur.y, e);
+        const float ly = __int_as_float(__shfl(cur.z, e)), lx = __int_as_float(__shfl(cur.w, e));
+        if (e < nbs && ((info >> (9 + qc)) & 1u)) {
+          const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+          const float wy = (qc >> 1) ? ly : 1.0f - ly, wx = (qc & 1) ? lx : 1.0f - lx;
+          const float w = wy * wx;
+          const bf16_t hi = f32_to_bf16(w);
+          const bf16_t lo = f32_to_bf16(w - bf16_to_f32(hi));
+          const int P = (cy - 1 + (qc >> 1)) * p.CW + (cx - 1 + (qc & 1));
+          const int a = P * 32 + (((j >> 3) ^ ((P >> 2) & 1)) << 4) + (j & 7) * 2;
+          *(bf16_t*)(at + a) = hi;
+          *(bf16_t*)(at + 2048 + a) = lo;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint4 ahi[2], alo[2], bq[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = mb * 32 + (lane & 31);
+        const int a = row * 32 + (((lane >> 5) ^ ((row >> 2) & 1)) << 4);
+        ahi[mb] = *(const uint4*)(at + a);
+        alo[mb] = *(const uint4*)(at + 2048 + a);
+      }
+      bq[1] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nb_ = 0; nb_ < 2; ++nb_) {
+        if (nb_ == 1 && !nb1) break;  // columns past a 32-channel chunk are not read
+        const int gq = lane >> 4, j = lane & 15;
+        const int col = nb_ * 32 + 16 * (gq & 1) + 4 * (j & 3);
+        uint2 h[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int krow = ks * 16 + 8 * (gq >> 1) + 4 * t + (j >> 2);
+          h[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                               (__attribute__((address_space(3))) bf16x4_t*)(
+                                                   (unsigned char*)dst + krow * p.dcstr * 2 + col * 2)));
+        }
+        bq[nb_] = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (mb == 1 && !mb1) break;
+#pragma unroll
+        for (int nb_ = 0; nb_ < 2; ++nb_) {
+          if (nb_ == 1 && !nb1) break;
+          mfma_chunk(acc[mb][nb_], ahi[mb], bq[nb_], bf16_t());
+          mfma_chunk(acc[mb][nb_], alo[mb], bq[nb_], bf16_t());
+        }
+      }
+    }
+    doffset_owned<bf16_t>(cur, nb, lane, dst, p.dcstr, xl, p.xstr, XW, p.CC, HoWo, doffp);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // the four waves' partial sums, added in a fixed order in LDS [channel][pixel]
+  __syncthreads();
+  float* R = (float*)(smem + p.lds_dc);
+  constexpr int RS = 65;
+#pragma unroll 1
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb_ = 0; nb_ < 2; ++nb_)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int pix = mb * 32 + acc_row(lane, r), c = nb_ * 32 + (lane & 31);
+            if (pix < PX && c < p.CC) {
+              float* d = R + c * RS + pix;
+              *d = (w == 0 ? 0.f : *d) + acc[mb][nb_][r];
+            }
+          }
+    }
+    __syncthreads();
+  }
+  for (int k = tid; k < p.CC * chn * cwn; k += 256) {
+    const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
+    const int y = r / cwn, xx = r - y * cwn;
+    p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = R[cc * RS + y * p.CW + xx];
   }
 }
 
@@ -880,7 +1067,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck;
     b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
     b.CC = p.chunk_b;
-    b.dcstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
+    b.dcstr = p.chunk_b + (p.bwd_mf ? 16 : (d.dtype == DEFT_BF16 ? 8 : 4));
     b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;
     int cb = 0;
     while ((1 << cb) < p.list_cap + 1) ++cb;
@@ -894,7 +1081,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     if (b.num_tg) DEFT_LAUNCH("sample_backward_list", k_sample_bwd_list, dim3(b.num_tg), dim3(256), 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto kern = k_sample_bwd<T>;
+    auto kern = p.bwd_mf ? k_sample_bwd_mf : k_sample_bwd<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
     if (e != hipSuccess) return e;
     if (b.num_wg) DEFT_LAUNCH("sample_backward", kern, dim3(b.num_wg), dim3(256), p.lb_total, st, b);

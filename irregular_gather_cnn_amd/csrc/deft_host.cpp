@@ -88,14 +88,25 @@ bool layout_backward(deft_plan& p) {
   const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
   const int xstr = cb + vec;
   const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
-  const int ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core + spill slots
-  const int ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
+  // bf16 with a core of at most 64 pixels and 32 or 64 channels: the scatter
+  // runs on the MFMA units (per wave two 2 KB weight tiles; dCol rows padded
+  // to 16 extra channels so transposed reads of four rows hit distinct banks)
+  const bool mf = d.dtype == DEFT_BF16 && ch * cw <= 64 && cb % 32 == 0;
+  int ldx, ldc;
+  if (mf) {
+    ldx = 4 * 4096;
+    ldc = 4 * 32 * (cb + 16) * 2;  // also holds the final [channel][65] fp32 sums
+  } else {
+    ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core + spill slots
+    ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
+  }
   const int total = lx + ldx + ldc + 16 + 4 * 49 * 4 + 48 * 8;  // + list counter and per-tap tables
   if (total > kMaxLds) return false;
   p.btile_h = ch; p.btile_w = cw;
   p.btiles_h = (d.h + ch - 1) / ch; p.btiles_w = (d.w + cw - 1) / cw;
   p.num_btiles = d.n * p.btiles_h * p.btiles_w;
   p.chunk_b = cb;
+  p.bwd_mf = mf ? 1 : 0;
   p.lb_dx = lx; p.lb_dc = lx + ldx; p.lb_cnt = lx + ldx + ldc; p.lb_total = total;
   // list capacity: every output pixel whose tap's grid point lies within the
   // halo (plus one row/column for the +1 corners) of the core, for every tap
