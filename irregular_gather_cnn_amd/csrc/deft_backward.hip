@@ -462,11 +462,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  int4 my = make_int4(0, 0, 0, 0);
+  // list entries are fetched one block ahead of the dCol rows they address
+  int4 my = make_int4(0, 0, 0, 0), mynext = make_int4(0, 0, 0, 0);
   uint4 q[KQ];
+  auto load_list = [&](int b0) {
+    if (b0 < L) mynext = lane < min(BLK, L - b0) ? list[b0 + lane] : make_int4(0, 0, 0, 0);
+  };
   auto load_block = [&](int b0) {
     const int nb = min(BLK, L - b0);
-    my = lane < nb ? list[b0 + lane] : make_int4(0, 0, 0, 0);
+    my = mynext;
+    load_list(b0 + 4 * BLK);
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
       const int r = k * epi + lane / lpe, v = lane % lpe;
@@ -477,6 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
   };
   int eb = wave * BLK;
+  load_list(eb);
   if (eb < L) load_block(eb);
   for (; eb < L; eb += 4 * BLK) {
     const int nb = min(BLK, L - eb);
@@ -488,9 +494,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       if (k * epi < BLK && r < BLK) *(uint4*)(dst + r * p.dcstr + v * VEC) = q[k];
     }
     const int4 cur = my;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the rows are read by other lanes below: a wave's LDS operations execute
+    // in issue order, so only the compiler has to be kept from reordering
+    asm volatile("" ::: "memory");
     if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
     const int nbs = __builtin_amdgcn_readfirstlane(nb);
 #pragma unroll
@@ -516,9 +522,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           *(bf16_t*)(at + 2048 + a) = lo;
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      asm volatile("" ::: "memory");
       uint4 ahi[2], alo[2], bq[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -557,32 +561,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     doffset_owned<bf16_t>(cur, nb, lane, dst, p.dcstr, xl, p.xstr, XW, p.CC, HoWo, doffp);
     __builtin_amdgcn_wave_barrier();
   }
-  // the four waves' partial sums, added in a fixed order in LDS [channel][pixel]
+  // the four waves' partial sums, added in a fixed order: waves 0 and 1
+  // store theirs ([channel][pixel], two regions), waves 2 and 3 add them to
+  // their own and store back, and the write-out adds the two regions:
+  // (acc0 + acc2) + (acc1 + acc3)
   __syncthreads();
-  float* R = (float*)(smem + p.lds_dc);
   constexpr int RS = 65;
-#pragma unroll 1
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+  const int rsz = p.CC * RS;
+  float* R = (float*)(smem + p.lds_dx);  // [2][CC][RS] over the weight tiles and dCol rows
+  float* Rw = R + (wave & 1) * rsz;
+  // (every one of the 64 pixel slots of a channel row is written; slots past
+  // the core's pixels are never read)
+  if (wave < 2) {
+#pragma unroll
+    for (int nb_ = 0; nb_ < 2; ++nb_) {
+      if (nb_ == 1 && !nb1) break;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb_ = 0; nb_ < 2; ++nb_)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int pix = mb * 32 + acc_row(lane, r), c = nb_ * 32 + (lane & 31);
-            if (pix < PX && c < p.CC) {
-              float* d = R + c * RS + pix;
-              *d = (w == 0 ? 0.f : *d) + acc[mb][nb_][r];
-            }
-          }
+        for (int r = 0; r < 16; ++r)
+          Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)] = acc[mb][nb_][r];
     }
-    __syncthreads();
   }
+  __syncthreads();
+  if (wave >= 2) {
+#pragma unroll
+    for (int nb_ = 0; nb_ < 2; ++nb_) {
+      if (nb_ == 1 && !nb1) break;
+      float v[2][16];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[mb][r] = Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)] = v[mb][r] + acc[mb][nb_][r];
+    }
+  }
+  __syncthreads();
   for (int k = tid; k < p.CC * chn * cwn; k += 256) {
     const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
     const int y = r / cwn, xx = r - y * cwn;
-    p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = R[cc * RS + y * p.CW + xx];
+    const int ri = cc * RS + y * p.CW + xx;
+    p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = R[ri] + R[rsz + ri];
   }
 }
 

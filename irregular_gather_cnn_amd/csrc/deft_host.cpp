@@ -95,7 +95,7 @@ bool layout_backward(deft_plan& p) {
   int ldx, ldc;
   if (mf) {
     ldx = 4 * 4096;
-    ldc = 4 * 32 * (cb + 16) * 2;  // also holds the final [channel][65] fp32 sums
+    ldc = 4 * 32 * (cb + 16) * 2;  // with the tiles, also holds the final 2 x [channel][65] fp32 sums
   } else {
     ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core + spill slots
     ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
