@@ -625,11 +625,10 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
     const size_t pid = base + lane;
     bool miss = false;
     if (pid < total) {
-      const int pix = (int)(pid % HoWo);
-      const size_t r = pid / HoWo;
-      const int t = (int)(r % p.K2);
-      const size_t r2 = r / p.K2;
-      const int g = (int)(r2 % p.G), n = (int)(r2 / p.G);
+      const int pi = (int)pid;  // total < 2^31 (checked on the host)
+      const int r = pi / HoWo, pix = pi - r * HoWo;
+      const int r2 = r / p.K2, t = r - r2 * p.K2;
+      const int n = r2 / p.G, g = r2 - n * p.G;
       const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
       const int ti = t / p.KW, tj = t - ti * p.KW;
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
@@ -641,12 +640,10 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
     while (mask) {
       const int l = __ffsll((long long)mask) - 1;
       mask &= mask - 1;
-      const size_t q = base + l;
-      const int pix = (int)(q % HoWo);
-      const size_t r = q / HoWo;
-      const int t = (int)(r % p.K2);
-      const size_t r2 = r / p.K2;
-      const int g = (int)(r2 % p.G), n = (int)(r2 / p.G);
+      const int qi = (int)(base + l);
+      const int r = qi / HoWo, pix = qi - r * HoWo;
+      const int r2 = r / p.K2, t = r - r2 * p.K2;
+      const int n = r2 / p.G, g = r2 - n * p.G;
       const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
       const int ti = t / p.KW, tj = t - ti * p.KW;
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
@@ -957,17 +954,17 @@ __global__ __launch_bounds__(256) void k_prep_backward(const T* __restrict__ w, 
   const size_t nz4 = nz0 / 4;
   const size_t total = n1 + n2 + nz4 + (nz0 & 3);
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    // weight tensors are far below 2^31 elements: 32-bit index arithmetic
     if (e < n1) {
-      const int co = (int)(e % Cout);
-      const size_t r = e / Cout;
-      const int c = (int)(r % Cin);
-      const int t = (int)(r / Cin);
-      w2[e] = w[((size_t)co * Cin + c) * K2 + t];
+      const int ei = (int)e;
+      const int r = ei / Cout, co = ei - r * Cout;
+      const int t = r / Cin, c = r - t * Cin;
+      w2[e] = w[(co * Cin + c) * K2 + t];
     } else if (e < n1 + n2) {
-      const size_t f = e - n1;
-      const int kk = (int)(f % KKP);
-      const int c = (int)(f / KKP);
-      wofft[f] = kk < Oc * K2 ? w_off[((size_t)(kk / K2) * Cin + c) * K2 + kk % K2] : zero_elem<T>();
+      const int f = (int)(e - n1);
+      const int c = f / KKP, kk = f - c * KKP;
+      const int o = kk / K2;
+      wofft[f] = kk < Oc * K2 ? w_off[(o * Cin + c) * K2 + (kk - o * K2)] : zero_elem<T>();
     } else if (e < n1 + n2 + nz4) {
       ((float4*)z0)[e - n1 - n2] = make_float4(0.f, 0.f, 0.f, 0.f);
     } else {
@@ -987,7 +984,20 @@ __global__ __launch_bounds__(256) void k_bias_partial(const T* __restrict__ dy, 
   const int o = main ? ch : ch - Cout;
   const size_t base = ((size_t)n * (main ? Cout : Oc) + o) * HoWo;
   float s = 0.f;
-  for (int q = threadIdx.x; q < HoWo; q += 256) s += main ? Elem<T>::to_f32(dy[base + q]) : doff[base + q];
+  if (main && sizeof(T) == 2 && (HoWo & 7) == 0) {  // 16-byte loads of eight bf16
+    for (int q = threadIdx.x * 8; q < HoWo; q += 256 * 8) {
+      float f[8];
+      unpack8(*(const uint4*)((const bf16_t*)dy + base + q), f);
+      s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+    }
+  } else if (!main && (HoWo & 3) == 0) {
+    for (int q = threadIdx.x * 4; q < HoWo; q += 256 * 4) {
+      const float4 v = *(const float4*)(doff + base + q);
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+  } else {
+    for (int q = threadIdx.x; q < HoWo; q += 256) s += main ? Elem<T>::to_f32(dy[base + q]) : doff[base + q];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -1012,10 +1022,9 @@ __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ 
     if (e < n1 + n2) {
       const bool first = e < n1;
       const size_t f = first ? e : e - n1;  // partial order: [o][t][c]
-      const int c = (int)(f % Cin);
-      const size_t r = f / Cin;
-      const int t = (int)(r % K2);
-      const size_t o = r / K2;
+      const int fi = (int)f;                // weight tensors: below 2^31 elements
+      const int r = fi / Cin, c = fi - r * Cin;
+      const int o = r / K2, t = r - o * K2;
       const float* src = first ? dwpart : dwoffpart;
       const size_t stride = first ? n1 : n2;
       const int cnt = first ? ndw : nwp;
@@ -1030,7 +1039,7 @@ __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ 
         for (int u = 0; u < 8; ++u) s += v[u];
       }
       for (; z < cnt; ++z) s += src[(size_t)z * stride + f];
-      (first ? dw : dwoff)[(o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
+      (first ? dw : dwoff)[((size_t)o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
     } else {
       const int ch = (int)(e - n1 - n2);
       T* dst = ch < Cout ? db : dboff;

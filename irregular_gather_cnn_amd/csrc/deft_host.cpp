@@ -48,8 +48,10 @@ int validate(const deft_desc* d) {
   const double x_elems = (double)d->n * d->c_in * d->h * d->w;
   const double col_elems = (double)d->n * out_dim(d->h, d->kh, d->stride_h, d->pad_h, d->dil_h) *
                            out_dim(d->w, d->kw, d->stride_w, d->pad_w, d->dil_w) * d->c_in * d->kh * d->kw;
+  const double pairs = col_elems / (d->c_in * d->kh * d->kw) * d->offset_groups * d->kh * d->kw;
   if (x_elems >= 2147483647.0 || (double)d->n * d->c_out * d->h * d->w >= 2147483647.0 ||
-      col_elems / (d->c_in * d->kh * d->kw) >= 2147483647.0)
+      col_elems / (d->c_in * d->kh * d->kw) >= 2147483647.0 || pairs >= 2147483647.0 ||
+      (double)(d->c_out + 2.0 * d->offset_groups * d->kh * d->kw + 64) * d->c_in * d->kh * d->kw >= 2147483647.0)
     return DEFT_ERR_UNSUPPORTED;
   return DEFT_OK;
 }

@@ -717,30 +717,28 @@ __global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, c
   const size_t n2 = CA > 0 ? (size_t)G * K2 * Cin * 32 : (size_t)OcP * K2 * Cin;
   const int nks = CA / 16, nch = CA > 0 ? Cin / CA : 1;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * 256) {
+    // weight tensors are far below 2^31 elements: 32-bit index arithmetic
     if (e < n1) {
-      const int c = (int)(e % Cin);
-      const size_t r = e / Cin;
-      const int t = (int)(r % K2);
-      const int co = (int)(r / K2);
-      wt[e] = w[((size_t)co * Cin + c) * K2 + t];
+      const int ei = (int)e;
+      const int r = ei / Cin, c = ei - r * Cin;
+      const int co = r / K2, t = r - co * K2;
+      wt[e] = w[(co * Cin + c) * K2 + t];
     } else if (CA > 0) {
-      const size_t f = e - n1;
-      const int e8 = (int)(f & 7), L = (int)((f >> 3) & 63);
-      size_t r = f >> 9;
-      const int k = (int)(r % nks); r /= nks;
-      const int ch = (int)(r % nch); r /= nch;
-      const int t = (int)(r % K2);
-      const int g = (int)(r / K2);
+      const int f = (int)(e - n1);
+      const int e8 = f & 7, L = (f >> 3) & 63;
+      int r = f >> 9;
+      const int k = r % nks; r /= nks;
+      const int ch = r % nch; r /= nch;
+      const int t = r % K2;
+      const int g = r / K2;
       const int ol = L & 31;
       const int c = ch * CA + (L >> 5) * (CA / 2) + k * 8 + e8;
-      woff_p[f] = ol < 2 * K2 ? w_off[((size_t)(2 * g * K2 + ol) * Cin + c) * K2 + t] : zero_elem<T>();
+      woff_p[f] = ol < 2 * K2 ? w_off[((2 * g * K2 + ol) * Cin + c) * K2 + t] : zero_elem<T>();
     } else {
-      const size_t f = e - n1;
-      const int c = (int)(f % Cin);
-      const size_t r = f / Cin;
-      const int t = (int)(r % K2);
-      const int o = (int)(r / K2);
-      woff_p[f] = o < Oc ? w_off[((size_t)o * Cin + c) * K2 + t] : zero_elem<T>();
+      const int f = (int)(e - n1);
+      const int r = f / Cin, c = f - r * Cin;
+      const int o = r / K2, t = r - o * K2;
+      woff_p[f] = o < Oc ? w_off[(o * Cin + c) * K2 + t] : zero_elem<T>();
     }
   }
 }
