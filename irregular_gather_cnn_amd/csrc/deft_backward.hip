@@ -753,13 +753,24 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
     }
   }
   {
-    const int tot = MB * 32 * p.band_rows * p.DLS;
-    for (int e = tid; e < tot; e += 256) {
-      const int o = e / (p.band_rows * p.DLS), rr = e - o * (p.band_rows * p.DLS);
-      const int ry = rr / p.DLS, wo = rr - ry * p.DLS;
-      float v = 0.f;
-      if (o < p.orows && ry < nrows && wo < p.Wo) v = doff[(size_t)(p.o0 + o) * HoWo + (size_t)(ho0 + ry) * p.Wo + wo];
-      dl[e] = Elem<T>::from_f32(v);
+    // eight elements per thread per pass, all loads of a pass in flight
+    const int rowlen = p.band_rows * p.DLS;
+    const int tot = MB * 32 * rowlen;
+    const FastDiv drow = make_fastdiv(rowlen), dls = make_fastdiv(p.DLS);
+    for (int e0 = tid; e0 < tot; e0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256;
+        const int o = fdiv(e, drow), rr = e - o * rowlen;
+        const int ry = fdiv(rr, dls), wo = rr - ry * p.DLS;
+        v[u] = 0.f;
+        if (e < tot && o < p.orows && ry < nrows && wo < p.Wo)
+          v[u] = doff[(size_t)(p.o0 + o) * HoWo + (size_t)(ho0 + ry) * p.Wo + wo];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (e0 + u * 256 < tot) dl[e0 + u * 256] = Elem<T>::from_f32(v[u]);
     }
   }
   __syncthreads();
@@ -1086,7 +1097,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  e = launch_gemm_dcol(p, w2, a.dy, dcol, maxbits, st);
+  e = launch_gemm_dcol(p, w2, a.dy, dcol, p.bwd_mf ? nullptr : maxbits, st);  // the MFMA scatter needs no max
   if (e != hipSuccess) return e;
   e = launch_gemm_dw(p, a.dy, cols, dwpart, st);
   if (e != hipSuccess) return e;

@@ -262,9 +262,10 @@ struct DcolOp {
   }
   __device__ void store(const TileCoord&, int mb, int nb, const f32x16_t& acc, int lane) const {
     const int q = nb + (lane & 31);
-    // max |value| of this block (valid entries only), one atomic per wave
+    // max |value| of this block (valid entries only), one atomic per wave;
+    // skipped when no maxbits word is given
     float mx = 0.f;
-    if (q < N) {
+    if (maxbits && q < N) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e0 = mb + 8 * j + 4 * (lane >> 5);
@@ -275,7 +276,8 @@ struct DcolOp {
     }
     for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
     // most blocks do not raise the running max: skip their atomics
-    if (lane == 0 && __float_as_uint(mx) > __hip_atomic_load(maxbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    if (maxbits && lane == 0 &&
+        __float_as_uint(mx) > __hip_atomic_load(maxbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
       atomicMax(maxbits, __float_as_uint(mx));
     if (q >= N) return;
     T* row = dcol + (size_t)q * M;

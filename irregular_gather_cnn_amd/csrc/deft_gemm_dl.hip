@@ -291,8 +291,10 @@ struct DlDcol {
     const int img = fdiv(q, div_howo), p = q - img * HoWo;
     return ((img * K + k) * HoWo + p) * 2;
   }
-  // running max of |dCol| (fp32 bits), one atomic per wave at most
+  // running max of |dCol| (fp32 bits), one atomic per wave at most; skipped
+  // when no maxbits word is given (only the fixed-point scatter needs it)
   __device__ void observe(const f32x16_t (&acc)[4][4], int mw, int nw, int lane) const {
+    if (!maxbits) return;
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
