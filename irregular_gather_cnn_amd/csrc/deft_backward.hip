@@ -752,7 +752,29 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
       xs[e] = v;
     }
   }
-  {
+  if (sizeof(T) == 2 && (p.Wo & 3) == 0 && (HoWo & 3) == 0 && (p.DLS & 3) == 0) {
+    // four pixels per piece (one 16-byte load, one 8-byte store), eight
+    // pieces per thread per pass; padding rows and columns are zero
+    const int pr = p.DLS >> 2, rowp = p.band_rows * pr;
+    const int tot = MB * 32 * rowp;
+    const FastDiv drow = make_fastdiv(rowp), dpr = make_fastdiv(pr);
+    for (int e0 = tid; e0 < tot; e0 += 256 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256;
+        const int o = fdiv(e, drow), rr = e - o * rowp;
+        const int ry = fdiv(rr, dpr), w4 = (rr - ry * pr) * 4;
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < tot && o < p.orows && ry < nrows && w4 < p.Wo)
+          v[u] = *(const float4*)(doff + (size_t)(p.o0 + o) * HoWo + (size_t)(ho0 + ry) * p.Wo + w4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (e0 + u * 256 < tot)
+          *(uint2*)(dl + (e0 + u * 256) * 4) = make_uint2(pack_bf16x2(v[u].x, v[u].y), pack_bf16x2(v[u].z, v[u].w));
+    }
+  } else {
     // eight elements per thread per pass, all loads of a pass in flight
     const int rowlen = p.band_rows * p.DLS;
     const int tot = MB * 32 * rowlen;
