@@ -927,22 +927,38 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
       kinfo[kl] = ki;
     }
     __syncthreads();
-    // B tile: dOffset at the output pixel whose tap lands on the input pixel
-    for (int pix = wave; pix < 64; pix += 4) {
-      const int q = pix0 + pix;
-      const int y = fdiv(q, p.div_w), xx = q - y * p.W;
-      for (int kl = lane; kl < len; kl += 64) {
-        const int4 ki = kinfo[kl];
-        float v = 0.f;
-        const int ny = y + ki.y, nx = xx + ki.z;
-        if (ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
-          int ho = ny, wo = nx;
-          bool ok = true;
-          if (p.SH != 1) { ho = fdiv(ny, p.div_sh); ok = ho * p.SH == ny; }
-          if (p.SW != 1) { wo = fdiv(nx, p.div_sw); ok = ok && wo * p.SW == nx; }
-          if (ok && ho < p.Ho && wo < p.Wo) v = doff[(size_t)ki.x + (size_t)ho * p.Wo + wo];
+    // B tile: dOffset at the output pixel whose tap lands on the input pixel;
+    // eight (pixel, depth) gathers per thread in flight at a time
+    {
+      const int tot = 64 * len;
+      const FastDiv dlen = make_fastdiv(len);
+      for (int e0 = tid; e0 < tot; e0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 256;
+          const int pix = fdiv(e, dlen), kl = e - pix * len;
+          const int q = pix0 + pix;
+          const int y = fdiv(q, p.div_w), xx = q - y * p.W;
+          const int4 ki = kinfo[e < tot ? kl : 0];
+          v[u] = 0.f;
+          const int ny = y + ki.y, nx = xx + ki.z;
+          if (e < tot && ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
+            int ho = ny, wo = nx;
+            bool ok = true;
+            if (p.SH != 1) { ho = fdiv(ny, p.div_sh); ok = ho * p.SH == ny; }
+            if (p.SW != 1) { wo = fdiv(nx, p.div_sw); ok = ok && wo * p.SW == nx; }
+            if (ok && ho < p.Ho && wo < p.Wo) v[u] = doff[(size_t)ki.x + (size_t)ho * p.Wo + wo];
+          }
         }
-        bt[pix * bstr + kl] = Elem<T>::from_f32(v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 256;
+          if (e < tot) {
+            const int pix = fdiv(e, dlen), kl = e - pix * len;
+            bt[pix * bstr + kl] = Elem<T>::from_f32(v[u]);
+          }
+        }
       }
     }
     __syncthreads();
