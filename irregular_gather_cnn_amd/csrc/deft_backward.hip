@@ -19,7 +19,7 @@
 //   k_woff_bwd     -- per (image, 32-channel slice, band of output rows):
 //                     dW_off partials = dOffset rows against the plain
 //                     patches of x, both staged in LDS, on MFMA.
-//   k_dx_final     -- per 64 input pixels x 128 channels: dX_offset, the
+//   k_dx_final     -- per 64 input pixels x 256 channels: dX_offset, the
 //                     transposed offset convolution (MFMA), plus the sampling
 //                     part of dX; rounded once.
 //   k_bias_partial, k_reduce_final -- per-image bias sums, then one fixed-order
@@ -877,7 +877,7 @@ struct DxParams {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
+__global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
   constexpr int VEC = Elem<T>::VEC;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
   const int bstr = p.KKC + VEC;
   T* bt = (T*)smem;  // [64][bstr]
   const float* __restrict__ doff = p.doff + (size_t)n * p.Oc * HoWo;
-  const int c0 = cb * 128 + wave * 32;
+  const int c0 = cb * 256 + wave * 32;  // eight waves, 32 channels each
   const bool active = c0 < p.Cin;
   const T* __restrict__ wt = (const T*)p.wofft;
   f32x16_t acc[2];
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
     const int len = min(p.KKC, p.KKP - kb);
     __syncthreads();
     // per depth index kk = o*K2 + tap: dOffset plane and the tap's shift
-    for (int kl = tid; kl < len; kl += 256) {
+    for (int kl = tid; kl < len; kl += 512) {
       const int kk = kb + kl;
       int4 ki = make_int4(-1, 0, 0, 0);
       if (kk < p.Oc * p.K2) {
@@ -932,11 +932,11 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
     {
       const int tot = 64 * len;
       const FastDiv dlen = make_fastdiv(len);
-      for (int e0 = tid; e0 < tot; e0 += 256 * 8) {
+      for (int e0 = tid; e0 < tot; e0 += 512 * 8) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 256;
+          const int e = e0 + u * 512;
           const int pix = fdiv(e, dlen), kl = e - pix * len;
           const int q = pix0 + pix;
           const int y = fdiv(q, p.div_w), xx = q - y * p.W;
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(256) void k_dx_final(const DxParams p) {
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 256;
+          const int e = e0 + u * 512;
           if (e < tot) {
             const int pix = fdiv(e, dlen), kl = e - pix * len;
             bt[pix * bstr + kl] = Elem<T>::from_f32(v[u]);
@@ -1227,7 +1227,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     q.K2 = p.taps; q.Oc = p.oc; q.KKP = p.kk_pad;
     q.KKC = p.kk_pad < 256 ? p.kk_pad : 256;
     q.pix_blocks = (d.h * d.w + 63) / 64;
-    q.cblocks = (d.c_in + 127) / 128;
+    q.cblocks = (d.c_in + 255) / 256;
     q.num_wg = d.n * q.pix_blocks * q.cblocks;
     q.wofft = wofft; q.doff = doff; q.dxs = dxs; q.dx = a.dx;
     q.div_w = make_fastdiv(d.w); q.div_sh = make_fastdiv(d.stride_h); q.div_sw = make_fastdiv(d.stride_w);
@@ -1235,7 +1235,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     auto kern = k_dx_final<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    if (q.num_wg) DEFT_LAUNCH("dx_final", kern, dim3(q.num_wg), dim3(256), lds, st, q);
+    if (q.num_wg) DEFT_LAUNCH("dx_final", kern, dim3(q.num_wg), dim3(512), lds, st, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
