@@ -27,16 +27,24 @@
 namespace deft {
 namespace {
 
-constexpr int kBK = 32;          // k elements per stage (64 bytes per row)
-constexpr int kStages = 4;       // LDS ring depth; loads run three stages ahead
-constexpr int kTile = 256;       // BM = BN
-constexpr int kWave = 128;       // per-wave block (WM = WN)
-constexpr int kStageBytes = 2 * kTile * kBK * 2;          // A + B per stage
-constexpr int kLdsMain = kStages * kStageBytes;           // 128 KB
-constexpr int kEpiStride = kWave * 2 + 16;                 // bytes per transposed row
-constexpr int kLdsEpi = 4 * kWave * kEpiStride;            // 136 KB
-constexpr int kLds = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
-constexpr int kPerWave = kTile * kBK * 2 / 1024 / 4;      // 1 KB loads per wave per operand per stage
+constexpr int kBK = 32;  // k elements per stage (64 bytes per row)
+
+// Tile shape of one GEMM: BM x BN per workgroup of 2 x 2 waves (each wave
+// BM/2 x BN/2), STAGES-deep LDS ring (loads run STAGES-1 stages ahead), OCC
+// workgroups per CU the LDS and registers are sized for.
+template <int BM_, int BN_, int STAGES_, int OCC_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  static constexpr int kStageBytes = (BM + BN) * kBK * 2;  // A + B per stage
+  static constexpr int kPerA = BM * kBK * 2 / 1024 / 4;     // 1 KB loads per wave per stage, A
+  static constexpr int kPerB = BN * kBK * 2 / 1024 / 4;     // and B
+  static constexpr int kLdsMain = STAGES * kStageBytes;
+  static constexpr int kEpiStride = WM * 2 + 16;            // bytes per transposed row
+  static constexpr int kLdsEpi = 4 * WN * kEpiStride;
+  static constexpr int kLds = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
+};
+using Cfg256 = GemmCfg<256, 256, 4, 1>;
 __device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
   const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
   return __builtin_bit_cast(uint2, v);
@@ -45,19 +53,20 @@ __device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
 // Row-form swizzle (64-byte rows, 4 chunks): 16 consecutive rows reading the
 // same logical chunk hit 16 distinct 16-byte bank slots.
 __device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
-// k-major swizzle (rows of 2*kTile bytes): the four k rows a 16-lane group of
+// k-major swizzle (rows of 2*ROWS bytes): the four k rows a 16-lane group of
 // a transposed read touches land in four distinct 64-byte bank windows.
 __device__ __forceinline__ int swz_kmaj(int k) { return 4 * (k & 3); }
 
-// Issues the loads of one operand's stage: rows [0, kTile) (row form) or k
-// rows [0, kBK) (k-major form) of the tile, `op_off` giving the byte offset
-// of each 16-byte chunk or kOOB.
-template <bool KMAJ, class F>
+// Issues the loads of one operand's stage: rows [0, ROWS) (row form) or k
+// rows [0, kBK) (k-major form, ROWS columns) of the tile, `op_off` giving the
+// byte offset of each 16-byte chunk or kOOB.
+template <bool KMAJ, int ROWS, class F>
 __device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* base, int wave, int lane,
                                               int k0, const F& op_off) {
+  constexpr int kPer = ROWS * kBK * 2 / 1024 / 4;
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int b = wave * kPerWave + i;
+  for (int i = 0; i < kPer; ++i) {
+    const int b = wave * kPer + i;
     unsigned char* dst = base + b * 1024;
     int off;
     if constexpr (!KMAJ) {
@@ -66,8 +75,8 @@ __device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* bas
       off = op_off(row, k0 + 8 * c);
     } else {
       const int pos = b * 1024 + lane * 16;
-      const int krow = pos / (2 * kTile);
-      const int c = ((pos % (2 * kTile)) >> 4) ^ swz_kmaj(krow);
+      const int krow = pos / (2 * ROWS);
+      const int c = ((pos % (2 * ROWS)) >> 4) ^ swz_kmaj(krow);
       off = op_off(k0 + krow, 8 * c);
     }
     load_lds16(r, dst, off);
@@ -76,7 +85,7 @@ __device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* bas
 
 // MFMA fragment (8 consecutive k of row/column `rc` of the tile) for k-chunk
 // pair `ks` (16 k) of a stage.
-template <bool KMAJ>
+template <bool KMAJ, int ROWS>
 __device__ __forceinline__ uint4 fragment(const unsigned char* base, int rc0, int ks, int lane) {
   if constexpr (!KMAJ) {
     const int row = rc0 + (lane & 31);
@@ -90,16 +99,18 @@ __device__ __forceinline__ uint4 fragment(const unsigned char* base, int rc0, in
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int krow = 16 * ks + 8 * (g >> 1) + 4 * t + (j >> 2);
-      h[t] = read_tr(base + krow * (2 * kTile) + ((c ^ swz_kmaj(krow)) << 4) + (n & 7) * 2);
+      h[t] = read_tr(base + krow * (2 * ROWS) + ((c ^ swz_kmaj(krow)) << 4) + (n & 7) * 2);
     }
     return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
   }
 }
 
 template <class Op>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_dl(const Op op) {
-  constexpr int MI = kWave / 32, NI = kWave / 32;
-  constexpr int kIssue = 2 * kPerWave;  // loads per wave per stage
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Op::Cfg::OCC, Op::Cfg::OCC))) void k_gemm_dl(
+    const Op op) {
+  using C = typename Op::Cfg;
+  constexpr int MI = C::MI, NI = C::NI, kStages = C::STAGES, kStageBytes = C::kStageBytes;
+  constexpr int kIssue = C::kPerA + C::kPerB;  // loads per wave per stage
   extern __shared__ __align__(16) unsigned char smem[];
   const TileCoord tc = op.tile(blockIdx.x);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -118,10 +129,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto issue = [&](int s) {
     unsigned char* st = smem + (s % kStages) * kStageBytes;
     const int k0 = tc.kb + s * kBK;
-    issue_operand<Op::A_KMAJ>(ra, st, wave, lane, k0,
-                              [&](int x, int y) { return op.a_off(tc, x, y); });
-    issue_operand<Op::B_KMAJ>(rb, st + kTile * kBK * 2, wave, lane, k0,
-                              [&](int x, int y) { return op.b_off(tc, x, y); });
+    issue_operand<Op::A_KMAJ, C::BM>(ra, st, wave, lane, k0,
+                                     [&](int x, int y) { return op.a_off(tc, x, y); });
+    issue_operand<Op::B_KMAJ, C::BN>(rb, st + C::BM * kBK * 2, wave, lane, k0,
+                                     [&](int x, int y) { return op.b_off(tc, x, y); });
   };
   // A stage holds two 16-k steps.  The fragments of the next step are read
   // while the MFMAs of the current one run, also across the stage boundary:
@@ -130,11 +141,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int kReads = MI * (Op::A_KMAJ ? 2 : 1) + NI * (Op::B_KMAJ ? 2 : 1);  // LDS reads per step
   auto read_step = [&](int s, int ks, uint4* fa, uint4* fb) {
     const unsigned char* a = smem + (s % kStages) * kStageBytes;
-    const unsigned char* b = a + kTile * kBK * 2;
+    const unsigned char* b = a + C::BM * kBK * 2;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i] = fragment<Op::A_KMAJ>(a, wm * kWave + i * 32, ks, lane);
+    for (int i = 0; i < MI; ++i) fa[i] = fragment<Op::A_KMAJ, C::BM>(a, wm * C::WM + i * 32, ks, lane);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) fb[j] = fragment<Op::B_KMAJ>(b, wn * kWave + j * 32, ks, lane);
+    for (int j = 0; j < NI; ++j) fb[j] = fragment<Op::B_KMAJ, C::BN>(b, wn * C::WN + j * 32, ks, lane);
   };
   auto mfma_step = [&](const uint4* fa, const uint4* fb) {
 #pragma unroll
@@ -176,8 +187,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     interleave();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave is done reading stage it
     if (it + 1 < nk) {
-      // stages issued after it+1 so far: up to it+3
-      wait_stage(min(2, nk - 2 - it));
+      // stages issued after it+1 so far: up to it+STAGES-1
+      wait_stage(min(kStages - 2, nk - 2 - it));
       __syncthreads();
       if (it + kStages < nk) issue(it + kStages);  // into the buffer of stage it
       read_step(it + 1, 0, fa0, fb0);
@@ -186,13 +197,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     interleave();
   }
 
-  const int mw = tc.m0 + wm * kWave, nw = tc.n0 + wn * kWave;
+  const int mw = tc.m0 + wm * C::WM, nw = tc.n0 + wn * C::WN;
   op.observe(acc, mw, nw, lane);
   if constexpr (Op::LDS_EPILOGUE) {
     // Transpose this wave's block through LDS: row n (local) holds the
     // wave's 128 m values; each lane owns 4 consecutive m of one n per block.
     __syncthreads();
-    unsigned char* reg = smem + wave * kWave * kEpiStride;
+    constexpr int kEpiStride = C::kEpiStride;
+    unsigned char* reg = smem + wave * C::WN * kEpiStride;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -209,9 +221,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
     __syncthreads();
+    constexpr int kCh = C::WM / 8, kRows = 64 / kCh;  // 16-byte chunks per row, rows per pass
 #pragma unroll 4
-    for (int it = 0; it < kWave / 4; ++it) {
-      const int nl = it * 4 + (lane >> 4), c = lane & 15;
+    for (int it = 0; it < C::WN / kRows; ++it) {
+      const int nl = it * kRows + lane / kCh, c = lane % kCh;
       const uint4 v = *(const uint4*)(reg + nl * kEpiStride + c * 16);
       op.store_chunk(nw + nl, mw + c * 8, v);
     }
@@ -229,6 +242,7 @@ __host__ __device__ inline uint32_t rsrc_bytes(size_t bytes) {
 
 // ---- forward: C[m = q][n = co] = sum_k cols[q][k] Wt[co][k]; y[img][co][p] = C + b[co] ----
 struct DlFwd {
+  using Cfg = Cfg256;
   static constexpr bool A_KMAJ = false, B_KMAJ = false, LDS_EPILOGUE = true;
   const bf16_t* cols;  // [M][K]
   const bf16_t* wt;    // [N][K]
@@ -241,7 +255,7 @@ struct DlFwd {
   __device__ TileCoord tile(int bid) const {
     const int lb = xcd_swizzle(bid, tilesM * tilesN);
     const int mt = lb / tilesN, nt = lb - mt * tilesN;
-    return TileCoord{mt * kTile, nt * kTile, 0, K, 0};
+    return TileCoord{mt * Cfg::BM, nt * Cfg::BN, 0, K, 0};
   }
   __device__ int a_off(const TileCoord& tc, int row, int k) const {
     const int m = tc.m0 + row;
@@ -251,7 +265,8 @@ struct DlFwd {
     const int n = tc.n0 + row;
     return (n < N && k < K) ? (n * K + k) * 2 : kOOB;
   }
-  __device__ void observe(const f32x16_t (&)[4][4], int, int, int) const {}
+  template <int MI_, int NI_>
+  __device__ void observe(const f32x16_t (&)[MI_][NI_], int, int, int) const {}
   __device__ float column_add(int n) const { return (bias && n < N) ? bf16_to_f32(bias[n]) : 0.f; }
   // 8 consecutive pixels q = m..m+7 of output channel n (never split by an
   // image boundary: HoWo % 8 == 0 on this path)
@@ -265,6 +280,7 @@ struct DlFwd {
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
+  using Cfg = GemmCfg<256, 128, 3, 2>;
   static constexpr bool A_KMAJ = false, B_KMAJ = true, LDS_EPILOGUE = true;
   const bf16_t* w2;  // [M][K]
   const bf16_t* dy;  // [img][K][HoWo]
@@ -278,7 +294,7 @@ struct DlDcol {
     // consecutive workgroups (one XCD) share the dY tile of one pixel range
     const int lb = xcd_swizzle(bid, tilesM * tilesN);
     const int nt = lb / tilesM, mt = lb - nt * tilesM;
-    return TileCoord{mt * kTile, nt * kTile, 0, K, 0};
+    return TileCoord{mt * Cfg::BM, nt * Cfg::BN, 0, K, 0};
   }
   __device__ int a_off(const TileCoord& tc, int row, int k) const {
     const int m = tc.m0 + row;
@@ -293,13 +309,14 @@ struct DlDcol {
   }
   // running max of |dCol| (fp32 bits), one atomic per wave at most; skipped
   // when no maxbits word is given (only the fixed-point scatter needs it)
-  __device__ void observe(const f32x16_t (&acc)[4][4], int mw, int nw, int lane) const {
+  template <int MI_, int NI_>
+  __device__ void observe(const f32x16_t (&acc)[MI_][NI_], int mw, int nw, int lane) const {
     if (!maxbits) return;
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI_; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NI_; ++j) {
         if (nw + j * 32 + (lane & 31) >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -319,6 +336,7 @@ struct DlDcol {
 
 // ---- dW partial of split z: part[z][co][e] = sum_{q in split} dY[img(q)][co][p(q)] cols[q][e] ----
 struct DlDw {
+  using Cfg = Cfg256;
   static constexpr bool A_KMAJ = false, B_KMAJ = true, LDS_EPILOGUE = false;
   const bf16_t* dy;    // [img][M][HoWo]
   const bf16_t* cols;  // [P][N]
@@ -334,7 +352,7 @@ struct DlDw {
     const int z = lb / per, r = lb - z * per;
     const int mt = r / tilesN, nt = r - mt * tilesN;
     const int kb = z * kper, ke = min(P, kb + kper);
-    return TileCoord{mt * kTile, nt * kTile, kb, ke, z};
+    return TileCoord{mt * Cfg::BM, nt * Cfg::BN, kb, ke, z};
   }
   // 8 consecutive pixels q..q+7 (one image) of output channel m
   __device__ int a_off(const TileCoord& tc, int row, int q) const {
@@ -347,7 +365,8 @@ struct DlDw {
     const int e = tc.n0 + col;
     return (q < tc.ke && e < N) ? (q * N + e) * 2 : kOOB;
   }
-  __device__ void observe(const f32x16_t (&)[4][4], int, int, int) const {}
+  template <int MI_, int NI_>
+  __device__ void observe(const f32x16_t (&)[MI_][NI_], int, int, int) const {}
   __device__ float column_add(int) const { return 0.f; }
   __device__ void store_chunk(int, int, const uint4) const {}
   __device__ void store_acc(const TileCoord& tc, int mb, int nb, const f32x16_t& acc, int lane) const {
@@ -365,14 +384,15 @@ struct DlDw {
 template <class Op>
 hipError_t run_dl(const char* name, const Op& op, int grid, hipStream_t st) {
   auto kern = k_gemm_dl<Op>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  constexpr int lds = Op::Cfg::kLds;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   if (grid == 0) return hipSuccess;
-  DEFT_LAUNCH(name, kern, dim3(grid), dim3(256), kLds, st, op);
+  DEFT_LAUNCH(name, kern, dim3(grid), dim3(256), lds, st, op);
   return hipGetLastError();
 }
 
-int tiles(int x) { return (x + kTile - 1) / kTile; }
+int tiles(int x, int t) { return (x + t - 1) / t; }
 
 }  // namespace
 
@@ -387,7 +407,7 @@ bool gemm_dl_supported(const deft_plan& p) {
 
 void gemm_dl_dw_split(const deft_plan& p, int* splits, int* kper) {
   const int P = p.d.n * p.ho * p.wo;
-  const int per = tiles(p.d.c_out) * tiles(p.ck);
+  const int per = tiles(p.d.c_out, DlDw::Cfg::BM) * tiles(p.ck, DlDw::Cfg::BN);
   int s = 256 / per;
   if (s < 1) s = 1;
   int k = (P + s - 1) / s;
@@ -403,7 +423,7 @@ hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols,
   op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
   op.M = p.d.n * p.ho * p.wo; op.N = p.d.c_out; op.K = p.ck; op.HoWo = p.ho * p.wo;
   op.div_howo = make_fastdiv(op.HoWo);
-  op.tilesM = tiles(op.M); op.tilesN = tiles(op.N);
+  op.tilesM = tiles(op.M, DlFwd::Cfg::BM); op.tilesN = tiles(op.N, DlFwd::Cfg::BN);
   return run_dl("gemm_forward", op, op.tilesM * op.tilesN, st);
 }
 
@@ -413,7 +433,7 @@ hipError_t dl_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void
   op.w2 = (const bf16_t*)w2; op.dy = (const bf16_t*)dy; op.dcol = (bf16_t*)dcol; op.maxbits = maxbits;
   op.M = p.ck; op.N = p.d.n * p.ho * p.wo; op.K = p.d.c_out; op.HoWo = p.ho * p.wo;
   op.div_howo = make_fastdiv(op.HoWo);
-  op.tilesM = tiles(op.M); op.tilesN = tiles(op.N);
+  op.tilesM = tiles(op.M, DlDcol::Cfg::BM); op.tilesN = tiles(op.N, DlDcol::Cfg::BN);
   return run_dl("gemm_dcol", op, op.tilesM * op.tilesN, st);
 }
 
@@ -422,7 +442,7 @@ hipError_t dl_gemm_dw(const deft_plan& p, const void* dy, const void* cols, floa
   op.dy = (const bf16_t*)dy; op.cols = (const bf16_t*)cols; op.part = part;
   op.M = p.d.c_out; op.N = p.ck; op.P = p.d.n * p.ho * p.wo; op.HoWo = p.ho * p.wo;
   op.div_howo = make_fastdiv(op.HoWo);
-  op.tilesM = tiles(op.M); op.tilesN = tiles(op.N);
+  op.tilesM = tiles(op.M, DlDw::Cfg::BM); op.tilesN = tiles(op.N, DlDw::Cfg::BN);
   gemm_dl_dw_split(p, &op.splits, &op.kper);
   return run_dl("gemm_dw", op, op.tilesM * op.tilesN * op.splits, st);
 }

@@ -277,6 +277,26 @@ def test_backward_matches_oracle_small(case, dtype):
         assert e <= tol, k
 
 
+@pytest.mark.parametrize("plan", [(4, 8, 0, 0), (8, 8, 1, 0), (8, 8, 1, -1)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_small_halo_misses(plan, dtype):
+    """A halo of 0 or 1 with offsets of about 2 px: many taps fall beyond the
+    halo and take the miss path (recorded by the core holding their grid
+    point, including grid points in the padding beyond the image border)."""
+    if plan[3] == -1 and dtype != "bf16":
+        pytest.skip("direct gather is bf16 only")
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, train=True, n=2, c_in=32, c_out=24, h=13, w=11,
+                                                     pad=2, dil=2, offset_std=2.0)
+    say("backward small halo", dtype, plan)
+    inp, layer, y, off, g = run_backward(wl, plan=plan)
+    s = shape_of(wl)
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL[dtype], k
+
+
 @pytest.mark.parametrize("case", [
     dict(n=3, c_in=48, c_out=40, h=12, w=10),             # ragged tiles in m, n and k; dW splits cross images
     dict(n=2, c_in=16, c_out=8, h=8, w=8),                # single partial tile everywhere
