@@ -36,10 +36,16 @@ KERNELS = {
     "gemm_forward": (r"k_gemm_dl<.*DlFwd|k_gemm<.*FwdOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dw": (r"k_gemm_dl<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
-    "sample_backward": (r"k_sample_bwd<", ["deft_backward.hip", "deft_device.h"]),
+    "sample_backward": (r"k_sample_bwd<|k_sample_bwd_mf\b", ["deft_backward.hip", "deft_device.h"]),
     "sample_backward_miss": (r"k_sample_bwd_miss<", ["deft_backward.hip", "deft_device.h"]),
+    "sample_backward_list": (r"k_sample_bwd_list\b", ["deft_backward.hip", "deft_device.h"]),
     "offset_weight_backward": (r"k_woff_bwd<", ["deft_backward.hip", "deft_device.h"]),
     "dx_final": (r"k_dx_final<", ["deft_backward.hip", "deft_device.h"]),
+    "doff_sum": (r"k_doff_sum\b", ["deft_backward.hip"]),
+    "bias_partial": (r"k_bias_partial<", ["deft_backward.hip"]),
+    "reduce_final": (r"k_reduce_final<", ["deft_backward.hip"]),
+    "prep_backward": (r"k_prep_backward<", ["deft_backward.hip"]),
+    "prep_forward": (r"k_prep_forward<", ["deft_sample.hip"]),
 }
 
 
@@ -55,8 +61,6 @@ def source_hash(bench_name: str) -> str:
 def bench_name_of(symbol: str):
     s = symbol.replace("(anonymous namespace)::", "")
     for name, (pat, _) in KERNELS.items():
-        if name == "sample_backward" and "k_sample_bwd_miss" in s:
-            continue
         if re.search(pat, s):
             return name
     return None
