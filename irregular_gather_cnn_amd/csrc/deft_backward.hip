@@ -4,16 +4,19 @@
 // glance", "This paper's idea"), so the backward is the exact derivative of
 // the forward.  dCol = W^T dY and the pixel-range partials of dW = dY Col
 // run on the MFMA GEMMs (deft_gemm.hip, deft_gemm_dl.hip); this file holds
-//   k_sample_bwd   -- per (core tile of input pixels, offset group, channel
-//                     chunk): lists the (output pixel, tap) pairs whose
-//                     corners touch the core within the halo, then (lanes =
-//                     channels) scatters dCol x bilinear weight into a
-//                     fixed-point LDS copy of the core with integer LDS
-//                     atomics (64 consecutive addresses per atomic, order-
-//                     independent sums) and writes the core's dX once with
-//                     plain stores; the unique owner of each pair reduces
-//                     dOffset = the chunk's sum of dCol x the corner
-//                     differences into that chunk's partial.
+//   k_sample_bwd_list -- per (core tile of input pixels, offset group):
+//                     lists the (output pixel, tap) pairs whose corners
+//                     touch the core within the halo.
+//   k_sample_bwd_mf -- bf16, per (core, group, 64-channel chunk): dX of the
+//                     core as MFMA products of sparse bilinear-weight tiles
+//                     with the listed entries' dCol rows, summed over the
+//                     waves in a fixed order and written once; the unique
+//                     owner of each pair reduces dOffset over the chunk's
+//                     channels into that chunk's partial.
+//   k_sample_bwd   -- the same without MFMA (fp32, small chunks): lanes =
+//                     channels scatter dCol x weight into a fixed-point LDS
+//                     copy of the core with integer LDS atomics (order-
+//                     independent sums).
 //   k_sample_bwd_miss -- the rare taps beyond the halo: dOffset from global
 //                     memory, dX added with global atomics.
 //   k_woff_bwd     -- per (image, 32-channel slice, band of output rows):

@@ -19,8 +19,10 @@
 //     conflicts;
 //   * results whose output is contiguous along m leave through LDS: each wave
 //     transposes its 128x128 block there and writes whole 16-byte chunks.
-// 256 threads = 2x2 waves, 256x256 tile, 128x128 per wave (16 32x32x16 MFMA
-// blocks).  One workgroup per CU (136 KB of LDS).
+// 256 threads = 2x2 waves; the tile shape, ring depth and occupancy are set
+// per operation (GemmCfg): 256x256 tiles, 128x128 per wave (16 32x32x16 MFMA
+// blocks), one workgroup per CU for the forward and dW; 256x128 tiles, two per
+// CU, for dCol.
 #include "deft_device.h"
 #include "deft_internal.h"
 

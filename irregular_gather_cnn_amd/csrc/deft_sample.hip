@@ -16,6 +16,9 @@
 // gathers in on-chip memory; a halo sized from the offset distribution keeps
 // out-of-tile accesses rare.  The workgroup order is XCD-aware so tiles that
 // share halo rows run on the same XCD's L2 (the page's block-ID swizzle).
+// A second variant (k_sample_direct, bf16) reads every corner straight from a
+// channel-minor copy of the input held in the caches instead of an LDS halo;
+// its phase A stages only the footprint, by direct buffer-to-LDS loads.
 #include "deft_device.h"
 #include "deft_internal.h"
 
