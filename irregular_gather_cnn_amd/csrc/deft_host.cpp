@@ -447,7 +447,7 @@ int deft_forward(const deft_plan* p, const void* x, const void* w_off, const voi
   if (p->d.n == 0) return DEFT_OK;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  hipError_t e = deft::launch_prep_forward(*p, w, w_off, ws + p->ws_wt, ws + p->ws_woff, st);
+  hipError_t e = deft::launch_prep_forward(*p, w, w_off, ws + p->ws_wt, ws + p->ws_woff, x, ws + p->ws_xh, st);
   if (e != hipSuccess) return hip_fail(e);
   deft::SampleArgs a;
   a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_in = nullptr; a.off_out = offsets_out;

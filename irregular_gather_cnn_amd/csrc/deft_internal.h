@@ -60,8 +60,8 @@ struct SampleArgs {
   void* xh;                // direct gather: channel-minor copy of x (workspace)
 };
 
-hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt,
-                               void* woff_p, hipStream_t s);
+hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt, void* woff_p,
+                               const void* x, void* xh, hipStream_t s);
 hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hipStream_t s);
 hipError_t launch_sample_index(const deft_desc& d, int ho, int wo, const float* off, int32_t* y0,
                                int32_t* x0, uint8_t* mask, hipStream_t s);

@@ -599,10 +599,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // along the pixels, a register transpose with byte permutes, eight 16-byte
 // stores along the channels.  A wave covers 64 pixels x 64 channels, so both
 // the loads and the stores come in whole 128-byte runs.
-__global__ __launch_bounds__(256) void k_x_channel_minor(const bf16_t* __restrict__ x, bf16_t* __restrict__ xh,
-                                                         int Cin, int HW, int pgroups, int cgroups, int total_waves) {
+__device__ __forceinline__ void x_channel_minor_body(int bid, const bf16_t* __restrict__ x, bf16_t* __restrict__ xh,
+                                                     int Cin, int HW, int pgroups, int cgroups, int total_waves) {
   const int lane = threadIdx.x & 63;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = bid * 4 + (threadIdx.x >> 6);
   if (wv >= total_waves) return;
   const int cgi = wv % cgroups, r = wv / cgroups;
   const int pgi = r % pgroups, n = r / pgroups;
@@ -713,13 +713,13 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
 // channel L % 32 of the group, zero past 2 * taps; channels
 // chunk * CA + (L / 32) * CA / 2 + step * 8 ... + 7).
 template <typename T>
-__global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, const T* __restrict__ w_off,
-                                                      T* wt, T* woff_p, int Cout, int Cin, int K2, int Oc,
-                                                      int OcP, int G, int CA) {
+__device__ __forceinline__ void prep_forward_body(int bid, int nblocks, const T* __restrict__ w,
+                                                  const T* __restrict__ w_off, T* wt, T* woff_p, int Cout, int Cin,
+                                                  int K2, int Oc, int OcP, int G, int CA) {
   const size_t n1 = (size_t)Cout * K2 * Cin;
   const size_t n2 = CA > 0 ? (size_t)G * K2 * Cin * 32 : (size_t)OcP * K2 * Cin;
   const int nks = CA / 16, nch = CA > 0 ? Cin / CA : 1;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * 256) {
+  for (size_t e = (size_t)bid * 256 + threadIdx.x; e < n1 + n2; e += (size_t)nblocks * 256) {
     // weight tensors are far below 2^31 elements: 32-bit index arithmetic
     if (e < n1) {
       const int ei = (int)e;
@@ -744,6 +744,28 @@ __global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, c
       woff_p[f] = o < Oc ? w_off[(o * Cin + c) * K2 + t] : zero_elem<T>();
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep_forward(const T* __restrict__ w, const T* __restrict__ w_off,
+                                                      T* wt, T* woff_p, int Cout, int Cin, int K2, int Oc,
+                                                      int OcP, int G, int CA) {
+  prep_forward_body<T>(blockIdx.x, gridDim.x, w, w_off, wt, woff_p, Cout, Cin, K2, Oc, OcP, G, CA);
+}
+
+// The direct-gather forward's prologue in one launch: the first nxb
+// workgroups build the channel-minor copy of x, the rest lay out the weights.
+__global__ __launch_bounds__(256) void k_x_channel_minor_prep(const bf16_t* __restrict__ x, bf16_t* __restrict__ xh,
+                                                              int Cin, int HW, int pgroups, int cgroups,
+                                                              int total_waves, int nxb, const bf16_t* __restrict__ w,
+                                                              const bf16_t* __restrict__ w_off, bf16_t* wt,
+                                                              bf16_t* woff_p, int Cout, int K2, int Oc, int OcP, int G,
+                                                              int CA) {
+  if ((int)blockIdx.x < nxb)
+    x_channel_minor_body(blockIdx.x, x, xh, Cin, HW, pgroups, cgroups, total_waves);
+  else
+    prep_forward_body<bf16_t>(blockIdx.x - nxb, gridDim.x - nxb, w, w_off, wt, woff_p, Cout, Cin, K2, Oc, OcP, G,
+                              CA);
 }
 
 // ---------------------------------------------------------------------------
@@ -806,14 +828,7 @@ hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hi
   SampleParams s = make_params(p, a);
   if (p.num_wg == 0) return hipSuccess;
   if (p.direct && fused) {
-    // channel-minor copy of x with a zero pixel per image, then the gather
-    const int HW = p.d.h * p.d.w;
-    const int pgroups = (HW + 1 + 63) / 64, cgroups = (p.d.c_in + 63) / 64;
-    const int waves = p.d.n * pgroups * cgroups;
-    DEFT_LAUNCH("x_channel_minor", k_x_channel_minor, dim3((waves + 3) / 4), dim3(256), 0, st,
-                (const bf16_t*)a.x, (bf16_t*)a.xh, p.d.c_in, HW, pgroups, cgroups, waves);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the gather from the channel-minor copy (built by the prologue launch)
     s.xh = (const bf16_t*)a.xh;
     int l = 0;
     while ((1 << l) < p.cg / 8) ++l;
@@ -862,13 +877,22 @@ hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off
 }
 
 hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt,
-                               void* woff_p, hipStream_t st) {
+                               void* woff_p, const void* x, void* xh, hipStream_t st) {
   const deft_desc& d = p.d;
   const int ca = p.direct ? p.chunk_a : 0;
   const size_t total = (size_t)d.c_out * p.taps * d.c_in +
                        (ca ? (size_t)d.offset_groups * p.taps * d.c_in * 32 : (size_t)p.oc_pad * p.taps * d.c_in);
   unsigned g = grid_for(total);
   if (g > 4096) g = 4096;
+  if (p.direct) {
+    const int HW = d.h * d.w;
+    const int pgroups = (HW + 1 + 63) / 64, cgroups = (d.c_in + 63) / 64;
+    const int waves = d.n * pgroups * cgroups, nxb = (waves + 3) / 4;
+    DEFT_LAUNCH("x_channel_minor", k_x_channel_minor_prep, dim3(nxb + g), dim3(256), 0, st, (const bf16_t*)x,
+                (bf16_t*)xh, d.c_in, HW, pgroups, cgroups, waves, nxb, (const bf16_t*)w, (const bf16_t*)w_off,
+                (bf16_t*)wt, (bf16_t*)woff_p, d.c_out, p.taps, p.oc, p.oc_pad, d.offset_groups, ca);
+    return hipGetLastError();
+  }
   if (d.dtype == DEFT_BF16)
     DEFT_LAUNCH("prep_forward", k_prep_forward<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)w,
                        (const bf16_t*)w_off, (bf16_t*)wt, (bf16_t*)woff_p, d.c_out, d.c_in, p.taps, p.oc,
