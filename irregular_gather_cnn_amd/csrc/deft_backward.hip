@@ -4,9 +4,10 @@
 // glance", "This paper's idea"), so the backward is the exact derivative of
 // the forward.  dCol = W^T dY and the pixel-range partials of dW = dY Col
 // run on the MFMA GEMMs (deft_gemm.hip, deft_gemm_dl.hip); this file holds
-//   k_sample_bwd_list -- per (core tile of input pixels, offset group):
-//                     lists the (output pixel, tap) pairs whose corners
-//                     touch the core within the halo.
+//   k_prep_backward -- one launch: per (core tile of input pixels, offset
+//                     group) the list of (output pixel, tap) pairs whose
+//                     corners touch the core within the halo; dY sums for db;
+//                     W2 / W_off^T layouts; zeroing.
 //   k_sample_bwd_mf -- bf16, per (core, group, 64-channel chunk): dX of the
 //                     core as MFMA products of sparse bilinear-weight tiles
 //                     with the listed entries' dCol rows, summed over the
@@ -25,8 +26,9 @@
 //   k_dx_final     -- per 64 input pixels x 256 channels: dX_offset, the
 //                     transposed offset convolution (MFMA), plus the sampling
 //                     part of dX; rounded once.
-//   k_bias_partial, k_reduce_final -- per-image bias sums, then one fixed-order
-//                     reduction of all partials to dW, dW_off, db, db_off.
+//   k_doff_sum     -- dOffset from the per-chunk partials, and db_off sums.
+//   k_reduce_final -- one fixed-order reduction of all partials to dW,
+//                     dW_off, db, db_off.
 // Global atomics are avoided on every hot path: on gfx950 they run far below
 // the bandwidth of plain stores.
 #include <type_traits>
@@ -139,11 +141,12 @@ __device__ __forceinline__ void doffset_owned(const int4 cur, int nb, int lane, 
 
 // The (output pixel, tap) pairs whose corners touch one core tile of input
 // pixels (for one offset group), written to that core's list; shared by the
-// core's channel-chunk workgroups of k_sample_bwd.
-__global__ __launch_bounds__(256) void k_sample_bwd_list(const BwdParams p) {
+// core's channel-chunk workgroups of the sampling backward.  Runs inside the
+// backward's preparation launch (its first num_tg workgroups).
+__device__ __forceinline__ void sample_bwd_list(const BwdParams& p, int bid) {
   __shared__ int tabs[4 + 48 * 3 + 49 + 96];
   const int tid = threadIdx.x;
-  const int tg = xcd_swizzle(blockIdx.x, p.num_tg);
+  const int tg = xcd_swizzle(bid, p.num_tg);
   const int tile = tg / p.G, g = tg - tile * p.G;
   const int tpi = p.bt_h * p.bt_w;
   const int n = tile / tpi, trem = tile - n * tpi;
@@ -687,12 +690,41 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
 }
 
 // dOffset = sum of the per-chunk partials, in chunk order.
-__global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part, float* doff, size_t n, int chunks) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    float v = part[i];
-    for (int k = 1; k < chunks; ++k) v += part[(size_t)k * n + i];
-    doff[i] = v;
+// dOffset = the sum of the per-chunk partials, one workgroup per (offset
+// channel, image) plane, which also leaves that plane's sum as the db_off
+// partial bpart[(Cout + o) * N + n].
+__global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part, float* doff, size_t n, int chunks,
+                                                  int Oc, int N, int HoWo, int Cout, float* bpart) {
+  __shared__ float red[256];
+  const int o = blockIdx.x, img = blockIdx.y;
+  const size_t base = ((size_t)img * Oc + o) * HoWo;
+  float s = 0.f;
+  if ((HoWo & 3) == 0 && (n & 3) == 0) {
+    // four pixels per thread per pass; each chunk's partial one 16-byte load
+    for (int q = threadIdx.x * 4; q < HoWo; q += 256 * 4) {
+      float4 v = *(const float4*)(part + base + q);
+      for (int k = 1; k < chunks; ++k) {
+        const float4 u = *(const float4*)(part + (size_t)k * n + base + q);
+        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+      }
+      *(float4*)(doff + base + q) = v;
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+  } else {
+    for (int q = threadIdx.x; q < HoWo; q += 256) {
+      float v = part[base + q];
+      for (int k = 1; k < chunks; ++k) v += part[(size_t)k * n + base + q];
+      doff[base + q] = v;
+      s += v;
+    }
   }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bpart[(size_t)(Cout + o) * N + img] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -999,13 +1031,13 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
 // Prep: W2[(t,c)][co] = W[co][c][t]; WoffT[c][o*K2+t] = W_off[o][c][t] (zero
 // for kk >= Oc*K2); the nz0 floats at z0 zeroed.
 template <typename T>
-__global__ __launch_bounds__(256) void k_prep_backward(const T* __restrict__ w, const T* __restrict__ w_off, T* w2,
-                                                       T* wofft, float* z0, size_t nz0, int Cout, int Cin, int K2,
-                                                       int Oc, int KKP) {
+__device__ __forceinline__ void prep_backward_body(int bid, int nblocks, const T* __restrict__ w,
+                                                   const T* __restrict__ w_off, T* w2, T* wofft, float* z0,
+                                                   size_t nz0, int Cout, int Cin, int K2, int Oc, int KKP) {
   const size_t n1 = (size_t)Cout * K2 * Cin, n2 = (size_t)Cin * KKP;
   const size_t nz4 = nz0 / 4;
   const size_t total = n1 + n2 + nz4 + (nz0 & 3);
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+  for (size_t e = (size_t)bid * 256 + threadIdx.x; e < total; e += (size_t)nblocks * 256) {
     // weight tensors are far below 2^31 elements: 32-bit index arithmetic
     if (e < n1) {
       const int ei = (int)e;
@@ -1027,28 +1059,22 @@ __global__ __launch_bounds__(256) void k_prep_backward(const T* __restrict__ w, 
 
 // Per-(channel, image) sums: part[ch][n] = sum over pixels of dY (ch < Cout)
 // or of dOffset (ch >= Cout).  Fixed-order tree reduction.
+// Sum of dY over the pixels of one (output channel, image): bias partial
+// part[ch * N + n] (16-byte loads for bf16 when the plane allows).
 template <typename T>
-__global__ __launch_bounds__(256) void k_bias_partial(const T* __restrict__ dy, const float* __restrict__ doff,
-                                                      float* part, int Cout, int Oc, int N, int HoWo) {
+__device__ __forceinline__ void bias_dy_body(const T* __restrict__ dy, float* part, int Cout, int N, int HoWo, int ch,
+                                             int n) {
   __shared__ float red[256];
-  const int ch = blockIdx.x, n = blockIdx.y;
-  const bool main = ch < Cout;
-  const int o = main ? ch : ch - Cout;
-  const size_t base = ((size_t)n * (main ? Cout : Oc) + o) * HoWo;
+  const size_t base = ((size_t)n * Cout + ch) * HoWo;
   float s = 0.f;
-  if (main && sizeof(T) == 2 && (HoWo & 7) == 0) {  // 16-byte loads of eight bf16
+  if (sizeof(T) == 2 && (HoWo & 7) == 0) {
     for (int q = threadIdx.x * 8; q < HoWo; q += 256 * 8) {
       float f[8];
       unpack8(*(const uint4*)((const bf16_t*)dy + base + q), f);
       s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
     }
-  } else if (!main && (HoWo & 3) == 0) {
-    for (int q = threadIdx.x * 4; q < HoWo; q += 256 * 4) {
-      const float4 v = *(const float4*)(doff + base + q);
-      s += (v.x + v.y) + (v.z + v.w);
-    }
   } else {
-    for (int q = threadIdx.x; q < HoWo; q += 256) s += main ? Elem<T>::to_f32(dy[base + q]) : doff[base + q];
+    for (int q = threadIdx.x; q < HoWo; q += 256) s += Elem<T>::to_f32(dy[base + q]);
   }
   red[threadIdx.x] = s;
   __syncthreads();
@@ -1057,6 +1083,26 @@ __global__ __launch_bounds__(256) void k_bias_partial(const T* __restrict__ dy, 
     __syncthreads();
   }
   if (threadIdx.x == 0) part[(size_t)ch * N + n] = red[0];
+}
+
+// The backward's preparation in one launch: workgroups [0, num_tg) build the
+// candidate lists, the next Cout*N sum dY per (channel, image), the rest lay
+// out W2 and W_off^T and zero the dOffset partials and the max word.
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep_backward(const BwdParams b, const T* __restrict__ w,
+                                                       const T* __restrict__ w_off, T* w2, T* wofft, float* z0,
+                                                       size_t nz0, int Cout, int Cin, int K2, int Oc, int KKP,
+                                                       const T* __restrict__ dy, float* bpart, int N, int HoWo) {
+  const int bid = blockIdx.x;
+  if (bid < b.num_tg) {
+    sample_bwd_list(b, bid);
+  } else if (bid < b.num_tg + Cout * N) {
+    const int r = bid - b.num_tg;
+    bias_dy_body<T>(dy, bpart, Cout, N, HoWo, r % Cout, r / Cout);
+  } else {
+    const int base = b.num_tg + Cout * N;
+    prep_backward_body<T>(bid - base, gridDim.x - base, w, w_off, w2, wofft, z0, nz0, Cout, Cin, K2, Oc, KKP);
+  }
 }
 
 // All weight and bias gradients from their partials, summed in a fixed order
@@ -1128,13 +1174,32 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   float* bpart = (float*)(ws + p.ws_biaspart);
   const size_t ndoff = (size_t)d.n * p.oc * p.ho * p.wo;
   hipError_t e;
+  BwdParams b;
+  b.N = d.n; b.Cin = d.c_in; b.H = d.h; b.W = d.w; b.Ho = p.ho; b.Wo = p.wo; b.KH = d.kh; b.KW = d.kw;
+  b.SH = d.stride_h; b.SW = d.stride_w; b.PH = d.pad_h; b.PW = d.pad_w; b.DH = d.dil_h; b.DW = d.dil_w;
+  b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck;
+  b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
+  b.CC = p.chunk_b;
+  b.dcstr = p.chunk_b + (p.bwd_mf ? 16 : (d.dtype == DEFT_BF16 ? 8 : 4));
+  b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;
+  int cb = 0;
+  while ((1 << cb) < p.list_cap + 1) ++cb;
+  b.capbits = cb;
+  b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
+  b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
+  b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
+  b.lists = lists;
+  b.num_tg = p.num_btiles * d.offset_groups;
+  b.counts = (int*)(ws + p.ws_lcount);
   {
-    // zero: the dOffset partials (fully outside taps keep 0) and the max |dCol|
-    // word that follows them
+    // candidate lists, dY bias sums, W2 / W_off^T, and zero: the dOffset
+    // partials (fully outside taps keep 0) and the max |dCol| word after them
     const size_t nz = ndoff * (size_t)(p.cg / p.chunk_b) + 4;
     const size_t total = (size_t)d.c_out * p.ck + (size_t)d.c_in * p.kk_pad + nz / 4 + 4;
-    DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid_cap(total, 8192)), dim3(256), 0, st,
-                (const T*)a.w, (const T*)a.w_off, w2, wofft, doffp, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad);
+    const unsigned grid = (unsigned)b.num_tg + (unsigned)(d.c_out * d.n) + grid_cap(total, 8192);
+    DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid), dim3(256), 0, st, b, (const T*)a.w,
+                (const T*)a.w_off, w2, wofft, doffp, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad, (const T*)a.dy,
+                bpart, d.n, p.ho * p.wo);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1145,26 +1210,6 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
 
   // sampling backward, the taps beyond the halo, then dOffset
   {
-    BwdParams b;
-    b.N = d.n; b.Cin = d.c_in; b.H = d.h; b.W = d.w; b.Ho = p.ho; b.Wo = p.wo; b.KH = d.kh; b.KW = d.kw;
-    b.SH = d.stride_h; b.SW = d.stride_w; b.PH = d.pad_h; b.PW = d.pad_w; b.DH = d.dil_h; b.DW = d.dil_w;
-    b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck;
-    b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
-    b.CC = p.chunk_b;
-    b.dcstr = p.chunk_b + (p.bwd_mf ? 16 : (d.dtype == DEFT_BF16 ? 8 : 4));
-    b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;
-    int cb = 0;
-    while ((1 << cb) < p.list_cap + 1) ++cb;
-    b.capbits = cb;
-    b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
-    b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
-    b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
-    b.lists = lists;
-    b.num_tg = p.num_btiles * d.offset_groups;
-    b.counts = (int*)(ws + p.ws_lcount);
-    if (b.num_tg) DEFT_LAUNCH("sample_backward_list", k_sample_bwd_list, dim3(b.num_tg), dim3(256), 0, st, b);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     auto kern = p.bwd_mf ? k_sample_bwd_mf : k_sample_bwd<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
     if (e != hipSuccess) return e;
@@ -1176,7 +1221,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = p.cg / p.chunk_b;
-    DEFT_LAUNCH("doff_sum", k_doff_sum, dim3(grid_cap(ndoff, 2048)), dim3(256), 0, st, doffp, doff, ndoff, chunks);
+    DEFT_LAUNCH("doff_sum", k_doff_sum, dim3(p.oc, d.n), dim3(256), 0, st, doffp, doff, ndoff, chunks, p.oc, d.n,
+                p.ho * p.wo, d.c_out, bpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1244,8 +1290,6 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   }
   // bias partials, then every weight / bias gradient
   {
-    DEFT_LAUNCH("bias_partial", k_bias_partial<T>, dim3(d.c_out + p.oc, d.n), dim3(256), 0, st, (const T*)a.dy, doff,
-                bpart, d.c_out, p.oc, d.n, p.ho * p.wo);
     const size_t total = ((size_t)d.c_out + p.oc) * p.ck + d.c_out + p.oc;
     DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dwpart, p.dw_splits, (T*)a.dw,
                 d.c_out, dwoffpart, (T*)a.dw_off, p.oc, d.n * p.woff_bands, bpart, (T*)a.db, (T*)a.db_off, d.n,
