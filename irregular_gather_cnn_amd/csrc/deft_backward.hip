@@ -55,6 +55,7 @@ struct BwdParams {
   int4* lists;   // [num_tg][list_cap]: one list per (core, group)
   int* counts;   // [num_tg]: entries in each list
   int num_tg;    // cores x groups
+  const bf16_t* xh;  // channel-minor copy of x left by a direct-gather forward, or null
 };
 
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
@@ -457,8 +458,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int c0 = chunk * p.CC;
   const int cglob = g * p.Cg + c0;
   float* doffp = p.doffp + (size_t)chunk * pstride + ((size_t)n * p.Oc + obase) * HoWo;
-  stage_region<bf16_t>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
-  __syncthreads();
+  // The input region around the core is needed only by dOffset.  From the
+  // channel-minor copy (direct-gather forward) it is copied by buffer-to-LDS
+  // loads issued here and awaited just before the first dOffset, so the copy
+  // overlaps the first block's loads and MFMAs; otherwise it is staged now.
+  bool x_ready = true;
+  if (p.xh) {
+    const int HWi = p.H * p.W;
+    const rsrc_t xr = make_rsrc(p.xh + (size_t)n * (HWi + 1) * p.Cin, (uint32_t)((size_t)(HWi + 1) * p.Cin * 2));
+    const int pps = p.xstr >> 3;  // 16-byte slots per staged pixel (the last ones padding)
+    const int nslots = (p.CH + 2) * XW * pps;
+    for (int s0 = wave * 64; s0 < nslots; s0 += 256) {
+      const int sl = s0 + lane, px = sl / pps, pc = sl - px * pps;
+      const int ry = px / XW, rx = px - ry * XW;
+      const int y = Y0 - 1 + ry, xx = X0 - 1 + rx;
+      const int pix = ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) ? y * p.W + xx : HWi;
+      const int voff = pc * 8 < p.CC ? (pix * p.Cin + cglob + pc * 8) * 2 : kOOB;
+      if (sl < nslots) load_lds16(xr, (unsigned char*)xl + s0 * 16, voff);  // lanes past the region write nothing
+    }
+    x_ready = false;
+  } else {
+    stage_region<bf16_t>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
+    __syncthreads();
+  }
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -564,8 +586,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
       }
     }
+    if (!x_ready) {  // every wave passes this barrier once (below if it has no block)
+      wait_vm<0>();
+      __syncthreads();
+      x_ready = true;
+    }
     doffset_owned<bf16_t>(cur, nb, lane, dst, p.dcstr, xl, p.xstr, XW, p.CC, HoWo, doffp);
     __builtin_amdgcn_wave_barrier();
+  }
+  if (!x_ready) {
+    wait_vm<0>();
+    __syncthreads();
   }
   // the four waves' partial sums, added in a fixed order: waves 0 and 1
   // store theirs ([channel][pixel], two regions), waves 2 and 3 add them to
@@ -1189,6 +1220,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
   b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
   b.lists = lists;
+  b.xh = (p.direct && p.bwd_mf) ? (const bf16_t*)(ws + p.ws_xh) : nullptr;
   b.num_tg = p.num_btiles * d.offset_groups;
   b.counts = (int*)(ws + p.ws_lcount);
   {
