@@ -770,6 +770,7 @@ struct WoffParams {
   const void* x;
   const float* doff;
   float* part;  // [N*bands][Oc][K2][Cin]
+  const bf16_t* xh;  // channel-minor copy of x left by a direct-gather forward, or null
 };
 
 // dW_off partial of one (image, 32-channel slice, band of output rows): a
@@ -802,9 +803,26 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   constexpr bool kHwc = sizeof(T) == 2;
   if constexpr (kHwc) {
     const int nc = min(32, p.Cin - cs * 32);
-    const FastDiv drh = make_fastdiv(p.XR);
-    const StageGeom sg = stage_geom<T>(p.W, -p.PW, p.XS, (size_t)p.Cin * p.H * p.W);
-    stage_region<T>(xs, x, p.Cin, p.H, p.W, n, cs * 32, nc, y0, -p.PW, p.XR, p.XS, drh, sg, 32);
+    if (p.xh) {
+      // from the channel-minor copy: buffer-to-LDS loads of 16-byte pieces
+      // (4 per staged pixel), awaited after the dOffset rows are staged
+      const int HWi = p.H * p.W;
+      const rsrc_t xr = make_rsrc(p.xh + (size_t)n * (HWi + 1) * p.Cin, (uint32_t)((size_t)(HWi + 1) * p.Cin * 2));
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int nslots = p.XR * p.XS * 4;
+      for (int s0 = wv * 64; s0 < nslots; s0 += 256) {
+        const int sl = s0 + lane, px = sl >> 2, pc = sl & 3;
+        const int ry = px / p.XS, rx = px - ry * p.XS;
+        const int y = y0 + ry, xx = rx - p.PW;
+        const int pix = ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) ? y * p.W + xx : HWi;
+        const int voff = pc * 8 < nc ? (pix * p.Cin + cs * 32 + pc * 8) * 2 : kOOB;
+        if (sl < nslots) load_lds16(xr, (unsigned char*)xs + s0 * 16, voff);  // lanes past the region write nothing
+      }
+    } else {
+      const FastDiv drh = make_fastdiv(p.XR);
+      const StageGeom sg = stage_geom<T>(p.W, -p.PW, p.XS, (size_t)p.Cin * p.H * p.W);
+      stage_region<T>(xs, x, p.Cin, p.H, p.W, n, cs * 32, nc, y0, -p.PW, p.XR, p.XS, drh, sg, 32);
+    }
   } else {
     const int tot = 32 * p.XR * p.XS;
     for (int e = tid; e < tot; e += 256) {
@@ -861,6 +879,7 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
         if (e0 + u * 256 < tot) dl[e0 + u * 256] = Elem<T>::from_f32(v[u]);
     }
   }
+  if (kHwc && p.xh) wait_vm<0>();
   __syncthreads();
   // ---- taps in groups of 12 (three per wave) ----
   for (int tg = 0; tg < p.K2; tg += 12) {
@@ -1277,6 +1296,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     w.XS = span;  // pixels per staged row, from x = -PW
     w.DLS = w.WoP + (d.dtype == DEFT_BF16 ? 8 : 4);
     w.x = a.x; w.doff = doff; w.part = dwoffpart;
+    w.xh = p.direct ? (const bf16_t*)(ws + p.ws_xh) : nullptr;
     for (int o0 = 0; o0 < p.oc && w.num_wg; o0 += 96) {
       w.o0 = o0;
       w.orows = p.oc - o0 < 96 ? p.oc - o0 : 96;
