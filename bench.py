@@ -183,6 +183,35 @@ def main():
     if dom in tr and tr[dom][1] == profiling.source_hash(dom):
         roof["traffic"] = tr[dom][0]
 
+    # The fused forward against the unfused three-operator forward (offset conv
+    # -> offsets through HBM -> sampling -> GEMM) on the same plan and inputs:
+    # what fusing the offset convolution into the sampling kernel buys here.
+    def time_forward(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b_.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / args.steps
+
+    fused_fn = lambda: layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
+    unfused_fn = lambda: layer.forward_unfused(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
+    fusion = {"fused_fwd_ms": round(time_forward(fused_fn), 4), "unfused_fwd_ms": round(time_forward(unfused_fn), 4)}
+    L.deft_timing_start(8 * args.steps)
+    for _ in range(args.steps):
+        unfused_fn()
+    L.deft_timing_stop()
+    un = {}
+    for i in range(L.deft_timing_count()):
+        name, ms = L.deft_timing_get(i)
+        un.setdefault(name, []).append(ms)
+    fusion["unfused_kernels_ms"] = {k: round(sum(v) / len(v), 5) for k, v in un.items()}
+    log("fusion: %s" % fusion)
+
     total_flop = sum(f for k, (b_, f) in work.items())
     gflops = total_flop / (ms_step * 1e-3) / 1e9
 
@@ -218,6 +247,7 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
+        "fusion": fusion,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

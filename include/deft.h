@@ -136,6 +136,19 @@ int deft_forward(const deft_plan* p, const void* x, const void* w_off, const voi
                  const void* w, const void* b, void* y, float* offsets_out, void* workspace,
                  size_t ws_bytes, void* stream);
 
+/* The same forward in the unfused three-operator form the DefT explainer page
+ * compares against ("What people did before this paper", "The argument in one
+ * glance"): an offset-convolution launch writes the offsets to HBM
+ * (`offsets`, fp32 [N][Oc][Ho][Wo], required), a sampling launch reads them
+ * back with the input and writes the deformed columns, then the GEMM.  Same
+ * arguments, checks and error codes as deft_forward, plus DEFT_ERR_NULLPTR
+ * when `offsets` is NULL.  y, offsets and the columns left in the workspace
+ * are bit-identical to deft_forward's with the same plan (same arithmetic in
+ * the same order), so deft_backward may follow it. */
+int deft_forward_unfused(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
+                         const void* w, const void* b, void* y, float* offsets, void* workspace,
+                         size_t ws_bytes, void* stream);
+
 /* Backward of the forward that last ran on this workspace (it must have been
  * sized with training = 1 and the forward must have written offsets_out,
  * passed here as `offsets`).  dy [N][Cout][Ho][Wo].  Writes (overwrites) dx,

@@ -433,31 +433,53 @@ size_t deft_workspace_bytes(const deft_plan* p, int training) {
   return training ? p->ws_train_end : p->ws_fwd_end;
 }
 
-int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
-                 const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream) {
+// The forward in the fused form (one sampling launch computes the offsets and
+// the columns) or in the unfused three-operator form (offset conv -> offsets
+// in HBM -> sampling -> GEMM), which needs the offsets buffer.
+static int forward_impl(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
+                        const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream,
+                        bool fused) {
   if (!p) return DEFT_ERR_NULLPTR;
   if (p->d.n == 0) return DEFT_OK;  // empty batch: nothing is read or written
   if (!x || !w_off || !w || !y) return DEFT_ERR_NULLPTR;
+  if (!fused && !offsets_out) return DEFT_ERR_NULLPTR;
   if (!workspace || ws_bytes < p->ws_fwd_end) return DEFT_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(w_off) || !aligned16(w) || !aligned16(y) || !aligned16(workspace) ||
       (offsets_out && !aligned16(offsets_out)))
     return DEFT_ERR_ALIGN;
   const size_t esz = p->d.dtype == DEFT_BF16 ? 2 : 4;
   if (((uintptr_t)b_off % esz) || ((uintptr_t)b % esz)) return DEFT_ERR_ALIGN;
-  if (p->d.n == 0) return DEFT_OK;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   hipError_t e = deft::launch_prep_forward(*p, w, w_off, ws + p->ws_wt, ws + p->ws_woff, x, ws + p->ws_xh, st);
   if (e != hipSuccess) return hip_fail(e);
   deft::SampleArgs a;
-  a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_in = nullptr; a.off_out = offsets_out;
+  a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_out = offsets_out;
   a.cols = ws + p->ws_cols;
-  a.xh = ws + p->ws_xh;
-  e = deft::launch_sample(*p, true, a, st);
+  a.xh = p->direct ? ws + p->ws_xh : nullptr;
+  if (fused) {
+    e = deft::launch_sample(*p, deft::kFusedMode, a, st);
+  } else {
+    e = deft::launch_sample(*p, deft::kOffsetsMode, a, st);
+    if (e != hipSuccess) return hip_fail(e);
+    a.off_out = nullptr;
+    a.off_in = offsets_out;
+    e = deft::launch_sample(*p, deft::kSampleMode, a, st);
+  }
   if (e != hipSuccess) return hip_fail(e);
   e = deft::launch_gemm_forward(*p, ws + p->ws_wt, ws + p->ws_cols, b, y, st);
   if (e != hipSuccess) return hip_fail(e);
   return DEFT_OK;
+}
+
+int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
+                 const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(p, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, stream, true);
+}
+
+int deft_forward_unfused(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
+                         const void* b, void* y, float* offsets, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(p, x, w_off, b_off, w, b, y, offsets, workspace, ws_bytes, stream, false);
 }
 
 int deft_backward(const deft_plan* p, const void* x, const void* w_off, const void* w, const float* offsets,
@@ -510,10 +532,10 @@ int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, v
     for (int c = 64; c >= 16 && !ok; c /= 2)
       if (p->cg % c == 0) ok = layout_plan(q, p->tile_h, p->tile_w, p->halo, c);
     if (!ok) return DEFT_ERR_PLAN;
-    const hipError_t e = deft::launch_sample(q, false, a, (hipStream_t)stream);
+    const hipError_t e = deft::launch_sample(q, deft::kSampleMode, a, (hipStream_t)stream);
     return e == hipSuccess ? DEFT_OK : hip_fail(e);
   }
-  const hipError_t e = deft::launch_sample(*p, false, a, (hipStream_t)stream);
+  const hipError_t e = deft::launch_sample(*p, deft::kSampleMode, a, (hipStream_t)stream);
   return e == hipSuccess ? DEFT_OK : hip_fail(e);
 }
 

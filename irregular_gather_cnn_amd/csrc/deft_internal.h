@@ -51,18 +51,21 @@ void timing_after(hipStream_t s);
   } while (0)
 
 struct SampleArgs {
-  const void* x;
-  const void* woff_p;      // prepared offset-conv weight [oc_pad][taps][Cin]
-  const void* b_off;       // nullable, dtype
-  const float* off_in;     // unfused: offsets to sample from
-  float* off_out;          // nullable
-  void* cols;              // [N*Ho*Wo][taps][Cin]
-  void* xh;                // direct gather: channel-minor copy of x (workspace)
+  const void* x = nullptr;
+  const void* woff_p = nullptr;   // prepared offset-conv weight [oc_pad][taps][Cin]
+  const void* b_off = nullptr;    // nullable, dtype
+  const float* off_in = nullptr;  // sampling alone: offsets to sample from
+  float* off_out = nullptr;       // nullable
+  void* cols = nullptr;           // [N*Ho*Wo][taps][Cin]
+  void* xh = nullptr;             // direct gather: channel-minor copy of x (workspace)
 };
 
 hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt, void* woff_p,
                                const void* x, void* xh, hipStream_t s);
-hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hipStream_t s);
+// What a sampling launch computes: the fused offset conv + sampling, the
+// offset conv alone (offsets to off_out), or the sampling alone from off_in.
+enum SampleMode { kFusedMode = 0, kOffsetsMode = 1, kSampleMode = 2 };
+hipError_t launch_sample(const deft_plan& p, SampleMode mode, const SampleArgs& a, hipStream_t s);
 hipError_t launch_sample_index(const deft_desc& d, int ho, int wo, const float* off, int32_t* y0,
                                int32_t* x0, uint8_t* mask, hipStream_t s);
 hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off, uint32_t* hist,

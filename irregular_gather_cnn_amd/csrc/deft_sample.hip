@@ -38,6 +38,7 @@ struct SampleParams {
   void* cols;
   const bf16_t* xh;  // direct path: x channel-minor [N][H*W+1][Cin], pixel H*W = 0
   int nv_log;        // direct path: log2(Cg / 8)
+  int offsets_only;  // 1: stop after the offset convolution (offsets written to off_out)
   int stage_d;       // direct path: footprint-staging loads per wave per chunk
   FastDiv div_fw;
 };
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       if (p.off_out && ty < thn && tx < twn)
         p.off_out[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx] = v;
     }
+    if (p.offsets_only) return;  // uniform: the whole workgroup leaves together
   } else {
     const int tot = ocw * PT;
     for (int e = tid; e < tot; e += 256) {
@@ -363,7 +365,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // offset conv reads its MFMA operand fragments from the same copy.  Out-of-
 // image corners read the copy's extra zero pixel, so fully outside taps blend
 // to zero without a special case.
-template <int MB>
+// MODE: kFusedMode (offset conv + sampling), kOffsetsMode (offset conv only,
+// offsets to off_out), kSampleMode (sampling from offsets read from off_in).
+template <int MB, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_direct(const SampleParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -386,8 +390,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const bf16_t* __restrict__ xn = p.xh + (size_t)n * (HW + 1) * p.Cin;
   const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
 
+  if constexpr (MODE == kSampleMode) {
+    // offsets of this tile from global memory (the unfused formulation)
+    const int tot = ocw * PT;
+    for (int e = tid; e < tot; e += 256) {
+      const int o = e / PT, pix = e - o * PT;
+      const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
+      float v = 0.f;
+      if (ty < thn && tx < twn)
+        v = p.off_in[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx];
+      off_l[e] = v;
+    }
+    __syncthreads();
+  } else {
   // ---- phase A: offsets of this tile, operand fragments from the copy ----
-  {
     f32x16_t acc[MB][2];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -523,6 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       if (p.off_out && ty < thn && tx < twn)
         p.off_out[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx] = v;
     }
+    if constexpr (MODE == kOffsetsMode) return;
     __syncthreads();
   }
 
@@ -790,54 +807,61 @@ static SampleParams make_params(const deft_plan& p, const SampleArgs& a) {
   s.stage_d = p.stage_d;
   s.xh = nullptr;
   s.nv_log = 0;
+  s.offsets_only = 0;
   s.x = a.x; s.woff_p = a.woff_p; s.b_off = a.b_off; s.off_in = a.off_in; s.off_out = a.off_out;
   s.cols = a.cols;
   return s;
 }
 
 template <typename T, bool FUSED, int MB>
-static hipError_t launch_sample_t(const deft_plan& p, const SampleParams& s, hipStream_t st) {
+static hipError_t launch_sample_t(const deft_plan& p, const SampleParams& s, const char* name, hipStream_t st) {
   auto kern = k_sample<T, FUSED, MB>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
   if (e != hipSuccess) return e;
-  DEFT_LAUNCH(FUSED ? "fused_offset_sample" : "sample_only", kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
+  DEFT_LAUNCH(name, kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_sample_dt(const deft_plan& p, bool fused, const SampleParams& s, hipStream_t st) {
-  if (!fused) return launch_sample_t<T, false, 1>(p, s, st);
+static hipError_t launch_sample_dt(const deft_plan& p, SampleMode mode, const SampleParams& s, hipStream_t st) {
+  if (mode == kSampleMode) return launch_sample_t<T, false, 1>(p, s, "sample_only", st);
+  const char* name = mode == kOffsetsMode ? "offset_conv" : "fused_offset_sample";
   switch (p.mblocks) {
-    case 1: return launch_sample_t<T, true, 1>(p, s, st);
-    case 2: return launch_sample_t<T, true, 2>(p, s, st);
-    case 3: return launch_sample_t<T, true, 3>(p, s, st);
+    case 1: return launch_sample_t<T, true, 1>(p, s, name, st);
+    case 2: return launch_sample_t<T, true, 2>(p, s, name, st);
+    case 3: return launch_sample_t<T, true, 3>(p, s, name, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int MB>
-static hipError_t launch_direct_t(const deft_plan& p, const SampleParams& s, hipStream_t st) {
-  auto kern = k_sample_direct<MB>;
+template <int MODE>
+static hipError_t launch_direct_t(const deft_plan& p, const SampleParams& s, const char* name, hipStream_t st) {
+  auto kern = k_sample_direct<1, MODE>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
   if (e != hipSuccess) return e;
-  DEFT_LAUNCH("fused_offset_sample", kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
+  DEFT_LAUNCH(name, kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
   return hipGetLastError();
 }
 
-hipError_t launch_sample(const deft_plan& p, bool fused, const SampleArgs& a, hipStream_t st) {
+hipError_t launch_sample(const deft_plan& p, SampleMode mode, const SampleArgs& a, hipStream_t st) {
   SampleParams s = make_params(p, a);
+  s.offsets_only = mode == kOffsetsMode;
   if (p.num_wg == 0) return hipSuccess;
-  if (p.direct && fused) {
+  if (p.direct && a.xh) {
     // the gather from the channel-minor copy (built by the prologue launch)
     s.xh = (const bf16_t*)a.xh;
     int l = 0;
     while ((1 << l) < p.cg / 8) ++l;
     s.nv_log = l;
     if (p.mblocks != 1) return hipErrorInvalidValue;
-    return launch_direct_t<1>(p, s, st);
+    switch (mode) {
+      case kFusedMode: return launch_direct_t<kFusedMode>(p, s, "fused_offset_sample", st);
+      case kOffsetsMode: return launch_direct_t<kOffsetsMode>(p, s, "offset_conv", st);
+      default: return launch_direct_t<kSampleMode>(p, s, "sample_only", st);
+    }
   }
-  return p.d.dtype == DEFT_BF16 ? launch_sample_dt<bf16_t>(p, fused, s, st)
-                                : launch_sample_dt<float>(p, fused, s, st);
+  return p.d.dtype == DEFT_BF16 ? launch_sample_dt<bf16_t>(p, mode, s, st)
+                                : launch_sample_dt<float>(p, mode, s, st);
 }
 
 static IndexParams make_index_params(const deft_desc& d, int ho, int wo) {

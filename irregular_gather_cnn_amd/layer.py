@@ -58,6 +58,16 @@ class DeformConv:
         _lib.deft_forward(self.plan, x, w_off, b_off, w, b, y, offsets, self.ws, self.ws_bytes, self.stream())
         return y, offsets
 
+    def forward_unfused(self, x, w_off, b_off, w, b, y=None, offsets=None):
+        """The three-operator form: offsets written to and read back from HBM."""
+        if y is None:
+            y = torch.empty((self.n, self.c_out, self.ho, self.wo), dtype=self.tdtype, device=self.device)
+        if offsets is None:
+            offsets = torch.empty((self.n, self.oc, self.ho, self.wo), dtype=torch.float32, device=self.device)
+        _lib.deft_forward_unfused(self.plan, x, w_off, b_off, w, b, y, offsets, self.ws, self.ws_bytes,
+                                  self.stream())
+        return y, offsets
+
     def backward(self, x, w_off, w, offsets, dy, with_bias=True, out=None):
         if out is None:
             out = dict(dx=torch.empty_like(x), dw_off=torch.empty_like(w_off), dw=torch.empty_like(w),

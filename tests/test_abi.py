@@ -143,6 +143,29 @@ def test_forward_validation_before_launch():
     assert lib.deft_forward(None, *ok[1:]) == -4
 
 
+def test_unfused_forward_validation_before_launch():
+    d = desc()
+    p = L.deft_plan_create(d)
+    ws = L.deft_workspace_bytes(p, 0)
+    lib = L.load()
+    ok = [p, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, ws, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.deft_forward_unfused(*a)
+
+    assert call(7, None) == -4   # the offsets buffer is required here
+    assert call(1, None) == -4
+    assert call(6, None) == -4
+    assert call(8, None) == -5
+    assert call(9, ws - 1) == -5
+    assert call(7, FAKE + 4) == -7
+    assert lib.deft_forward_unfused(None, *ok[1:]) == -4
+    e = L.deft_plan_create(desc(n=0))
+    assert lib.deft_forward_unfused(e, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
 def test_empty_batch_is_a_no_op():
     d = desc(n=0)
     p = L.deft_plan_create(d)

@@ -178,9 +178,15 @@ def test_fused_equals_unfused_and_plan_invariance(name):
         y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
         cols = layer.cols_view().clone()
         un = layer.sample(t["x"], off)
+        # the three-operator forward: offsets through HBM, then sampling, then GEMM
+        y3, off3 = layer.forward_unfused(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+        cols3 = layer.cols_view().clone()
         torch.cuda.synchronize()
-        assert torch.equal(cols.view(torch.int16 if wl.dtype == "bf16" else torch.int32),
-                           un.view(torch.int16 if wl.dtype == "bf16" else torch.int32))
+        bits = torch.int16 if wl.dtype == "bf16" else torch.int32
+        assert torch.equal(cols.view(bits), un.view(bits))
+        assert torch.equal(off3, off)
+        assert torch.equal(cols3.view(bits), cols.view(bits))
+        assert torch.equal(y3.view(bits), y.view(bits))
         cur = (y.clone(), off.clone(), cols)
         if ref is None:
             ref = cur
@@ -232,6 +238,7 @@ def test_edge_shapes_forward(case, dtype):
     t = {k: dev(v, dtype) for k, v in inp.items()}
     layer = make_layer(wl)
     y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    y3, off3 = layer.forward_unfused(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
     torch.cuda.synchronize()
     if wl.n == 0:
         return
@@ -239,6 +246,9 @@ def test_edge_shapes_forward(case, dtype):
     y_ref, off_ref = oracle.forward(s, inp["x"], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
     assert rel(host(off), off_ref) <= 1e-5
     assert rel(host(y), y_ref) <= TOL[dtype]
+    # the unfused three-operator forward computes the same values in the same order
+    assert torch.equal(off3, off)
+    assert torch.equal(y3, y)
 
 
 # --- backward -------------------------------------------------------------------------
@@ -320,6 +330,29 @@ def test_backward_bf16_direct_gemm(case):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
         assert e <= TOL["bf16"], k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_after_unfused_forward(dtype):
+    """deft_backward following the unfused three-operator forward: the
+    workspace holds the same columns (and channel-minor copy), so the
+    gradients agree with the oracle and with the fused forward's backward."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, train=True, n=2, c_in=32, c_out=24, h=10, w=11)
+    say("backward after unfused forward", dtype)
+    inp, layer, y, off, g = run_backward(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    y3, off3 = layer.forward_unfused(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    g3 = layer.backward(t["x"], t["w_off"], t["w"], off3, t["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y) and torch.equal(off3, off)
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g3[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL[dtype], k
+        # fixed-order sums: identical to the backward after the fused forward
+        # (dx may take a few float atomics for taps beyond the halo)
+        assert rel(host(g3[k]), host(g[k])) <= (1e-6 if k == "dx" else 0.0), k
 
 
 @pytest.mark.timeout(900)
