@@ -366,4 +366,19 @@ __device__ __forceinline__ void store8(float* dst, const float* f) {
   *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
+// 16-byte store with the non-temporal hint, for large results that a later
+// kernel streams back from HBM (the deformed columns, dCol, y): they leave for
+// memory at once instead of staying in the L2 and the Infinity Cache as dirty
+// lines, whose write-back would otherwise compete with the next kernel's reads.
+__device__ __forceinline__ void store16_nt(void* dst, const uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  v4u q;
+  q.x = v.x; q.y = v.y; q.z = v.z; q.w = v.w;
+  __builtin_nontemporal_store(q, (v4u*)dst);
+}
+__device__ __forceinline__ void store8_nt(bf16_t* dst, const float* f) {
+  store16_nt(dst, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                             pack_bf16x2(f[6], f[7])));
+}
+
 }  // namespace deft

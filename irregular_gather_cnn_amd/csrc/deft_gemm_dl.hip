@@ -275,7 +275,7 @@ struct DlFwd {
   __device__ void store_chunk(int n, int m, const uint4 v) const {
     if (n >= N || m >= M) return;
     const int img = fdiv(m, div_howo), p = m - img * HoWo;
-    *(uint4*)(y + ((size_t)img * N + n) * HoWo + p) = v;
+    store16_nt(y + ((size_t)img * N + n) * HoWo + p, v);
   }
   __device__ void store_acc(const TileCoord&, int, int, const f32x16_t&, int) const {}
 };
@@ -331,7 +331,7 @@ struct DlDcol {
   __device__ float column_add(int) const { return 0.f; }
   __device__ void store_chunk(int n, int m, const uint4 v) const {
     if (n >= N || m >= M) return;
-    *(uint4*)(dcol + (size_t)n * M + m) = v;
+    store16_nt(dcol + (size_t)n * M + m, v);
   }
   __device__ void store_acc(const TileCoord&, int, int, const f32x16_t&, int) const {}
 };

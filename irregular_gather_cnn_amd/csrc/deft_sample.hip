@@ -606,7 +606,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       unpack8(q[u][3], f11);
 #pragma unroll
       for (int c = 0; c < 8; ++c) o8[c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
-      store8(colt + tb[u].z, o8);
+      store8_nt(colt + tb[u].z, o8);
     }
   }
 }
