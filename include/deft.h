@@ -136,6 +136,20 @@ int deft_forward(const deft_plan* p, const void* x, const void* w_off, const voi
                  const void* w, const void* b, void* y, float* offsets_out, void* workspace,
                  size_t ws_bytes, void* stream);
 
+/* deft_forward that also observes the offset distribution: the fused
+ * sampling launch adds the required-halo histogram of every tap it samples to
+ * `hist` (device uint32 [hist_len], 3 <= hist_len <= 64; the same bins as
+ * deft_halo_histogram).  The counts are ADDED: the caller zeroes the buffer
+ * and may let several calls accumulate before re-planning with
+ * deft_plan_create (DefT page, "What to keep in mind": the gains rest on the
+ * offset distribution, which shifts as training goes on and differs per
+ * layer).  Other outputs are those of deft_forward.  DEFT_ERR_BAD_DESC for
+ * hist_len out of range, DEFT_ERR_NULLPTR for a NULL hist (N > 0),
+ * DEFT_ERR_ALIGN if hist is not 4-byte aligned; checks run before any launch. */
+int deft_forward_hist(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
+                      const void* w, const void* b, void* y, float* offsets_out, void* workspace,
+                      size_t ws_bytes, uint32_t* hist, int hist_len, void* stream);
+
 /* The same forward in the unfused three-operator form the DefT explainer page
  * compares against ("What people did before this paper", "The argument in one
  * glance"): an offset-convolution launch writes the offsets to HBM

@@ -19,7 +19,8 @@ STATUS = {0: "DEFT_OK", -1: "DEFT_ERR_BAD_DESC", -2: "DEFT_ERR_GROUPS", -3: "DEF
           -4: "DEFT_ERR_NULLPTR", -5: "DEFT_ERR_WORKSPACE", -6: "DEFT_ERR_DTYPE", -7: "DEFT_ERR_ALIGN",
           -8: "DEFT_ERR_HIP", -9: "DEFT_ERR_PLAN", -10: "DEFT_ERR_UNSUPPORTED"}
 EXPORTED = ["deft_desc_validate", "deft_plan_create", "deft_plan_create_forced", "deft_plan_get_info",
-            "deft_plan_destroy", "deft_workspace_bytes", "deft_forward", "deft_forward_unfused", "deft_backward",
+            "deft_plan_destroy", "deft_workspace_bytes", "deft_forward", "deft_forward_hist", "deft_forward_unfused",
+            "deft_backward",
             "deft_debug_sample_index", "deft_debug_sample", "deft_halo_histogram", "deft_error_string",
             "deft_last_hip_error", "deft_timing_start", "deft_timing_stop", "deft_timing_count",
             "deft_timing_get"]
@@ -74,6 +75,7 @@ def load() -> ctypes.CDLL:
         "deft_workspace_bytes": (sz, [vp, i]),
         "deft_forward": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "deft_forward_unfused": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "deft_forward_hist": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp]),
         "deft_backward": (i, [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]),
         "deft_debug_sample_index": (i, [dp, vp, vp, vp, vp, vp]),
         "deft_debug_sample": (i, [vp, vp, vp, vp, vp]),
@@ -157,6 +159,13 @@ def deft_workspace_bytes(plan, training: int) -> int:
 def deft_forward(plan, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, stream=None) -> None:
     _check(load().deft_forward(plan, _ptr(x), _ptr(w_off), _ptr(b_off), _ptr(w), _ptr(b), _ptr(y),
                                _ptr(offsets_out), _ptr(workspace), int(ws_bytes), _ptr(stream)), "deft_forward")
+
+
+def deft_forward_hist(plan, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, hist, hist_len,
+                      stream=None) -> None:
+    _check(load().deft_forward_hist(plan, _ptr(x), _ptr(w_off), _ptr(b_off), _ptr(w), _ptr(b), _ptr(y),
+                                    _ptr(offsets_out), _ptr(workspace), int(ws_bytes), _ptr(hist), int(hist_len),
+                                    _ptr(stream)), "deft_forward_hist")
 
 
 def deft_forward_unfused(plan, x, w_off, b_off, w, b, y, offsets, workspace, ws_bytes, stream=None) -> None:

@@ -438,7 +438,7 @@ size_t deft_workspace_bytes(const deft_plan* p, int training) {
 // in HBM -> sampling -> GEMM), which needs the offsets buffer.
 static int forward_impl(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
                         const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream,
-                        bool fused) {
+                        bool fused, uint32_t* hist = nullptr, int hist_len = 0) {
   if (!p) return DEFT_ERR_NULLPTR;
   if (p->d.n == 0) return DEFT_OK;  // empty batch: nothing is read or written
   if (!x || !w_off || !w || !y) return DEFT_ERR_NULLPTR;
@@ -457,6 +457,8 @@ static int forward_impl(const deft_plan* p, const void* x, const void* w_off, co
   a.x = x; a.woff_p = ws + p->ws_woff; a.b_off = b_off; a.off_out = offsets_out;
   a.cols = ws + p->ws_cols;
   a.xh = p->direct ? ws + p->ws_xh : nullptr;
+  a.hist = hist;
+  a.hist_len = hist_len;
   if (fused) {
     e = deft::launch_sample(*p, deft::kFusedMode, a, st);
   } else {
@@ -475,6 +477,16 @@ static int forward_impl(const deft_plan* p, const void* x, const void* w_off, co
 int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
                  const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(p, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, stream, true);
+}
+
+int deft_forward_hist(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,
+                      const void* b, void* y, float* offsets_out, void* workspace, size_t ws_bytes, uint32_t* hist,
+                      int hist_len, void* stream) {
+  if (!p) return DEFT_ERR_NULLPTR;
+  if (hist_len < 3 || hist_len > 64) return DEFT_ERR_BAD_DESC;
+  if (!hist && p->d.n > 0) return DEFT_ERR_NULLPTR;
+  if ((uintptr_t)hist & 3u) return DEFT_ERR_ALIGN;
+  return forward_impl(p, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, stream, true, hist, hist_len);
 }
 
 int deft_forward_unfused(const deft_plan* p, const void* x, const void* w_off, const void* b_off, const void* w,

@@ -58,6 +58,8 @@ struct SampleArgs {
   float* off_out = nullptr;       // nullable
   void* cols = nullptr;           // [N*Ho*Wo][taps][Cin]
   void* xh = nullptr;             // direct gather: channel-minor copy of x (workspace)
+  uint32_t* hist = nullptr;       // nullable: required-halo histogram accumulated by the launch
+  int hist_len = 0;
 };
 
 hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_off, void* wt, void* woff_p,

@@ -39,6 +39,8 @@ struct SampleParams {
   const bf16_t* xh;  // direct path: x channel-minor [N][H*W+1][Cin], pixel H*W = 0
   int nv_log;        // direct path: log2(Cg / 8)
   int offsets_only;  // 1: stop after the offset convolution (offsets written to off_out)
+  uint32_t* hist;    // nullable: the tile's required-halo histogram is added here
+  int hist_len;      // 3..64 bins when hist is given
   int stage_d;       // direct path: footprint-staging loads per wave per chunk
   FastDiv div_fw;
 };
@@ -66,6 +68,45 @@ struct UnitWalk {
     }
   }
 };
+
+// Adds the required-halo histogram of this tile's taps to p.hist (the bins
+// of deft_halo_histogram: Chebyshev distance from the tap's grid point to its
+// corner (y0, x0), the last bin for fully outside taps), from the offsets in
+// LDS (off_l [2 * gw * K2][PT]).  The emitted distribution is what the
+// planner sizes the halo from (DefT page, "What to keep in mind": the gains
+// depend on the offset distribution, so it is observed as the layer runs).
+// Each wave counts its entries with one ballot per bin (lane b keeps bin b)
+// and adds its counts with at most hist_len global atomics.  Called by all
+// threads; the loop over entries is uniform within each wave.
+__device__ __forceinline__ void tile_halo_hist(const SampleParams& p, const float* off_l, int gw, int oh0, int ow0,
+                                            int thn, int twn) {
+  const int lane = threadIdx.x & 63;
+  const int PT = p.TH * p.TW, nidx = gw * PT * p.K2;
+  uint32_t cnt = 0;
+  for (int eb = (int)threadIdx.x - lane; eb < nidx; eb += (int)blockDim.x) {
+    const int e = eb + lane;
+    int bin = -1;
+    if (e < nidx) {
+      const int r = e / p.K2, t = e - r * p.K2;
+      const int gl = r / PT, pix = r - gl * PT;
+      const int ty = pix / p.TW, tx = pix - ty * p.TW;
+      if (ty < thn && tx < twn) {
+        const int ti = t / p.KW, tj = t - ti * p.KW;
+        const int by = (oh0 + ty) * p.SH - p.PH + ti * p.DH;
+        const int bx = (ow0 + tx) * p.SW - p.PW + tj * p.DW;
+        const float dy = off_l[(2 * (gl * p.K2 + t)) * PT + pix];
+        const float dx = off_l[(2 * (gl * p.K2 + t) + 1) * PT + pix];
+        const TapIndex ix = tap_index(by, bx, dy, dx, p.H, p.W);
+        bin = ix.outside ? p.hist_len - 1 : min(max(abs(ix.y0 - by), abs(ix.x0 - bx)), p.hist_len - 2);
+      }
+    }
+    for (int b = 0; b < p.hist_len; ++b) {
+      const uint64_t m = __ballot(bin == b);
+      if (lane == b) cnt += (uint32_t)__popcll(m);
+    }
+  }
+  if (lane < p.hist_len && cnt) atomicAdd(&p.hist[lane], cnt);
+}
 
 template <typename T, bool FUSED, int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sample(const SampleParams p) {
@@ -226,6 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   if (pipeB) pair_load(st, gb, ximg, g0 * p.Cg);  // first halo chunk, in flight during the index stage
   __syncthreads();
+  if (p.hist) tile_halo_hist(p, off_l, p.GW, oh0, ow0, thn, twn);
 
   // ---- tap index stage: once per (group, pixel, tap) ----
   // tab[e] = {corner (y0, x0) as an element offset into the staged region,
@@ -543,6 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     __syncthreads();
   }
 
+  if (p.hist) tile_halo_hist(p, off_l, 1, oh0, ow0, thn, twn);
   // ---- tap index stage: corner pixel, corner mask, column offset, weights ----
   const int nent = PT * p.K2;
   for (int e = tid; e < nent; e += 256) {
@@ -808,6 +851,8 @@ static SampleParams make_params(const deft_plan& p, const SampleArgs& a) {
   s.xh = nullptr;
   s.nv_log = 0;
   s.offsets_only = 0;
+  s.hist = a.hist;
+  s.hist_len = a.hist_len;
   s.x = a.x; s.woff_p = a.woff_p; s.b_off = a.b_off; s.off_in = a.off_in; s.off_out = a.off_out;
   s.cols = a.cols;
   return s;

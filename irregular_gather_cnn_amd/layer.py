@@ -18,10 +18,16 @@ class DeformConv:
     """Deformable kh x kw convolution (offset conv -> bilinear sampling -> GEMM).
 
     ``plan``: None (planner default halo), a halo histogram (list of uint32) or
-    a (tile_h, tile_w, halo, chunk) tuple for a forced plan."""
+    a (tile_h, tile_w, halo, chunk) tuple for a forced plan.
+
+    ``replan_every`` > 0: every forward also adds the required-halo histogram
+    of its taps (emitted by the fused sampling kernel) to a device buffer;
+    after that many forwards the next forward first re-plans from the
+    accumulated histogram (the plan, and the workspace if it must grow, are
+    swapped only between a backward and the next forward)."""
 
     def __init__(self, n, c_in, h, w, c_out, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dil=(1, 1), groups=1,
-                 dtype="bf16", plan=None, training=False, device="cuda"):
+                 dtype="bf16", plan=None, training=False, device="cuda", replan_every=0, hist_len=16):
         self.dtype = dtype
         self.tdtype = _tdtype(dtype)
         self.desc = _lib.make_desc(n, c_in, h, w, c_out, kh, kw, stride, pad, dil, groups,
@@ -38,6 +44,32 @@ class DeformConv:
         self.ho, self.wo, self.oc = self.info["ho"], self.info["wo"], self.info["oc"]
         self.n, self.c_in, self.h, self.w, self.c_out = n, c_in, h, w, c_out
         self.kh, self.kw, self.groups = kh, kw, groups
+        self.replan_every, self.hist_len = replan_every, hist_len
+        self.hist = torch.zeros((hist_len,), dtype=torch.int32, device=device) if replan_every else None
+        self.observed_calls, self.replans = 0, 0
+
+    PLAN_KEYS = ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h", "bwd_tile_w", "bwd_chunk")
+
+    def observed_histogram(self):
+        """The required-halo histogram accumulated since the last re-plan."""
+        return [int(v) & 0xFFFFFFFF for v in self.hist.cpu().tolist()]
+
+    def _replan(self):
+        hist = self.observed_histogram()
+        self.hist.zero_()
+        self.observed_calls = 0
+        new = _lib.deft_plan_create(self.desc, hist)
+        info = _lib.deft_plan_get_info(new)
+        if all(info[k] == self.info[k] for k in self.PLAN_KEYS):
+            _lib.deft_plan_destroy(new)
+            return False
+        _lib.deft_plan_destroy(self.plan)
+        self.plan, self.info = new, info
+        self.ws_bytes = _lib.deft_workspace_bytes(self.plan, 1 if self.training else 0)
+        if self.ws_bytes > self.ws.numel():
+            self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.replans += 1
+        return True
 
     def __del__(self):
         try:
@@ -55,7 +87,14 @@ class DeformConv:
             want_offsets = self.training
         if offsets is None and want_offsets:
             offsets = torch.empty((self.n, self.oc, self.ho, self.wo), dtype=torch.float32, device=self.device)
-        _lib.deft_forward(self.plan, x, w_off, b_off, w, b, y, offsets, self.ws, self.ws_bytes, self.stream())
+        if self.replan_every:
+            if self.observed_calls >= self.replan_every:
+                self._replan()
+            _lib.deft_forward_hist(self.plan, x, w_off, b_off, w, b, y, offsets, self.ws, self.ws_bytes, self.hist,
+                                   self.hist_len, self.stream())
+            self.observed_calls += 1
+        else:
+            _lib.deft_forward(self.plan, x, w_off, b_off, w, b, y, offsets, self.ws, self.ws_bytes, self.stream())
         return y, offsets
 
     def forward_unfused(self, x, w_off, b_off, w, b, y=None, offsets=None):

@@ -143,6 +143,27 @@ def test_forward_validation_before_launch():
     assert lib.deft_forward(None, *ok[1:]) == -4
 
 
+def test_forward_hist_validation_before_launch():
+    d = desc()
+    p = L.deft_plan_create(d)
+    ws = L.deft_workspace_bytes(p, 0)
+    lib = L.load()
+    ok = [p, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, ws, FAKE, 16, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.deft_forward_hist(*a)
+
+    assert call(11, 2) == -1      # too few bins
+    assert call(11, 65) == -1     # more bins than lanes
+    assert call(10, None) == -4   # histogram buffer
+    assert call(10, FAKE + 2) == -7
+    assert call(1, None) == -4    # then the forward's own checks
+    assert call(8, None) == -5
+    assert lib.deft_forward_hist(None, *ok[1:]) == -4
+
+
 def test_unfused_forward_validation_before_launch():
     d = desc()
     p = L.deft_plan_create(d)

@@ -196,6 +196,71 @@ def test_fused_equals_unfused_and_plan_invariance(name):
         del layer
 
 
+@pytest.mark.parametrize("name,plan", [
+    ("bf16_n16_c256_56x56", None),                 # direct gather, the headline forward
+    ("bf16_n16_c512_28x28_g4_wide", None),         # 4 groups, wide offsets, pushed taps
+    ("bf16_n16_c512_28x28_g4_wide", (8, 8, 2, 0)),  # LDS halo, several groups per workgroup
+    ("fp32_n8_c128_64x64", None),
+    ("fp32_n8_c128_64x64", (3, 7, 1, 16)),         # ragged tiles
+])
+def test_forward_emits_halo_histogram(name, plan):
+    """The histogram the fused sampling kernel emits equals the one computed
+    from its offsets afterwards, bin for bin; two calls add up."""
+    wl = WORKLOADS[name]
+    say("forward histogram", name, plan)
+    inp = make_inputs(wl)
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl, plan=plan)
+    for hist_len in (16, 5):
+        hist = torch.zeros((hist_len,), dtype=torch.int32, device="cuda")
+        y = torch.empty((wl.n, wl.c_out, layer.ho, layer.wo), dtype=layer.tdtype, device="cuda")
+        off = torch.empty((wl.n, layer.oc, layer.ho, layer.wo), dtype=torch.float32, device="cuda")
+        L.deft_forward_hist(layer.plan, t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y, off, layer.ws,
+                            layer.ws_bytes, hist, hist_len, layer.stream())
+        ref = halo_histogram(layer.desc, off, hist_len)
+        got = [int(v) for v in hist.cpu().tolist()]
+        say("  %d bins: %s" % (hist_len, got))
+        assert got == ref
+        assert sum(got) == wl.n * wl.groups * wl.taps * layer.ho * layer.wo
+        L.deft_forward_hist(layer.plan, t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y, off, layer.ws,
+                            layer.ws_bytes, hist, hist_len, layer.stream())
+        assert [int(v) for v in hist.cpu().tolist()] == [2 * v for v in ref]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replanning_from_observed_offsets(dtype):
+    """A layer that starts with a halo of 0 and sees offsets of about 3 px
+    re-plans from the histogram its forwards emitted; outputs stay identical
+    (forward results do not depend on the plan) and the backward after the
+    swap agrees with the oracle."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, train=True, n=2, c_in=32, c_out=24, h=14, w=12,
+                                                     offset_std=3.0)
+    say("replanning", dtype)
+    inp = make_inputs(wl, with_dy=True)
+    t = {k: dev(v, dtype) for k, v in inp.items()}
+    layer = make_layer(wl, plan=(4, 8, 0, 0), training=True)
+    layer.replan_every, layer.hist_len = 2, 16
+    layer.hist = torch.zeros((16,), dtype=torch.int32, device="cuda")
+    halo0 = layer.info["halo"]
+    y0_, off0 = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    y0_, off0 = y0_.clone(), off0.clone()
+    layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    hist = layer.observed_histogram()
+    say("  observed", hist)
+    assert sum(hist) == 2 * wl.n * wl.groups * wl.taps * layer.ho * layer.wo
+    y1, off1 = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])  # re-plans first
+    g = layer.backward(t["x"], t["w_off"], t["w"], off1, t["dy"])
+    torch.cuda.synchronize()
+    say("  halo %d -> %d, replans %d" % (halo0, layer.info["halo"], layer.replans))
+    assert layer.replans == 1 and layer.info["halo"] > halo0
+    assert torch.equal(y1, y0_) and torch.equal(off1, off0)
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off1).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL[dtype], k
+
+
 def test_halo_histogram_matches_index_stage():
     wl = WORKLOADS["bf16_n16_c512_28x28_g4_wide"]
     say("halo histogram")
