@@ -296,6 +296,29 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Waits until at most n vector-memory loads of this wave are outstanding, n
+// rounded down to a multiple of 4 (at most 60): waiting for more than asked
+// is always safe.  n must be wave-uniform.
+__device__ __forceinline__ void wait_vm_atmost(int n) {
+  switch (n < 0 ? 0 : (n > 60 ? 15 : n >> 2)) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<4>(); break;
+    case 2: wait_vm<8>(); break;
+    case 3: wait_vm<12>(); break;
+    case 4: wait_vm<16>(); break;
+    case 5: wait_vm<20>(); break;
+    case 6: wait_vm<24>(); break;
+    case 7: wait_vm<28>(); break;
+    case 8: wait_vm<32>(); break;
+    case 9: wait_vm<36>(); break;
+    case 10: wait_vm<40>(); break;
+    case 11: wait_vm<44>(); break;
+    case 12: wait_vm<48>(); break;
+    case 13: wait_vm<52>(); break;
+    case 14: wait_vm<56>(); break;
+    default: wait_vm<60>(); break;
+  }
+}
 
 // ximg: buffer over one image; c0: first channel of the chunk.  Words outside
 // the image read as zero through the buffer range check.
