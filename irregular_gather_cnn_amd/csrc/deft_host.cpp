@@ -298,28 +298,43 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
   if (!found) return DEFT_ERR_UNSUPPORTED;
   // Direct gather where supported: the halo chosen above still bounds the
   // backward's candidate window; the tile only sets the forward's launch
-  // shape (every workgroup pays a fixed cost for its offset weights and
-  // staging round trips, about as much as writing 64 KB of columns).
+  // shape.  Every tile of 32..64 pixels is a candidate (fewer only when the
+  // output is smaller).  Cost: the columns of every pixel slot the launch
+  // covers, including the empty slots of ragged edge tiles (their offset conv
+  // and tap work is done anyway); the footprint each workgroup stages for its
+  // offset conv (served from the L2, weighted down); a fixed cost per
+  // workgroup for its offset weights and staging round trips (about as much as
+  // writing 64 KB of columns); all divided by the share of the machine the
+  // launch keeps busy.  On 56 x 56 this prefers 7 x 7 (1024 workgroups, four
+  // per CU) over 4 x 16, whose last tile column is half empty (measured 72.8
+  // against 79.0 us).
   if (direct_ok(d)) {
-    static const int dtiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}};
     double dbest = 1e300;
     deft_plan bd;
     bool dfound = false;
-    for (auto& t : dtiles) {
-      deft_plan p;
-      p.d = d;
-      if (!layout_plan(p, t[0], t[1], best.halo, s.cg, true) || p.chunk_b == 0) continue;
-      const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
-      const double slots = (double)kNumCUs * occ;
-      const double waves = std::ceil(p.num_wg / slots);
-      const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
-      const double cost = (col_bytes + (double)p.num_wg * 65536.0) / std::max(busy, 0.05);
-      if (cost < dbest * 0.999) {
-        dbest = cost;
-        bd = p;
-        dfound = true;
+    const double valid = (double)d.n * s.ho * s.wo * d.offset_groups;
+    const int min_pt = std::min(32, s.ho * s.wo);
+    for (int th = 1; th <= 16; ++th)
+      for (int tw = 1; th * tw <= 64; ++tw) {
+        if (th * tw < min_pt) continue;
+        deft_plan p;
+        p.d = d;
+        if (!layout_plan(p, th, tw, best.halo, s.cg, true) || p.chunk_b == 0) continue;
+        const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
+        const double slots = (double)kNumCUs * occ;
+        const double waves = std::ceil(p.num_wg / slots);
+        const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
+        const double padded = (double)p.num_wg * th * tw;
+        const double stage = (double)p.num_wg * p.foot_h * p.foot_w * d.c_in * s.esz;
+        const double cost =
+            (col_bytes * padded / std::max(valid, 1.0) + 0.25 * stage + (double)p.num_wg * 65536.0) /
+            std::max(busy, 0.05);
+        if (cost < dbest * 0.999) {
+          dbest = cost;
+          bd = p;
+          dfound = true;
+        }
       }
-    }
     if (dfound) {
       bd.est_miss = best.est_miss;
       best = bd;
