@@ -116,6 +116,34 @@ def test_direct_gather_selection():
         assert e.value.code == -9
 
 
+def test_planner_direct_tile_avoids_ragged_edges():
+    """The direct-gather tile is costed with the empty pixel slots of ragged
+    edge tiles: on 56 x 56 and 28 x 28 outputs it picks a tile that divides the
+    output (7 x 7), not 4 x 16 (whose last tile column would be half empty)."""
+    for kw in (dict(n=16, c_in=256, c_out=256, h=56, w=56),
+               dict(n=16, c_in=512, c_out=512, h=28, w=28, groups=4)):
+        i = L.deft_plan_get_info(L.deft_plan_create(desc(**kw)))
+        assert i["gather_direct"] == 1
+        assert (i["tile_h"], i["tile_w"]) == (7, 7)
+        assert i["ho"] % i["tile_h"] == 0 and i["wo"] % i["tile_w"] == 0
+
+
+@pytest.mark.parametrize("h,w,stride,dil,groups", [
+    (5, 5, 1, 1, 1), (9, 11, 1, 1, 2), (13, 70, 1, 2, 1), (56, 56, 2, 1, 1), (31, 17, 2, 1, 4), (64, 64, 1, 1, 1),
+])
+def test_planner_tiles_are_valid(h, w, stride, dil, groups):
+    """Every automatic plan has a tile of at most 64 pixels, at least one
+    workgroup and a workspace; the direct gather covers the output."""
+    d = desc(n=2, c_in=64, c_out=24, h=h, w=w, stride=(stride, stride), pad=(dil, dil), dil=(dil, dil),
+             groups=groups)
+    i = L.deft_plan_get_info(L.deft_plan_create(d))
+    assert 1 <= i["tile_h"] * i["tile_w"] <= 64
+    assert i["num_workgroups"] >= 1 and i["ws_forward"] > 0
+    tiles = -(-i["ho"] // i["tile_h"]) * -(-i["wo"] // i["tile_w"])
+    if i["gather_direct"]:
+        assert i["num_workgroups"] == 2 * groups * tiles
+
+
 FAKE = 1 << 40  # 16-byte aligned, never dereferenced (validation fails first)
 
 
