@@ -91,6 +91,9 @@ typedef struct deft_plan_info {
   int gather_direct;      /* 1: the forward gathers corners from a channel-minor copy of x held
                              in the caches (no LDS halo; halo then bounds only the backward's
                              candidate window); 0: LDS tile + halo */
+  int gather_gemm;        /* 1: the forward runs the offset conv, then one launch that gathers the
+                             columns straight into the main GEMM's LDS tiles (y and the columns
+                             written; the GEMM reads no columns from HBM) */
 } deft_plan_info;
 
 /* Checks the descriptor alone.  Pure host function. */
@@ -112,7 +115,9 @@ int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len
 /* Plan with a forced tile (tile_h*tile_w <= 64), halo (0..32) and channel
  * chunk (multiple of 16 dividing Cin/G, at most 64; 0 = largest that fits;
  * -1 = direct gather: the forward reads the corners from a channel-minor copy
- * of x instead of an LDS halo, bf16 only, Cin/(8G) a power of two <= 256).
+ * of x instead of an LDS halo, bf16 only, Cin/(8G) a power of two <= 256;
+ * -2 = direct gather fused into the main GEMM, which also needs Cin/G and
+ * Cin multiples of 32, Ho*Wo and c_out multiples of 8).
  * DEFT_ERR_PLAN if its LDS does not fit or the direct gather is unsupported; deft_backward returns DEFT_ERR_PLAN
  * for a forced plan whose backward tile does not fit even with 8 channels.
  * Forward results (offsets, columns, y) are bit-identical across plans; the

@@ -210,6 +210,9 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   p.ws_cols = o; o = align256(o + P * s.ck * s.esz);
   p.ws_xh = o;
   if (direct) o = align256(o + (size_t)d.n * ((size_t)d.h * d.w + 1) * d.c_in * s.esz);
+  p.igemm = 0;
+  p.ws_offs = o;
+  if (direct && deft::igemm_supported(p)) o = align256(o + P * s.oc * 4);  // offsets when the caller keeps none
   p.ws_fwd_end = o;
   p.ws_w2 = o; o = align256(o + (size_t)s.ck * d.c_out * s.esz);
   p.ws_wofft = o; o = align256(o + (size_t)d.c_in * p.kk_pad * s.esz);
@@ -398,15 +401,20 @@ int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo
   if (v) return v;
   const Shape s = shape_of(*d);
   if (tile_h < 1 || tile_w < 1 || tile_h * tile_w > 64 || halo < 0 || halo > 32) return DEFT_ERR_PLAN;
-  if (chunk != 0 && chunk != -1 && (chunk < 16 || chunk > 64 || chunk % 16 || s.cg % chunk)) return DEFT_ERR_PLAN;
-  if (chunk == -1 && !direct_ok(*d)) return DEFT_ERR_PLAN;
+  if (chunk != 0 && chunk != -1 && chunk != -2 && (chunk < 16 || chunk > 64 || chunk % 16 || s.cg % chunk))
+    return DEFT_ERR_PLAN;
+  if ((chunk == -1 || chunk == -2) && !direct_ok(*d)) return DEFT_ERR_PLAN;
   deft_plan* p = new (std::nothrow) deft_plan();
   if (!p) return DEFT_ERR_UNSUPPORTED;
   p->d = *d;
   p->num_btiles = 0;
   bool ok = false;
-  if (chunk == -1) {
+  if (chunk == -1 || chunk == -2) {
     ok = layout_plan(*p, tile_h, tile_w, halo, s.cg, true);
+    if (ok && chunk == -2) {
+      ok = deft::igemm_supported(*p);
+      p->igemm = ok ? 1 : 0;
+    }
   } else if (chunk != 0) {
     ok = layout_plan(*p, tile_h, tile_w, halo, chunk);
   } else {
@@ -437,6 +445,7 @@ int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
   info->bwd_chunk = p->chunk_b;
   info->gemm_direct = p->gemm_dl;
   info->gather_direct = p->direct;
+  info->gather_gemm = p->igemm;
   info->dw_splits = p->dw_splits;
   return DEFT_OK;
 }
@@ -474,6 +483,16 @@ static int forward_impl(const deft_plan* p, const void* x, const void* w_off, co
   a.xh = p->direct ? ws + p->ws_xh : nullptr;
   a.hist = hist;
   a.hist_len = hist_len;
+  if (fused && p->igemm) {
+    // offset conv, then the gather fused into the main GEMM (y and columns)
+    float* off = offsets_out ? offsets_out : (float*)(ws + p->ws_offs);
+    a.off_out = off;
+    e = deft::launch_sample(*p, deft::kOffsetsMode, a, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = deft::launch_igemm(*p, ws + p->ws_xh, off, ws + p->ws_wt, b, y, ws + p->ws_cols, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return DEFT_OK;
+  }
   if (fused) {
     e = deft::launch_sample(*p, deft::kFusedMode, a, st);
   } else {

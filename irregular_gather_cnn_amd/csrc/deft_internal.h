@@ -35,6 +35,11 @@ struct deft_plan {
   // bf16 GEMMs with direct global-to-LDS staging (else the generic kernel)
   int gemm_dl;
   int dw_splits, dw_kper;      // dW partials: pixel ranges of dw_kper (per image on the generic path)
+  // forward with the gather fused into the main GEMM (deft_igemm.hip): the
+  // offset conv writes the offsets (to the caller's buffer or ws_offs), then
+  // one launch gathers, multiplies and stores y and the columns
+  int igemm;
+  size_t ws_offs;
 };
 
 namespace deft {
@@ -75,6 +80,10 @@ hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off
 
 hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b,
                                void* y, hipStream_t s);
+// gather fused into the main GEMM (deft_igemm.hip)
+bool igemm_supported(const deft_plan& p);
+hipError_t launch_igemm(const deft_plan& p, const void* xh, const float* off, const void* wt, const void* b,
+                        void* y, void* cols, hipStream_t st);
 // direct-staging bf16 GEMMs (deft_gemm_dl.hip)
 bool gemm_dl_supported(const deft_plan& p);
 void gemm_dl_dw_split(const deft_plan& p, int* splits, int* kper);

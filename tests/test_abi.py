@@ -144,6 +144,20 @@ def test_planner_tiles_are_valid(h, w, stride, dil, groups):
         assert i["num_workgroups"] == 2 * groups * tiles
 
 
+def test_forced_gather_gemm_plan():
+    """chunk -2 selects the forward that gathers straight into the main GEMM;
+    it needs bf16, the direct gather, 32-channel slices and 8-pixel runs."""
+    ok = L.deft_plan_get_info(L.deft_plan_create_forced(desc(n=2, c_in=64, c_out=40, h=10, w=12), 7, 7, 2, -2))
+    assert ok["gather_gemm"] == 1 and ok["gather_direct"] == 1
+    plain = L.deft_plan_get_info(L.deft_plan_create_forced(desc(n=2, c_in=64, c_out=40, h=10, w=12), 7, 7, 2, -1))
+    assert plain["gather_gemm"] == 0
+    assert ok["ws_forward"] > plain["ws_forward"] - 1  # room for the offsets when the caller keeps none
+    for bad in (desc(n=2, c_in=64, dtype=L.DEFT_F32), desc(n=2, c_in=16, c_out=8), desc(n=2, c_in=64, h=9, w=11)):
+        with pytest.raises(L.DeftError) as e:
+            L.deft_plan_create_forced(bad, 7, 7, 2, -2)
+        assert e.value.code == -9
+
+
 FAKE = 1 << 40  # 16-byte aligned, never dereferenced (validation fails first)
 
 

@@ -397,6 +397,62 @@ def test_backward_bf16_direct_gemm(case):
         assert e <= TOL["bf16"], k
 
 
+GATHER_GEMM_CASES = [
+    ("bf16_n16_c256_56x56", None),
+    ("bf16_n16_c512_28x28_g4_wide", None),
+    ("small", dict(n=3, c_in=64, c_out=40, h=10, w=12)),
+    ("small", dict(n=2, c_in=64, c_out=264, h=8, w=6, groups=2)),
+    ("small", dict(n=2, c_in=32, c_out=24, h=16, w=16, stride=2)),
+]
+
+
+@pytest.mark.parametrize("name,kw", GATHER_GEMM_CASES)
+def test_gather_fused_gemm_forward(name, kw):
+    """The forward whose gather feeds the main GEMM directly: offsets and
+    columns bit-identical to the two-kernel forward (same sampling
+    arithmetic), y within one bf16 ulp of it (the GEMM sums in another order)
+    and within the bf16 tolerance of the oracle; the same y without an
+    offsets buffer from the caller."""
+    wl = WORKLOADS[name] if kw is None else WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype="bf16", **kw)
+    say("gather-fused GEMM forward", name, kw)
+    inp = make_inputs(wl)
+    t = {k: dev(v, "bf16") for k, v in inp.items()}
+    base = make_layer(wl)
+    y0, off0 = base.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    cols0 = base.cols_view().clone()
+    layer = make_layer(wl, plan=(7, 7, 2, -2))
+    assert layer.info["gather_gemm"] == 1
+    y1, off1 = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
+    cols1 = layer.cols_view().clone()
+    y2, _ = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=False)
+    torch.cuda.synchronize()
+    assert torch.equal(off1, off0)
+    assert torch.equal(cols1.view(torch.int16), cols0.view(torch.int16))
+    assert torch.equal(y2, y1)
+    a1, a0 = host(y1).astype(np.float64), host(y0).astype(np.float64)
+    assert np.all(np.abs(a1 - a0) <= 2.0 ** -7 * np.maximum(np.abs(a1), np.abs(a0)) + 1e-30)
+    s1 = image_shape(wl, 1)
+    for n in (0, wl.n - 1):
+        y_ref, _ = oracle.forward(s1, inp["x"][n:n + 1], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+        e = rel(a1[n:n + 1], y_ref)
+        say("  image %d: y rel %.2e" % (n, e))
+        assert e <= TOL["bf16"]
+
+
+def test_backward_after_gather_fused_gemm_forward():
+    """deft_backward after the gather-fused forward (same columns and
+    channel-minor copy in the workspace) matches the oracle."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype="bf16", train=True, n=2, c_in=64, c_out=24, h=10, w=12)
+    say("backward after gather-fused GEMM forward")
+    inp, layer, y, off, g = run_backward(wl, plan=(7, 7, 2, -2))
+    assert layer.info["gather_gemm"] == 1
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL["bf16"], k
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_backward_after_unfused_forward(dtype):
     """deft_backward following the unfused three-operator forward: the
