@@ -201,6 +201,15 @@ def main():
     fused_fn = lambda: layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
     unfused_fn = lambda: layer.forward_unfused(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
     fusion = {"fused_fwd_ms": round(time_forward(fused_fn), 4), "unfused_fwd_ms": round(time_forward(unfused_fn), 4)}
+    # the forward whose gather feeds the main GEMM directly (same tile and halo)
+    try:
+        gg = DeformConv(**geo, plan=(info["tile_h"], info["tile_w"], info["halo"], -2), training=True, device=dev)
+    except L.DeftError:
+        gg = None
+    if gg is not None:
+        gg_fn = lambda: gg.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
+        fusion["gather_gemm_fwd_ms"] = round(time_forward(gg_fn), 4)
+        del gg
     L.deft_timing_start(8 * args.steps)
     for _ in range(args.steps):
         unfused_fn()
