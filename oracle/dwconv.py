@@ -1,0 +1,34 @@
+"""CPU oracle for the dilated depthwise 1-D convolution -- test infrastructure.
+
+Only ``tests/`` and ``bench.py``'s CPU-baseline leg may import this module; the
+product path never does.
+
+The operation is the one the JAX issue page on grouped and dilated
+convolutions benchmarks (its reproduction script: ``depthwise`` with
+``feature_group_count`` equal to the channel count, "NTC" input, "TIO" kernel
+with one input feature per group, stride 1, VALID padding, ``rhs_dilation``
+d): for every batch b, output step t < T and channel c,
+
+    y[b, t, c] = sum_{k < K} w[k, c] * x[b, t + k*d, c],
+
+with x of length T + d*(K - 1).  Written out here in fp64 as a sum of K
+shifted, scaled copies of the input, in the order k = 0, 1, ..., K-1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def dwconv1d(x: np.ndarray, w: np.ndarray, dilation: int) -> np.ndarray:
+    """x [B][T + d(K-1)][C], w [K][C] -> y [B][T][C] (float64)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    K, C = w.shape
+    B, L, C2 = x.shape
+    assert C2 == C and dilation >= 1
+    T = L - dilation * (K - 1)
+    assert T >= 0
+    y = np.zeros((B, T, C), np.float64)
+    for k in range(K):
+        y += w[k][None, None, :] * x[:, k * dilation:k * dilation + T, :]
+    return y

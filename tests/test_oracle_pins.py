@@ -382,3 +382,57 @@ def test_index_stage_matches_fp64_floor_away_from_rounding(oracle):
             assert np.array_equal(y0[:, g, k], ey)
             assert np.array_equal(x0[:, g, k], ex)
             assert np.array_equal(m[:, g, k], em)
+
+
+# --- dilated depthwise 1-D convolution (JAX issue page workload) ---------------
+
+from oracle import dwconv as dw  # noqa: E402
+
+
+@pytest.mark.parametrize("K,C,d", [(1, 4, 1), (4, 8, 1), (4, 8, 3), (16, 5, 8), (3, 6, 64)])
+def test_dwconv1d_equals_grouped_conv(K, C, d):
+    """Library special case: torch's grouped conv1d with groups = channels and
+    the same dilation, in fp64, on the NCT layout."""
+    r = np.random.default_rng(K * 100 + C * 10 + d)
+    T = 37
+    x = r.standard_normal((2, T + d * (K - 1), C))
+    w = r.standard_normal((K, C))
+    y = dw.dwconv1d(x, w, d)
+    ref = F.conv1d(torch.from_numpy(x).permute(0, 2, 1), torch.from_numpy(w.T.copy()).unsqueeze(1),
+                   dilation=d, groups=C).permute(0, 2, 1).numpy()
+    assert y.shape == (2, T, C)
+    assert rel(y, ref) <= 1e-13
+
+
+def test_dwconv1d_closed_forms():
+    """K = 1 scales the input; a one-hot kernel at tap k0 shifts it by k0*d;
+    channels never mix."""
+    r = np.random.default_rng(7)
+    x = r.standard_normal((3, 50, 4))
+    w1 = r.standard_normal((1, 4))
+    assert np.array_equal(dw.dwconv1d(x, w1, 5), x * w1[0])
+    K, d, k0 = 5, 3, 2
+    T = 50 - d * (K - 1)
+    w = np.zeros((K, 4))
+    w[k0] = 1.0
+    assert np.array_equal(dw.dwconv1d(x, w, d), x[:, k0 * d:k0 * d + T, :])
+    x2 = x.copy()
+    x2[:, :, 1] += 100.0  # perturbing channel 1 leaves the other channels unchanged
+    wf = r.standard_normal((K, 4))
+    a, b = dw.dwconv1d(x, wf, d), dw.dwconv1d(x2, wf, d)
+    assert np.array_equal(a[:, :, [0, 2, 3]], b[:, :, [0, 2, 3]])
+
+
+def test_dwconv1d_phase_decomposition():
+    """Outputs whose step has residue r modulo d read only inputs with residue
+    r: the dilated conv equals d undilated convs on the phase subsequences."""
+    r = np.random.default_rng(11)
+    K, d, C = 4, 5, 3
+    T = 23
+    x = r.standard_normal((2, T + d * (K - 1), C))
+    w = r.standard_normal((K, C))
+    y = dw.dwconv1d(x, w, d)
+    for ph in range(d):
+        sub = dw.dwconv1d(x[:, ph::d, :], w, 1)
+        n = len(range(ph, T, d))
+        assert np.allclose(y[:, ph::d, :], sub[:, :n, :], rtol=0, atol=1e-12)
