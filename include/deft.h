@@ -198,6 +198,23 @@ int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, v
 int deft_halo_histogram(const deft_desc* d, const float* offsets, uint32_t* hist, int hist_len,
                         void* stream);
 
+/* Dilated depthwise 1-D convolution, the workload of the JAX issue page on
+ * grouped and dilated convolutions (its reproduction script: depthwise
+ * lax.conv_general_dilated with feature_group_count = channels, "NTC" input,
+ * "TIO" kernel with one input feature per group, stride 1, VALID padding,
+ * rhs_dilation = dilation).  fp32, device pointers:
+ *   x [batch][steps + dilation*(ksize-1)][channels]  (channel-minor)
+ *   w [ksize][channels]
+ *   y [batch][steps][channels]  (written)
+ *   y[b][t][c] = sum_k w[k][c] * x[b][t + k*dilation][c].
+ * channels a multiple of 4, 1 <= ksize <= 256, dilation >= 1, all pointers
+ * 16-byte aligned.  DEFT_ERR_BAD_DESC for sizes out of range (also when the
+ * input length exceeds 2^31 - 1 steps), DEFT_ERR_NULLPTR, DEFT_ERR_ALIGN; checks
+ * run before any launch.  batch = 0 or steps = 0 is a no-op.  Asynchronous on
+ * `stream`; the caller owns every buffer. */
+int deft_dwconv1d_forward(const float* x, const float* w, float* y, int batch, int steps, int channels,
+                          int ksize, int dilation, void* stream);
+
 /* Per-kernel timing for benchmarks (host-side events only; no device memory).
  * deft_timing_start(capacity) creates `capacity` event pairs for the calling
  * thread; while active, each kernel that deft_forward / deft_backward /

@@ -596,6 +596,20 @@ int deft_halo_histogram(const deft_desc* d, const float* offsets, uint32_t* hist
   return e == hipSuccess ? DEFT_OK : hip_fail(e);
 }
 
+int deft_dwconv1d_forward(const float* x, const float* w, float* y, int batch, int steps, int channels, int ksize,
+                          int dilation, void* stream) {
+  if (batch < 0 || steps < 0 || channels < 4 || channels % 4 || ksize < 1 || ksize > 256 || dilation < 1)
+    return DEFT_ERR_BAD_DESC;
+  const long long len = (long long)steps + (long long)dilation * (ksize - 1);
+  if (len > 0x7fffffffLL) return DEFT_ERR_BAD_DESC;
+  if (batch == 0 || steps == 0) return DEFT_OK;
+  if (!x || !w || !y) return DEFT_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return DEFT_ERR_ALIGN;
+  const hipError_t e =
+      deft::launch_dwconv1d(x, w, y, batch, steps, channels, ksize, dilation, (hipStream_t)stream);
+  return e == hipSuccess ? DEFT_OK : hip_fail(e);
+}
+
 int deft_timing_start(int capacity) {
   if (capacity < 1) return DEFT_ERR_BAD_DESC;
   Timing& t = g_timing;

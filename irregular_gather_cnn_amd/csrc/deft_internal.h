@@ -80,6 +80,9 @@ hipError_t launch_halo_hist(const deft_desc& d, int ho, int wo, const float* off
 
 hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b,
                                void* y, hipStream_t s);
+// dilated depthwise 1-D convolution (deft_dwconv.hip)
+hipError_t launch_dwconv1d(const float* x, const float* w, float* y, int B, int T, int C, int K, int d,
+                           hipStream_t st);
 // gather fused into the main GEMM (deft_igemm.hip)
 bool igemm_supported(const deft_plan& p);
 hipError_t launch_igemm(const deft_plan& p, const void* xh, const float* off, const void* wt, const void* b,

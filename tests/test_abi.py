@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     txt = open(os.path.join(ROOT, "include", "deft.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(deft_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(deft_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -266,6 +266,28 @@ def test_other_entry_points_validate():
     assert lib.deft_debug_sample_index(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == -2
     p = L.deft_plan_create(d)
     assert lib.deft_debug_sample(p, FAKE, FAKE, None, None) == -4
+
+
+def test_dwconv1d_validation_before_launch():
+    lib = L.load()
+    ok = [FAKE, FAKE, FAKE, 2, 16, 8, 3, 2, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.deft_dwconv1d_forward(*a)
+
+    assert call(5, 6) == -1        # channels not a multiple of 4
+    assert call(5, 0) == -1
+    assert call(6, 0) == -1        # ksize
+    assert call(6, 257) == -1
+    assert call(7, 0) == -1        # dilation
+    assert call(3, -1) == -1       # batch
+    assert call(7, 1 << 30) == -1  # input longer than 2^31 - 1 steps
+    assert call(0, None) == -4
+    assert call(2, None) == -4
+    assert call(1, FAKE + 4) == -7
+    assert call(3, 0) == 0 and call(4, 0) == 0  # empty: nothing launched
 
 
 def test_error_strings():
