@@ -58,6 +58,7 @@ def main():
     ap.add_argument("--workload", default="train_bf16_n16_c256_56x56_s1")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    ap.add_argument("--no-dwconv", action="store_true", help="skip the dilated depthwise conv timings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) after the timed steps, as the "
                          "reference kernel for scaling hardware byte counters")
@@ -221,6 +222,28 @@ def main():
     fusion["unfused_kernels_ms"] = {k: round(sum(v) / len(v), 5) for k, v in un.items()}
     log("fusion: %s" % fusion)
 
+    # Second workload: the dilated depthwise 1-D convolution of the JAX issue
+    # page (batch 32, 1024 steps, 512 channels, fp32, ramp inputs as there),
+    # timed per kernel size and dilation; algorithmic bytes = x + y + w once.
+    dwc = {}
+    if not args.no_dwconv:
+        B_, T_, C_ = 32, 1024, 512
+        for K_ in (4, 16, 64):
+            row = {}
+            for d_ in (1, 2, 4, 8, 16, 32, 64, 128):
+                L_ = T_ + d_ * (K_ - 1)
+                xd = torch.arange(B_ * L_ * C_, dtype=torch.float32, device=dev).div_(B_ * L_ * C_).view(B_, L_, C_)
+                wd = torch.arange(K_ * C_, dtype=torch.float32, device=dev).div_(K_ * C_).view(K_, C_)
+                yd = torch.empty((B_, T_, C_), dtype=torch.float32, device=dev)
+                fn = lambda: L.deft_dwconv1d_forward(xd, wd, yd, B_, T_, C_, K_, d_,
+                                                     torch.cuda.current_stream().cuda_stream)
+                ms_ = time_forward(fn)
+                nbytes = 4.0 * (B_ * L_ * C_ + B_ * T_ * C_ + K_ * C_)
+                row[str(d_)] = {"us": round(ms_ * 1e3, 1), "gbs": round(nbytes / (ms_ * 1e-3) / 1e9, 1)}
+                del xd, wd, yd
+            dwc["k%d" % K_] = row
+        log("dilated depthwise conv (32x1024x512 fp32): %s" % dwc)
+
     total_flop = sum(f for k, (b_, f) in work.items())
     gflops = total_flop / (ms_step * 1e-3) / 1e9
 
@@ -257,6 +280,7 @@ def main():
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
         "fusion": fusion,
+        "depthwise_dilated_1d": dwc or None,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

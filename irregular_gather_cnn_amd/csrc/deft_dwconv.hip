@@ -24,6 +24,7 @@ struct DwParams {
   float4* y;        // [B][T][C/4]
   int B, T, L, C4, K, d;
   int R, P, TJ, CV;          // non-empty phases, phases / steps / float4 lanes per tile
+  int four;                  // 1: four phase steps per thread (enough work items for the workgroup)
   int pgroups, jtiles, cchunks;
 };
 
@@ -59,24 +60,64 @@ __global__ __launch_bounds__(256) void k_dwconv1d(const DwParams p) {
   }
   __syncthreads();
 
-  const int items = p.TJ * per_row;
-  for (int e = threadIdx.x; e < items; e += 256) {
-    const int jl = e / per_row, rem = e - jl * per_row;
-    const int pl = rem / p.CV, v = rem - pl * p.CV;
-    const int r = r0 + pl, j = j0 + jl;
-    if (r >= p.R || c40 + v >= p.C4) continue;
-    const int t = r + p.d * j;
-    if (t >= p.T) continue;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4* xr = xs + (size_t)jl * per_row + pl * p.CV + v;
-    for (int k = 0; k < p.K; ++k) {
-      const float4 xv = xr[(size_t)k * per_row], wv = ws[k * p.CV + v];
-      acc.x = __builtin_fmaf(wv.x, xv.x, acc.x);
-      acc.y = __builtin_fmaf(wv.y, xv.y, acc.y);
-      acc.z = __builtin_fmaf(wv.z, xv.z, acc.z);
-      acc.w = __builtin_fmaf(wv.w, xv.w, acc.w);
+  if (!p.four) {
+    // short phases (large dilation and kernel): one output row per thread
+    for (int e = threadIdx.x; e < p.TJ * per_row; e += 256) {
+      const int jl = e / per_row, rem = e - jl * per_row;
+      const int pl = rem / p.CV, v = rem - pl * p.CV;
+      const int r = r0 + pl, j = j0 + jl;
+      if (r >= p.R || c40 + v >= p.C4) continue;
+      if (j >= (p.T - r + p.d - 1) / p.d) continue;
+      const float4* xr = xs + (size_t)jl * per_row + pl * p.CV + v;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < p.K; ++k) {
+        const float4 xv = xr[(size_t)k * per_row], wv = ws[k * p.CV + v];
+        acc.x = __builtin_fmaf(wv.x, xv.x, acc.x);
+        acc.y = __builtin_fmaf(wv.y, xv.y, acc.y);
+        acc.z = __builtin_fmaf(wv.z, xv.z, acc.z);
+        acc.w = __builtin_fmaf(wv.w, xv.w, acc.w);
+      }
+      p.y[yb + ((size_t)r + (size_t)p.d * j) * p.C4 + c40 + v] = acc;
     }
-    p.y[yb + (size_t)t * p.C4 + c40 + v] = acc;
+    return;
+  }
+  // each thread computes four consecutive phase steps of one (phase, 4
+  // channels) with a sliding window of input rows in registers: per tap one
+  // weight and one new input row are read from LDS for 16 FMAs
+  const int items = (p.TJ / 4) * per_row;  // TJ is a multiple of 4
+  for (int e = threadIdx.x; e < items; e += 256) {
+    const int jg = e / per_row, rem = e - jg * per_row;
+    const int pl = rem / p.CV, v = rem - pl * p.CV;
+    const int r = r0 + pl, jl0 = 4 * jg;
+    if (r >= p.R || c40 + v >= p.C4) continue;
+    const float4* xr = xs + (size_t)jl0 * per_row + pl * p.CV + v;
+    float4 acc[4], win[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    win[0] = xr[0];
+    win[1] = xr[per_row];
+    win[2] = xr[2 * per_row];
+#pragma unroll 4
+    for (int k = 0; k < p.K; ++k) {
+      win[3] = xr[(size_t)(k + 3) * per_row];  // row jl0 + k + 3 <= TJ + K - 2
+      const float4 wv = ws[k * p.CV + v];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[u].x = __builtin_fmaf(wv.x, win[u].x, acc[u].x);
+        acc[u].y = __builtin_fmaf(wv.y, win[u].y, acc[u].y);
+        acc[u].z = __builtin_fmaf(wv.z, win[u].z, acc[u].z);
+        acc[u].w = __builtin_fmaf(wv.w, win[u].w, acc[u].w);
+      }
+      win[0] = win[1];
+      win[1] = win[2];
+      win[2] = win[3];
+    }
+    const int n_r = (p.T - r + p.d - 1) / p.d;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + jl0 + u;
+      if (j < n_r) p.y[yb + ((size_t)r + (size_t)p.d * j) * p.C4 + c40 + v] = acc[u];
+    }
   }
 }
 
@@ -87,15 +128,15 @@ void dwconv1d_tile(int T, int C, int K, int d, int* tj, int* pp, int* cv, int* l
   const int R = d < T ? d : T;
   const int n_max = (T + d - 1) / d;
   int TJ = n_max < 64 ? n_max : 64;
-  if (TJ < 1) TJ = 1;
+  TJ = (TJ + 3) / 4 * 4;  // whole groups of four phase steps per thread
   int P = 64 / TJ;
   if (P < 1) P = 1;
   if (P > R) P = R > 0 ? R : 1;
   const int CV = C / 4 < 16 ? C / 4 : 16;
   auto bytes = [&](int tjv, int pv) { return ((tjv + K - 1) * pv + K) * CV * 16; };
-  while (bytes(TJ, P) > 65536 && (P > 1 || TJ > 1)) {
+  while (bytes(TJ, P) > 65536 && (P > 1 || TJ > 4)) {
     if (P > 1) P /= 2;
-    else TJ /= 2;
+    else TJ = (TJ / 2 + 3) / 4 * 4;
   }
   *tj = TJ; *pp = P; *cv = CV; *lds = bytes(TJ, P);
 }
@@ -112,6 +153,7 @@ hipError_t launch_dwconv1d(const float* x, const float* w, float* y, int B, int 
   p.pgroups = (p.R + p.P - 1) / p.P;
   p.jtiles = ((T + d - 1) / d + p.TJ - 1) / p.TJ;
   p.cchunks = (p.C4 + p.CV - 1) / p.CV;
+  p.four = (p.TJ / 4) * p.P * p.CV >= 256 ? 1 : 0;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const size_t grid = (size_t)B * p.pgroups * p.jtiles * p.cchunks;
   if (grid == 0) return hipSuccess;
