@@ -1,4 +1,5 @@
-"""CPU oracle for the dilated depthwise 1-D convolution -- test infrastructure.
+"""CPU oracle for the dilated depthwise 1-D convolution and the fused
+depthwise + pointwise module -- test infrastructure.
 
 Only ``tests/`` and ``bench.py``'s CPU-baseline leg may import this module; the
 product path never does.
@@ -32,3 +33,13 @@ def dwconv1d(x: np.ndarray, w: np.ndarray, dilation: int) -> np.ndarray:
     for k in range(K):
         y += w[k][None, None, :] * x[:, k * dilation:k * dilation + T, :]
     return y
+
+
+def dwpw1d(x: np.ndarray, w_dw: np.ndarray, w_pw: np.ndarray, dilation: int) -> np.ndarray:
+    """Depthwise then pointwise, the pair the FCM abstract fuses: the dilated
+    depthwise convolution above, then a 1x1 convolution mixing channels,
+    z[b, t, o] = sum_c y[b, t, c] * w_pw[c, o] ("TIO" kernel with one tap).
+    x [B][T + d(K-1)][C], w_dw [K][C], w_pw [C][O] -> z [B][T][O] (float64);
+    the channel mix is one matrix product per batch."""
+    y = dwconv1d(x, w_dw, dilation)
+    return y @ np.asarray(w_pw, np.float64)

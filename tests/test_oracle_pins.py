@@ -436,3 +436,24 @@ def test_dwconv1d_phase_decomposition():
         sub = dw.dwconv1d(x[:, ph::d, :], w, 1)
         n = len(range(ph, T, d))
         assert np.allclose(y[:, ph::d, :], sub[:, :n, :], rtol=0, atol=1e-12)
+
+
+def test_dwpw1d_equals_grouped_then_pointwise_conv():
+    """Library composition: torch's grouped conv1d (groups = channels) followed
+    by a 1x1 conv1d, in fp64; an identity pointwise kernel leaves the
+    depthwise result; a pointwise kernel that selects one channel picks it."""
+    r = np.random.default_rng(21)
+    B, T, C, O, K, d = 2, 29, 8, 12, 3, 4
+    x = r.standard_normal((B, T + d * (K - 1), C))
+    wd = r.standard_normal((K, C))
+    wp = r.standard_normal((C, O))
+    z = dw.dwpw1d(x, wd, wp, d)
+    xt = torch.from_numpy(x).permute(0, 2, 1)
+    y = F.conv1d(xt, torch.from_numpy(wd.T.copy()).unsqueeze(1), dilation=d, groups=C)
+    ref = F.conv1d(y, torch.from_numpy(wp.T.copy()).unsqueeze(2)).permute(0, 2, 1).numpy()
+    assert z.shape == (B, T, O)
+    assert rel(z, ref) <= 1e-13
+    assert np.allclose(dw.dwpw1d(x, wd, np.eye(C), d), dw.dwconv1d(x, wd, d), rtol=0, atol=1e-12)
+    sel = np.zeros((C, 1))
+    sel[5, 0] = 1.0
+    assert np.allclose(dw.dwpw1d(x, wd, sel, d)[:, :, 0], dw.dwconv1d(x, wd, d)[:, :, 5], rtol=0, atol=1e-12)
