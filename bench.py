@@ -242,7 +242,28 @@ def main():
                 row[str(d_)] = {"us": round(ms_ * 1e3, 1), "gbs": round(nbytes / (ms_ * 1e-3) / 1e9, 1)}
                 del xd, wd, yd
             dwc["k%d" % K_] = row
-        log("dilated depthwise conv (32x1024x512 fp32): %s" % dwc)
+        # fused depthwise + pointwise (512 -> 512 channels) against the
+        # depthwise kernel followed by a library fp32 matmul for the mix
+        O_ = 512
+        for K_, d_ in ((4, 1), (16, 8)):
+            L_ = T_ + d_ * (K_ - 1)
+            xd = torch.arange(B_ * L_ * C_, dtype=torch.float32, device=dev).div_(B_ * L_ * C_).view(B_, L_, C_)
+            wd = torch.arange(K_ * C_, dtype=torch.float32, device=dev).div_(K_ * C_).view(K_, C_)
+            wp = torch.arange(C_ * O_, dtype=torch.float32, device=dev).div_(C_ * O_).view(C_, O_)
+            yd = torch.empty((B_, T_, C_), dtype=torch.float32, device=dev)
+            zd = torch.empty((B_, T_, O_), dtype=torch.float32, device=dev)
+            st_ = torch.cuda.current_stream().cuda_stream
+            fused_ = time_forward(lambda: L.deft_dwpw1d_forward(xd, wd, wp, zd, B_, T_, C_, O_, K_, d_, st_))
+
+            def unfused_():
+                L.deft_dwconv1d_forward(xd, wd, yd, B_, T_, C_, K_, d_, st_)
+                torch.matmul(yd.view(-1, C_), wp, out=zd.view(-1, O_))
+            unf_ = time_forward(unfused_)
+            flop = 2.0 * B_ * T_ * C_ * (O_ + K_)
+            dwc["dwpw_k%d_d%d" % (K_, d_)] = {"fused_us": round(fused_ * 1e3, 1), "unfused_us": round(unf_ * 1e3, 1),
+                                              "fused_tflops": round(flop / (fused_ * 1e-3) / 1e12, 1)}
+            del xd, wd, wp, yd, zd
+        log("dilated depthwise conv (32x1024x512 fp32), fused depthwise+pointwise: %s" % dwc)
 
     total_flop = sum(f for k, (b_, f) in work.items())
     gflops = total_flop / (ms_step * 1e-3) / 1e9

@@ -215,6 +215,19 @@ int deft_halo_histogram(const deft_desc* d, const float* offsets, uint32_t* hist
 int deft_dwconv1d_forward(const float* x, const float* w, float* y, int batch, int steps, int channels,
                           int ksize, int dilation, void* stream);
 
+/* The depthwise convolution above followed by a pointwise (1x1) convolution,
+ * fused so that the depthwise result never reaches memory (the FCM abstract's
+ * fused depthwise + pointwise module).  fp32, device pointers:
+ *   x    [batch][steps + dilation*(ksize-1)][channels]
+ *   w_dw [ksize][channels]
+ *   w_pw [channels][out_channels]
+ *   z    [batch][steps][out_channels]  (written)
+ *   z[b][t][o] = sum_c w_pw[c][o] * sum_k w_dw[k][c] * x[b][t + k*dilation][c].
+ * channels and out_channels multiples of 32, 1 <= ksize <= 256, dilation >= 1,
+ * pointers 16-byte aligned; errors as for deft_dwconv1d_forward. */
+int deft_dwpw1d_forward(const float* x, const float* w_dw, const float* w_pw, float* z, int batch, int steps,
+                        int channels, int out_channels, int ksize, int dilation, void* stream);
+
 /* Per-kernel timing for benchmarks (host-side events only; no device memory).
  * deft_timing_start(capacity) creates `capacity` event pairs for the calling
  * thread; while active, each kernel that deft_forward / deft_backward /

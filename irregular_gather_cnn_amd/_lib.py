@@ -23,7 +23,7 @@ EXPORTED = ["deft_desc_validate", "deft_plan_create", "deft_plan_create_forced",
             "deft_backward",
             "deft_debug_sample_index", "deft_debug_sample", "deft_halo_histogram", "deft_error_string",
             "deft_last_hip_error", "deft_timing_start", "deft_timing_stop", "deft_timing_count",
-            "deft_timing_get", "deft_dwconv1d_forward"]
+            "deft_timing_get", "deft_dwconv1d_forward", "deft_dwpw1d_forward"]
 
 
 class DeftError(RuntimeError):
@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
         "deft_forward_unfused": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "deft_forward_hist": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp]),
         "deft_dwconv1d_forward": (i, [vp, vp, vp, i, i, i, i, i, vp]),
+        "deft_dwpw1d_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, vp]),
         "deft_backward": (i, [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]),
         "deft_debug_sample_index": (i, [dp, vp, vp, vp, vp, vp]),
         "deft_debug_sample": (i, [vp, vp, vp, vp, vp]),
@@ -173,6 +174,13 @@ def deft_forward_hist(plan, x, w_off, b_off, w, b, y, offsets_out, workspace, ws
 def deft_dwconv1d_forward(x, w, y, batch, steps, channels, ksize, dilation, stream=None) -> None:
     _check(load().deft_dwconv1d_forward(_ptr(x), _ptr(w), _ptr(y), int(batch), int(steps), int(channels),
                                         int(ksize), int(dilation), _ptr(stream)), "deft_dwconv1d_forward")
+
+
+def deft_dwpw1d_forward(x, w_dw, w_pw, z, batch, steps, channels, out_channels, ksize, dilation,
+                        stream=None) -> None:
+    _check(load().deft_dwpw1d_forward(_ptr(x), _ptr(w_dw), _ptr(w_pw), _ptr(z), int(batch), int(steps),
+                                      int(channels), int(out_channels), int(ksize), int(dilation), _ptr(stream)),
+           "deft_dwpw1d_forward")
 
 
 def deft_forward_unfused(plan, x, w_off, b_off, w, b, y, offsets, workspace, ws_bytes, stream=None) -> None:

@@ -610,6 +610,21 @@ int deft_dwconv1d_forward(const float* x, const float* w, float* y, int batch, i
   return e == hipSuccess ? DEFT_OK : hip_fail(e);
 }
 
+int deft_dwpw1d_forward(const float* x, const float* w_dw, const float* w_pw, float* z, int batch, int steps,
+                        int channels, int out_channels, int ksize, int dilation, void* stream) {
+  if (batch < 0 || steps < 0 || channels < 32 || channels % 32 || out_channels < 32 || out_channels % 32 ||
+      ksize < 1 || ksize > 256 || dilation < 1)
+    return DEFT_ERR_BAD_DESC;
+  const long long len = (long long)steps + (long long)dilation * (ksize - 1);
+  if (len > 0x7fffffffLL) return DEFT_ERR_BAD_DESC;
+  if (batch == 0 || steps == 0) return DEFT_OK;
+  if (!x || !w_dw || !w_pw || !z) return DEFT_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(w_dw) || !aligned16(w_pw) || !aligned16(z)) return DEFT_ERR_ALIGN;
+  const hipError_t e = deft::launch_dwpw1d(x, w_dw, w_pw, z, batch, steps, channels, out_channels, ksize, dilation,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? DEFT_OK : hip_fail(e);
+}
+
 int deft_timing_start(int capacity) {
   if (capacity < 1) return DEFT_ERR_BAD_DESC;
   Timing& t = g_timing;

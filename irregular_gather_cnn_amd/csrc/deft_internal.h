@@ -83,6 +83,9 @@ hipError_t launch_gemm_forward(const deft_plan& p, const void* wt, const void* c
 // dilated depthwise 1-D convolution (deft_dwconv.hip)
 hipError_t launch_dwconv1d(const float* x, const float* w, float* y, int B, int T, int C, int K, int d,
                            hipStream_t st);
+// fused depthwise + pointwise 1-D convolution (deft_dwpw.hip)
+hipError_t launch_dwpw1d(const float* x, const float* wdw, const float* wpw, float* z, int B, int T, int C, int O,
+                         int K, int d, hipStream_t st);
 // gather fused into the main GEMM (deft_igemm.hip)
 bool igemm_supported(const deft_plan& p);
 hipError_t launch_igemm(const deft_plan& p, const void* xh, const float* off, const void* wt, const void* b,

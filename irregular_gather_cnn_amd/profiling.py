@@ -37,6 +37,7 @@ KERNELS = {
     "sample_only": (r"k_sample<[^>]*, false|k_sample_direct<1, 2>", ["deft_sample.hip", "deft_device.h"]),
     "fused_gather_gemm": (r"k_igemm\b", ["deft_igemm.hip", "deft_device.h"]),
     "dwconv1d": (r"k_dwconv1d\b", ["deft_dwconv.hip"]),
+    "dwpw1d": (r"k_dwpw1d\b", ["deft_dwpw.hip"]),
     "gemm_forward": (r"k_gemm_dl<.*DlFwd|k_gemm<.*FwdOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dw": (r"k_gemm_dl<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),

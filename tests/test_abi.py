@@ -290,6 +290,24 @@ def test_dwconv1d_validation_before_launch():
     assert call(3, 0) == 0 and call(4, 0) == 0  # empty: nothing launched
 
 
+def test_dwpw1d_validation_before_launch():
+    lib = L.load()
+    ok = [FAKE, FAKE, FAKE, FAKE, 2, 16, 64, 32, 3, 2, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.deft_dwpw1d_forward(*a)
+
+    assert call(6, 48) == -1   # channels not a multiple of 32
+    assert call(7, 40) == -1   # out_channels
+    assert call(8, 0) == -1
+    assert call(9, 0) == -1
+    assert call(2, None) == -4
+    assert call(3, FAKE + 8) == -7
+    assert call(4, 0) == 0
+
+
 def test_error_strings():
     for code in range(-10, 1):
         s = L.deft_error_string(code)

@@ -93,3 +93,45 @@ def test_dwconv1d_empty_is_a_no_op():
     L.deft_dwconv1d_forward(None, None, y, 2, 0, 8, 3, 2, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert float(y.item()) == 7.0
+
+
+# --- fused depthwise + pointwise ------------------------------------------------
+
+def run_dwpw(x, wd, wp, d):
+    B, Lx, C = x.shape
+    K, O = wd.shape[0], wp.shape[1]
+    T = Lx - d * (K - 1)
+    t = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (x, wd, wp)]
+    z = torch.full((B, T, O), float("nan"), dtype=torch.float32, device="cuda")
+    L.deft_dwpw1d_forward(t[0], t[1], t[2], z, B, T, C, O, K, d, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return z.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,T,C,O,K,d", [
+    (2, 1024, 512, 512, 4, 1),   # the benchmark shape, fewer batches
+    (2, 1024, 128, 128, 16, 8),
+    (3, 100, 64, 288, 3, 2),     # ragged steps, output channels past one 256-wide tile
+    (1, 7, 32, 32, 1, 1),
+    (2, 70, 96, 64, 64, 3),
+])
+def test_dwpw1d_matches_oracle(B, T, C, O, K, d):
+    r = np.random.default_rng(B + T + C + O + K + d)
+    x = r.standard_normal((B, T + d * (K - 1), C)).astype(np.float32)
+    wd = r.standard_normal((K, C)).astype(np.float32)
+    wp = (r.standard_normal((C, O)) / np.sqrt(C)).astype(np.float32)
+    print("dwpw1d", (B, T, C, O, K, d), flush=True)
+    z = run_dwpw(x, wd, wp, d)
+    assert np.isfinite(z).all()
+    assert rel(z, dw.dwpw1d(x, wd, wp, d)) <= 1e-5
+
+
+def test_dwpw1d_page_ramps():
+    """The JAX page's ramp inputs through the fused module (channel mix by a
+    ramp kernel too)."""
+    B, T, C, O, K, d = 2, 256, 128, 64, 4, 16
+    x = ramp((B, T + d * (K - 1), C))
+    wd = ramp((K, C))
+    wp = ramp((C, O))
+    z = run_dwpw(x, wd, wp, d)
+    assert rel(z, dw.dwpw1d(x, wd, wp, d)) <= 1e-5
