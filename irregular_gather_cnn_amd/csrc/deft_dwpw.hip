@@ -4,12 +4,12 @@
 // The FCM abstract fuses a depthwise convolution with the pointwise (1x1)
 // convolution that follows it so that the depthwise output never goes to
 // memory.  Here the depthwise result is produced where the pointwise GEMM
-// consumes it: a workgroup owns 64 time steps x 256 output channels; for each
+// consumes it: a workgroup owns 64 time steps x 512 output channels; for each
 // slice of 32 input channels its threads compute the 64 x 32 depthwise
 // outputs (K taps at dilation d, read through the caches) straight into LDS,
-// stage the 32 x 256 slice of the pointwise weights next to them, and the
+// stage the 32 x 512 slice of the pointwise weights next to them, and the
 // 2 x 2 waves run the channel mix on the fp32 MFMA units (32x32x2, each wave
-// 32 steps x 128 output channels).  The depthwise arithmetic is the fused
+// 32 steps x 256 output channels).  The depthwise arithmetic is the fused
 // multiply-add chain over k of the depthwise kernel; the mix sums in the
 // MFMA's order.
 #include "deft_device.h"
@@ -18,7 +18,7 @@
 namespace deft {
 
 namespace {
-constexpr int kRT = 64, kOT = 256, kCS = 32;  // steps, output channels, input channels per stage
+constexpr int kRT = 64, kOT = 512, kCS = 32;  // steps, output channels, input channels per stage
 constexpr int kAS = kCS + 1;                  // LDS row stride of the depthwise tile (floats)
 constexpr int kBS = kOT + 4;                  // LDS row stride of the weight slice (floats)
 }  // namespace
@@ -32,8 +32,9 @@ struct DwpwParams {
 };
 
 __global__ __launch_bounds__(256) void k_dwpw1d(const DwpwParams p) {
-  __shared__ float As[kRT * kAS];
-  __shared__ __align__(16) float Bs[kCS * kBS];
+  extern __shared__ __align__(16) float smem_f[];
+  float* Bs = smem_f;                 // [kCS][kBS]
+  float* As = smem_f + kCS * kBS;     // [kRT][kAS]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -44,9 +45,9 @@ __global__ __launch_bounds__(256) void k_dwpw1d(const DwpwParams p) {
   const int t0 = tt * kRT, o0 = ot * kOT;
   const float* __restrict__ xb = p.x + (size_t)b * p.L * p.C;
 
-  f32x16_t acc[4];
+  f32x16_t acc[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
@@ -73,11 +74,11 @@ __global__ __launch_bounds__(256) void k_dwpw1d(const DwpwParams p) {
       ar[0] = a0.x; ar[1] = a0.y; ar[2] = a0.z; ar[3] = a0.w;
       ar[4] = a1.x; ar[5] = a1.y; ar[6] = a1.z; ar[7] = a1.w;
     }
-    // pointwise weights of this slice: 32 rows x 256 columns, float4 per thread x 8
+    // pointwise weights of this slice: 32 rows x 512 columns, float4 per thread x 16
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = tid + 256 * j;  // float4 index in the 32 x 64 grid
-      const int r = e >> 6, c4 = e & 63;
+    for (int j = 0; j < 16; ++j) {
+      const int e = tid + 256 * j;  // float4 index in the 32 x 128 grid
+      const int r = e >> 7, c4 = e & 127;
       const int o = o0 + c4 * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (o < p.O) v = *(const float4*)(p.wpw + (size_t)(c0 + r) * p.O + o);
@@ -90,18 +91,18 @@ __global__ __launch_bounds__(256) void k_dwpw1d(const DwpwParams p) {
       const int kr = 2 * kk + (lane >> 5);
       const float a = As[(wm * 32 + (lane & 31)) * kAS + kr];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float bv = Bs[kr * kBS + wn * 128 + j * 32 + (lane & 31)];
+      for (int j = 0; j < 8; ++j) {
+        const float bv = Bs[kr * kBS + wn * 256 + j * 32 + (lane & 31)];
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, acc[j], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
-  // element r of block j: step t0 + wm*32 + acc_row(lane, r), output o0 + wn*128 + j*32 + lane%32
+  // element r of block j: step t0 + wm*32 + acc_row(lane, r), output o0 + wn*256 + j*32 + lane%32
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int o = o0 + wn * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < 8; ++j) {
+    const int o = o0 + wn * 256 + j * 32 + (lane & 31);
     if (o >= p.O) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -122,7 +123,10 @@ hipError_t launch_dwpw1d(const float* x, const float* wdw, const float* wpw, flo
   const size_t grid = (size_t)B * p.ttiles * p.otiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidValue;
-  DEFT_LAUNCH("dwpw1d", k_dwpw1d, dim3((unsigned)grid), dim3(256), 0, st, p);
+  const int lds = (kCS * kBS + kRT * kAS) * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)k_dwpw1d, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  DEFT_LAUNCH("dwpw1d", k_dwpw1d, dim3((unsigned)grid), dim3(256), lds, st, p);
   return hipGetLastError();
 }
 
