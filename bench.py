@@ -59,6 +59,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
     ap.add_argument("--no-dwconv", action="store_true", help="skip the dilated depthwise conv timings")
+    ap.add_argument("--no-other", action="store_true", help="skip the forward at the other configurations")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) after the timed steps, as the "
                          "reference kernel for scaling hardware byte counters")
@@ -222,6 +223,55 @@ def main():
     fusion["unfused_kernels_ms"] = {k: round(sum(v) / len(v), 5) for k, v in un.items()}
     log("fusion: %s" % fusion)
 
+    # The forward at the other configurations of the layer (fp32, wide offsets
+    # with 4 groups and pushed taps, stride 2): fused sampling kernel GB/s and
+    # main GEMM MFMA share against the peak of each dtype, planned from each
+    # workload's own offset histogram.
+    others = {}
+    if not args.no_other:
+        for oname in ("fp32_n8_c128_64x64", "bf16_n16_c512_28x28_g4_wide", "train_bf16_n16_c256_56x56_s2"):
+            owl = WORKLOADS[oname]
+            otd = torch.bfloat16 if owl.dtype == "bf16" else torch.float32
+            oin = make_inputs(owl)
+            ot = {k: torch.from_numpy(v).to(otd).to(dev) for k, v in oin.items()}
+            ogeo = dict(n=owl.n, c_in=owl.c_in, h=owl.h, w=owl.w, c_out=owl.c_out, kh=owl.kh, kw=owl.kw,
+                        stride=(owl.stride,) * 2, pad=(owl.pad,) * 2, dil=(owl.dil,) * 2, groups=owl.groups,
+                        dtype=owl.dtype)
+            oprobe = DeformConv(**ogeo, training=True, device=dev)
+            _, ooff = oprobe.forward(ot["x"], ot["w_off"], ot["b_off"], ot["w"], ot["b"])
+            ohist = halo_histogram(oprobe.desc, ooff, 16)
+            del oprobe
+            olayer = DeformConv(**ogeo, plan=ohist, training=owl.train, device=dev)
+            oy = torch.empty((owl.n, owl.c_out, owl.ho, owl.wo), dtype=otd, device=dev)
+            oof = torch.empty((owl.n, owl.oc, owl.ho, owl.wo), dtype=torch.float32, device=dev)
+            ofn = lambda: olayer.forward(ot["x"], ot["w_off"], ot["b_off"], ot["w"], ot["b"], y=oy,
+                                         offsets=oof if owl.train else None)
+            fwd_ms_o = time_forward(ofn)
+            L.deft_timing_start(8 * args.steps)
+            for _ in range(args.steps):
+                ofn()
+            L.deft_timing_stop()
+            oper = {}
+            for i in range(L.deft_timing_count()):
+                name, ms = L.deft_timing_get(i)
+                oper.setdefault(name, []).append(ms)
+            owork = kernel_work(owl)
+            rec = {"fwd_ms": round(fwd_ms_o, 4), "plan": {k: olayer.info[k] for k in ("tile_h", "tile_w", "halo",
+                                                                                          "gather_direct")}}
+            for kname in ("fused_offset_sample", "gemm_forward"):
+                if kname in oper:
+                    avg = sum(oper[kname]) / len(oper[kname])
+                    b_, f_ = owork[kname]
+                    rec[kname] = {"us": round(avg * 1e3, 1), "gbs": round(b_ / (avg * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(b_ / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    if kname == "gemm_forward":
+                        tf = f_ / (avg * 1e-3) / 1e12
+                        rec[kname]["tflops"] = round(tf, 1)
+                        rec[kname]["mfma_frac"] = round(tf / MFMA_PEAK_TFLOPS[owl.dtype], 4)
+            others[oname] = rec
+            del olayer, ot, oy, oof
+        log("other configurations (forward): %s" % others)
+
     # Second workload: the dilated depthwise 1-D convolution of the JAX issue
     # page (batch 32, 1024 steps, 512 channels, fp32, ramp inputs as there),
     # timed per kernel size and dilation; algorithmic bytes = x + y + w once.
@@ -302,6 +352,7 @@ def main():
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
         "fusion": fusion,
         "depthwise_dilated_1d": dwc or None,
+        "other_configs_forward": others or None,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -315,10 +315,9 @@ __host__ __device__ inline uint32_t rsrc_bytes(size_t bytes) {
 }
 
 // ---- forward: C[m = q][n = co] = sum_k cols[q][k] Wt[co][k]; y[img][co][p] = C + b[co] ----
-struct DlFwd {
-  // 128 pixels x 256 output channels, two workgroups per CU; the weights (L2
-  // resident) need only a 2-deep ring (84 us against 92 us for 256 x 256)
-  using Cfg = GemmCfg<128, 256, 3, 2, 2>;
+template <class CfgT>
+struct DlFwdT {
+  using Cfg = CfgT;
   static constexpr bool A_KMAJ = false, B_KMAJ = false, LDS_EPILOGUE = true;
   const bf16_t* cols;  // [M][K]
   const bf16_t* wt;    // [N][K]
@@ -353,6 +352,14 @@ struct DlFwd {
   }
   __device__ void store_acc(const TileCoord&, int, int, const f32x16_t&, int) const {}
 };
+
+// Forward tiles: 128 pixels x 256 output channels, two workgroups per CU, with
+// a 2-deep ring for the L2-resident weights (84 us against 92 us for
+// 256 x 256 at 50 176 pixels); shapes with fewer pixels or output channels
+// take smaller tiles so the grid still covers the chip (at least 384 tiles).
+using DlFwd = DlFwdT<GemmCfg<128, 256, 3, 2, 2>>;
+using DlFwdMid = DlFwdT<GemmCfg<128, 128, 4, 2>>;
+using DlFwdSmall = DlFwdT<GemmCfg<64, 128, 4, 2>>;
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
@@ -493,14 +500,24 @@ void gemm_dl_dw_split(const deft_plan& p, int* splits, int* kper) {
   *splits = (P + k - 1) / k;
 }
 
-hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
-                           hipStream_t st) {
-  DlFwd op;
+template <class Op>
+static hipError_t dl_forward_with(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
+                                  hipStream_t st) {
+  Op op;
   op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
   op.M = p.d.n * p.ho * p.wo; op.N = p.d.c_out; op.K = p.ck; op.HoWo = p.ho * p.wo;
   op.div_howo = make_fastdiv(op.HoWo);
-  op.tilesM = tiles(op.M, DlFwd::Cfg::BM); op.tilesN = tiles(op.N, DlFwd::Cfg::BN);
+  op.tilesM = tiles(op.M, Op::Cfg::BM); op.tilesN = tiles(op.N, Op::Cfg::BN);
   return run_dl("gemm_forward", op, op.tilesM * op.tilesN, st);
+}
+
+hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
+                           hipStream_t st) {
+  const int M = p.d.n * p.ho * p.wo, N = p.d.c_out;
+  auto count = [&](int bm, int bn) { return tiles(M, bm) * tiles(N, bn); };
+  if (count(DlFwd::Cfg::BM, DlFwd::Cfg::BN) >= 384) return dl_forward_with<DlFwd>(p, wt, cols, b, y, st);
+  if (count(DlFwdMid::Cfg::BM, DlFwdMid::Cfg::BN) >= 384) return dl_forward_with<DlFwdMid>(p, wt, cols, b, y, st);
+  return dl_forward_with<DlFwdSmall>(p, wt, cols, b, y, st);
 }
 
 hipError_t dl_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
