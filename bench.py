@@ -97,9 +97,10 @@ def main():
     tot = float(sum(hist))
     log("offset std %.3f px; fully outside taps %.4f; required-halo histogram %s"
         % (float(off_h.std()), hist[-1] / tot, hist))
-    log("plan: tile %dx%d halo %d chunk %d, %d workgroups, %d B LDS, est. miss %.4f; backward tile %dx%d chunk %d"
-        % (info["tile_h"], info["tile_w"], info["halo"], info["chunk"], info["num_workgroups"],
-           info["lds_bytes"], info["est_miss_fraction"], info["bwd_tile_h"], info["bwd_tile_w"], info["bwd_chunk"]))
+    log("plan: tile %dx%d halo %d chunk %d, %d workgroups, %d B LDS; backward tile %dx%d chunk %d halo %d, "
+        "est. miss %.6f"
+        % (info["tile_h"], info["tile_w"], info["halo"], info["chunk"], info["num_workgroups"], info["lds_bytes"],
+           info["bwd_tile_h"], info["bwd_tile_w"], info["bwd_chunk"], info["bwd_halo"], info["est_miss_fraction"]))
 
     y = torch.empty((wl.n, wl.c_out, wl.ho, wl.wo), dtype=tdt, device=dev)
     offs = torch.empty((wl.n, wl.oc, wl.ho, wl.wo), dtype=torch.float32, device=dev)
@@ -346,7 +347,7 @@ def main():
                    "kernel": [wl.kh, wl.kw], "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil,
                    "offset_groups": wl.groups, "offset_std_px": wl.offset_std,
                    "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h",
-                                                 "bwd_tile_w", "bwd_chunk")}},
+                                                 "bwd_tile_w", "bwd_chunk", "bwd_halo")}},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),

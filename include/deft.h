@@ -72,13 +72,15 @@ typedef struct deft_plan deft_plan;
 
 typedef struct deft_plan_info {
   int tile_h, tile_w;     /* output pixels per workgroup tile of the fused kernel */
-  int halo;               /* LDS halo in input pixels around the tile's footprint */
+  int halo;               /* LDS halo in input pixels around the tile's footprint (LDS-halo
+                             forward; unused by the direct gather) */
   int chunk;              /* channels staged per LDS pass */
   int groups_per_wg;      /* offset groups handled by one workgroup */
   int num_workgroups;     /* fused-kernel grid size */
   int ho, wo, oc;
   int lds_bytes;          /* fused-kernel LDS per workgroup */
-  double est_miss_fraction; /* planner's estimate of taps outside the halo (-1: forced plan) */
+  double est_miss_fraction; /* planner's estimate of the share of taps outside bwd_halo, which
+                               take the backward's slow path (-1: forced plan) */
   size_t ws_forward, ws_training;
   size_t ws_cols_offset;  /* byte offset in the workspace of the deformed columns
                              [N*Ho*Wo][kh*kw][Cin] that deft_forward leaves there */
@@ -94,6 +96,9 @@ typedef struct deft_plan_info {
   int gather_gemm;        /* 1: the forward runs the offset conv, then one launch that gathers the
                              columns straight into the main GEMM's LDS tiles (y and the columns
                              written; the GEMM reads no columns from HBM) */
+  int bwd_halo;           /* the sampling backward's candidate window: taps whose corner lies
+                             within it of their grid position are scattered through LDS, the
+                             others one by one with global atomics */
 } deft_plan_info;
 
 /* Checks the descriptor alone.  Pure host function. */
@@ -103,12 +108,16 @@ int deft_desc_validate(const deft_desc* d);
  * histogram of deft_halo_histogram: hist[i] for i < hist_len-2 counts taps
  * whose corner (y0, x0) lies exactly i pixels (Chebyshev distance) from the
  * tap's grid position, hist[hist_len-2] counts taps at hist_len-2 or more,
- * hist[hist_len-1] counts fully outside taps.  NULL selects a default halo of
- * 2.  The planner sizes the halo so that the expected share of taps outside
- * it stays small and picks the tile and chunk from the LDS budget and the
- * launch shape (DefT page, "How DefT works", "The idea": pad each tile by
- * just enough margin that most sampled pixels stay on chip; "What it costs":
- * tile sizing depends on platform and layer shape).  Pure host function. */
+ * hist[hist_len-1] counts fully outside taps.  The forward's LDS halo, tile
+ * and chunk come from a cost estimate (columns written, input staged, taps
+ * outside the halo read from the caches, LDS occupancy and launch shape);
+ * the backward's halo is the smallest that leaves at most 1e-5 of the taps
+ * outside it besides those in the open-ended bin hist[hist_len-2], at most
+ * 16.  NULL: forward halo from default shares, backward halo 4.  (DefT
+ * page, "How DefT works", "The idea": pad each tile by just enough margin
+ * that most sampled pixels stay on chip; "What it costs": tile sizing
+ * depends on platform and layer shape.)  A forced plan uses its halo for
+ * both.  Pure host function. */
 int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len,
                      deft_plan** out);
 

@@ -49,7 +49,7 @@ class deft_plan_info(ctypes.Structure):
                 ("ws_training", ctypes.c_size_t), ("ws_cols_offset", ctypes.c_size_t),
                 ("bwd_tile_h", ctypes.c_int), ("bwd_tile_w", ctypes.c_int), ("bwd_chunk", ctypes.c_int),
                 ("gemm_direct", ctypes.c_int), ("dw_splits", ctypes.c_int), ("gather_direct", ctypes.c_int),
-                ("gather_gemm", ctypes.c_int)]
+                ("gather_gemm", ctypes.c_int), ("bwd_halo", ctypes.c_int)]
 
 
 _lib = None

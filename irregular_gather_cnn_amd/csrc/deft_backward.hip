@@ -1228,7 +1228,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.N = d.n; b.Cin = d.c_in; b.H = d.h; b.W = d.w; b.Ho = p.ho; b.Wo = p.wo; b.KH = d.kh; b.KW = d.kw;
   b.SH = d.stride_h; b.SW = d.stride_w; b.PH = d.pad_h; b.PW = d.pad_w; b.DH = d.dil_h; b.DW = d.dil_w;
   b.G = d.offset_groups; b.Cg = p.cg; b.K2 = p.taps; b.Oc = p.oc; b.Ck = p.ck;
-  b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.halo;
+  b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.bhalo;
   b.CC = p.chunk_b;
   b.dcstr = p.chunk_b + (p.bwd_mf ? 16 : (d.dtype == DEFT_BF16 ? 8 : 4));
   b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;

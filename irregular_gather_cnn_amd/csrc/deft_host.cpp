@@ -25,7 +25,6 @@ int hip_fail(hipError_t e) {
 }
 
 constexpr int kMaxLds = 160 * 1024;     // gfx950 LDS per workgroup
-constexpr int kTargetLds = 64 * 1024;   // keeps >= 2 workgroups per CU
 constexpr int kNumCUs = 256;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -112,8 +111,8 @@ bool layout_backward(deft_plan& p) {
   p.lb_dx = lx; p.lb_dc = lx + ldx; p.lb_cnt = lx + ldx + ldc; p.lb_total = total;
   // list capacity: every output pixel whose tap's grid point lies within the
   // halo (plus one row/column for the +1 corners) of the core, for every tap
-  const int wh = (p.btile_h + 2 * p.halo + 1 + d.stride_h - 1) / d.stride_h + 1;
-  const int ww = (p.btile_w + 2 * p.halo + 1 + d.stride_w - 1) / d.stride_w + 1;
+  const int wh = (p.btile_h + 2 * p.bhalo + 1 + d.stride_h - 1) / d.stride_h + 1;
+  const int ww = (p.btile_w + 2 * p.bhalo + 1 + d.stride_w - 1) / d.stride_w + 1;
   p.list_cap = s.taps * std::min(wh, s.ho) * std::min(ww, s.wo);
   // offset-weight backward: (image, channel slice, row band) workgroups; a
   // band's rows are staged at once, so bands are as tall as two workgroups
@@ -150,16 +149,17 @@ bool direct_ok(const deft_desc& d) {
 }
 
 // Fills every derived field of a plan for the given tile / halo / chunk
-// (direct: the forward gathers from the channel-minor copy; the halo then
-// only bounds the backward's candidate window).  Returns false if the LDS
-// does not fit.
-bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct = false) {
+// (direct: the forward gathers from the channel-minor copy and has no LDS
+// halo) and the backward's halo (negative: the forward's).  Returns false
+// if the LDS does not fit.
+bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct = false, int bhalo = -1) {
   const deft_desc& d = p.d;
   const Shape s = shape_of(d);
   if (direct && !direct_ok(d)) return false;
   p.direct = direct ? 1 : 0;
   p.ho = s.ho; p.wo = s.wo; p.taps = s.taps; p.oc = s.oc; p.cg = s.cg; p.ck = s.ck;
   p.tile_h = th; p.tile_w = tw; p.halo = halo; p.chunk = chunk;
+  p.bhalo = bhalo < 0 ? halo : bhalo;
   p.chunk_a = d.c_in % 64 == 0 ? 64 : (d.c_in % 32 == 0 ? 32 : 16);
   p.gw = 1;
   p.gsplit = d.offset_groups / p.gw;
@@ -253,12 +253,38 @@ double miss_fraction(const uint32_t* hist, int len, int halo) {
   return tot > 0 ? 1.0 - in / tot : 0.0;
 }
 
+// Backward halo: every tap whose corner lies beyond it goes to the
+// backward's slow path (one wave per tap, global atomics), measured at tens
+// of nanoseconds per tap and a tail of several microseconds for even a few
+// dozen taps, while each extra pixel of halo only widens the candidate scan
+// of the sampling backward by about one percent.  So it is the smallest halo
+// that leaves no more than 1e-5 of the taps outside, apart from those in the
+// histogram's open-ended last distance bin, which no halo it describes can
+// take in (capped at 16).  Without a histogram: 4 pixels.
+int backward_halo(const uint32_t* hist, int len) {
+  if (!hist || len < 3) return 4;
+  double tot = 0;
+  for (int i = 0; i < len - 1; ++i) tot += hist[i];
+  const double allowed = hist[len - 2] + 1e-5 * tot;
+  double in = 0;
+  const int hmax = std::min(16, len - 3);
+  for (int h = 0; h <= hmax; ++h) {
+    in += hist[h];
+    if (tot - in <= allowed) return h;
+  }
+  return hmax;
+}
+
 // Planner: pick (tile, halo, chunk) minimising a byte-cost estimate of the
 // fused kernel: the columns it must write, the input staged into LDS (served
 // mostly from L2, weighted down), the taps outside the halo, each of which
-// reads four corners per channel from global memory uncoalesced (weighted up),
-// and a fixed cost per channel-chunk pass, divided by the fraction of the
-// machine the launch keeps busy.
+// reads its four corners per channel from global memory (mostly L2 hits:
+// measured on 64 x 64 fp32, a third of the taps outside the halo costs the
+// kernel about 4 %, so they are weighted by their bytes alone), and a fixed
+// cost per channel-chunk pass, divided by the fraction of the machine the
+// launch keeps busy.  A region so large that only one workgroup fits a CU
+// leaves four waves to hide the gather latency: measured 1.7 to 1.8 times
+// slower than two per CU, whatever the halo saves.
 int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len) {
   const Shape s = shape_of(d);
   static const int tiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}, {4, 4}, {2, 16}, {16, 2}, {2, 8}, {1, 16}};
@@ -277,8 +303,7 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
         const double pt = (double)t[0] * t[1];
         const double per_tile_stage = (double)p.reg_h * p.reg_w * s.cg + (double)p.foot_h * p.foot_w * d.c_in;
         const double stage_bytes = (double)p.num_wg * per_tile_stage * s.esz;
-        // a missed tap costs its uncoalesced reads here and again in the backward
-        const double miss_bytes = miss * samples * 4.0 * s.esz * 32.0;
+        const double miss_bytes = miss * samples * 4.0 * s.esz;
         const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
         const double slots = (double)kNumCUs * occ;
         const double waves = std::ceil(p.num_wg / slots);
@@ -287,21 +312,19 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
         // two barriers, about as much as moving 16 KB
         const double passes = (double)p.num_wg * p.gw * (s.cg / chunk) + (double)p.num_wg * (d.c_in / p.chunk_a);
         double cost = (col_bytes + 0.25 * stage_bytes + miss_bytes + passes * 16384.0) / std::max(busy, 0.05);
-        if (p.lds_total > kTargetLds) cost *= 1.15;
+        if (occ == 1) cost *= 1.7;
         if (pt < 32) cost *= 1.1;  // phase-A MFMA blocks half empty
         if (cost < best_cost * 0.999) {
           best_cost = cost;
           best = p;
-          best.est_miss = miss;
           found = true;
         }
       }
     }
   }
   if (!found) return DEFT_ERR_UNSUPPORTED;
-  // Direct gather where supported: the halo chosen above still bounds the
-  // backward's candidate window; the tile only sets the forward's launch
-  // shape.  Every tile of 32..64 pixels is a candidate (fewer only when the
+  // Direct gather where supported: no LDS halo; the tile only sets the
+  // forward's launch shape.  Every tile of 32..64 pixels is a candidate (fewer only when the
   // output is smaller).  Cost: the columns of every pixel slot the launch
   // covers, including the empty slots of ragged edge tiles (their offset conv
   // and tap work is done anyway); the footprint each workgroup stages for its
@@ -338,11 +361,15 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
           dfound = true;
         }
       }
-    if (dfound) {
-      bd.est_miss = best.est_miss;
-      best = bd;
-    }
+    if (dfound) best = bd;
   }
+  // the backward's halo is set by the tap distances alone
+  const int bh = backward_halo(hist, hist_len);
+  deft_plan q;
+  q.d = d;
+  if (layout_plan(q, best.tile_h, best.tile_w, best.halo, best.chunk, best.direct != 0, bh) && q.chunk_b != 0)
+    best = q;
+  best.est_miss = miss_fraction(hist, hist_len, best.bhalo);
   return DEFT_OK;
 }
 
@@ -433,6 +460,7 @@ int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo
 int deft_plan_get_info(const deft_plan* p, deft_plan_info* info) {
   if (!p || !info) return DEFT_ERR_NULLPTR;
   info->tile_h = p->tile_h; info->tile_w = p->tile_w; info->halo = p->halo; info->chunk = p->chunk;
+  info->bwd_halo = p->bhalo;
   info->groups_per_wg = p->gw; info->num_workgroups = p->num_wg;
   info->ho = p->ho; info->wo = p->wo; info->oc = p->oc;
   info->lds_bytes = p->lds_total;

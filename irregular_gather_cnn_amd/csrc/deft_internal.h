@@ -12,6 +12,7 @@ struct deft_plan {
   int ho, wo, oc, taps, ck, cg;
   // fused sampling kernel
   int tile_h, tile_w, halo, chunk, chunk_a, gw, gsplit;
+  int bhalo;                   // sampling backward's candidate window (input pixels)
   int tiles_h, tiles_w, num_tiles, num_wg, mblocks;
   int foot_h, foot_w;          // nominal tile footprint (input pixels)
   int reg_h, reg_w;            // largest halo region (input pixels)

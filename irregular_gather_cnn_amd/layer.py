@@ -48,7 +48,8 @@ class DeformConv:
         self.hist = torch.zeros((hist_len,), dtype=torch.int32, device=device) if replan_every else None
         self.observed_calls, self.replans = 0, 0
 
-    PLAN_KEYS = ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h", "bwd_tile_w", "bwd_chunk")
+    PLAN_KEYS = ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h", "bwd_tile_w", "bwd_chunk",
+                 "bwd_halo")
 
     def observed_histogram(self):
         """The required-halo histogram accumulated since the last re-plan."""

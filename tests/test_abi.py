@@ -59,7 +59,7 @@ def test_plan_and_workspace_sizes():
     p = L.deft_plan_create(d)
     info = L.deft_plan_get_info(p)
     assert info["ho"] == 9 and info["wo"] == 11 and info["oc"] == 18
-    assert info["halo"] == 2  # default without a histogram
+    assert info["halo"] == 2 and info["bwd_halo"] == 4  # defaults without a histogram
     cols = 2 * 9 * 11 * 9 * 32 * 2
     assert info["ws_forward"] >= cols and info["ws_training"] >= info["ws_forward"] + cols
     assert L.deft_workspace_bytes(p, 0) == info["ws_forward"]
@@ -76,7 +76,24 @@ def test_planner_sizes_halo_from_histogram():
     pw = L.deft_plan_get_info(L.deft_plan_create(d, wide))
     assert pt["halo"] <= 3
     assert pw["halo"] > pt["halo"]
-    assert pt["est_miss_fraction"] < 0.01
+    # backward: the smallest halo leaving no tap outside but the open-ended bin
+    assert pt["bwd_halo"] == 3 and pt["est_miss_fraction"] == 0.0
+    assert pw["bwd_halo"] == 13 and abs(pw["est_miss_fraction"] - 100 / 1500) < 1e-12
+    # 1e-5 of the taps may stay outside
+    assert L.deft_plan_get_info(L.deft_plan_create(d, [10 ** 6, 5, 0, 0, 0, 0, 0, 0]))["bwd_halo"] == 0
+    assert L.deft_plan_get_info(L.deft_plan_create(d, [10 ** 6, 20, 0, 0, 0, 0, 0, 0]))["bwd_halo"] == 1
+
+
+def test_forward_halo_avoids_single_workgroup_occupancy():
+    """fp32 64 x 64 with offsets of about a pixel: halo 4 needs more than
+    80 KB of LDS (one workgroup per CU, measured 1.8x slower than halo 2 at
+    two per CU), so the forward takes a smaller halo while the backward's
+    halo still covers every tap."""
+    d = desc(n=8, c_in=128, h=64, w=64, c_out=128, dtype=L.DEFT_F32)
+    hist = [33919, 161534, 80818, 12822, 729, 15, 0, 0, 0, 0, 0, 0, 0, 0, 0, 5075]
+    info = L.deft_plan_get_info(L.deft_plan_create(d, hist))
+    assert info["lds_bytes"] <= 80 * 1024 and info["halo"] >= 1
+    assert info["bwd_halo"] == 5
 
 
 def test_forced_plan_limits():

@@ -241,7 +241,7 @@ def test_replanning_from_observed_offsets(dtype):
     layer = make_layer(wl, plan=(4, 8, 0, 0), training=True)
     layer.replan_every, layer.hist_len = 2, 16
     layer.hist = torch.zeros((16,), dtype=torch.int32, device="cuda")
-    halo0 = layer.info["halo"]
+    halo0 = layer.info["bwd_halo"]
     y0_, off0 = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
     y0_, off0 = y0_.clone(), off0.clone()
     layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
@@ -251,8 +251,8 @@ def test_replanning_from_observed_offsets(dtype):
     y1, off1 = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])  # re-plans first
     g = layer.backward(t["x"], t["w_off"], t["w"], off1, t["dy"])
     torch.cuda.synchronize()
-    say("  halo %d -> %d, replans %d" % (halo0, layer.info["halo"], layer.replans))
-    assert layer.replans == 1 and layer.info["halo"] > halo0
+    say("  backward halo %d -> %d, replans %d" % (halo0, layer.info["bwd_halo"], layer.replans))
+    assert layer.replans == 1 and layer.info["bwd_halo"] > halo0
     assert torch.equal(y1, y0_) and torch.equal(off1, off0)
     ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off1).astype(np.float64), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
