@@ -1012,23 +1012,23 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
       kinfo[kl] = ki;
     }
     __syncthreads();
-    // B tile: dOffset at the output pixel whose tap lands on the input pixel;
-    // eight (pixel, depth) gathers per thread in flight at a time
+    // B tile: dOffset at the output pixel whose tap lands on the input pixel.
+    // Lane = pixel, wave = depth index (stepping by 8): a wave's 64 gathers
+    // read one dOffset plane at a shifted run of consecutive pixels, a few
+    // cache lines; eight gathers per thread in flight at a time
     {
-      const int tot = 64 * len;
-      const FastDiv dlen = make_fastdiv(len);
-      for (int e0 = tid; e0 < tot; e0 += 512 * 8) {
+      const int pix = tid & 63;
+      const int q = pix0 + pix;
+      const int y = fdiv(q, p.div_w), xx = q - y * p.W;
+      for (int k0 = wave; k0 < len; k0 += 8 * 8) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 512;
-          const int pix = fdiv(e, dlen), kl = e - pix * len;
-          const int q = pix0 + pix;
-          const int y = fdiv(q, p.div_w), xx = q - y * p.W;
-          const int4 ki = kinfo[e < tot ? kl : 0];
+          const int kl = k0 + 8 * u;
+          const int4 ki = kinfo[kl < len ? kl : 0];
           v[u] = 0.f;
           const int ny = y + ki.y, nx = xx + ki.z;
-          if (e < tot && ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
+          if (kl < len && ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
             int ho = ny, wo = nx;
             bool ok = true;
             if (p.SH != 1) { ho = fdiv(ny, p.div_sh); ok = ho * p.SH == ny; }
@@ -1038,11 +1038,8 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 512;
-          if (e < tot) {
-            const int pix = fdiv(e, dlen), kl = e - pix * len;
-            bt[pix * bstr + kl] = Elem<T>::from_f32(v[u]);
-          }
+          const int kl = k0 + 8 * u;
+          if (kl < len) bt[pix * bstr + kl] = Elem<T>::from_f32(v[u]);
         }
       }
     }
