@@ -372,6 +372,26 @@ def test_backward_small_halo_misses(plan, dtype):
         assert e <= TOL[dtype], k
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_halo_planned_apart_from_forward(dtype):
+    """The planner sizes the backward's halo from the histogram on its own: a
+    histogram that claims offsets under one pixel gives a backward halo of 1,
+    while the offsets are about 2 px, so many taps take the backward's miss
+    path under a histogram-made plan; the gradients still match the oracle."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(dtype=dtype, train=True, n=2, c_in=32, c_out=24, h=13, w=11,
+                                                     offset_std=2.0)
+    say("backward halo from a tight histogram", dtype)
+    hist = [10 ** 6, 20] + [0] * 14
+    inp, layer, y, off, g = run_backward(wl, plan=hist)
+    say("  forward halo %d, backward halo %d" % (layer.info["halo"], layer.info["bwd_halo"]))
+    assert layer.info["bwd_halo"] == 1
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        e = rel(host(g[k]), ref[k])
+        say("  %s rel %.2e" % (k, e))
+        assert e <= TOL[dtype], k
+
+
 @pytest.mark.parametrize("case", [
     dict(n=3, c_in=48, c_out=40, h=12, w=10),             # ragged tiles in m, n and k; dW splits cross images
     dict(n=2, c_in=16, c_out=8, h=8, w=8),                # single partial tile everywhere
