@@ -1155,7 +1155,10 @@ __global__ __launch_bounds__(256) void k_prep_backward(const BwdParams b, const 
 // All weight and bias gradients from their partials, summed in a fixed order
 // and rounded once: dw[co][c][t] (from [ndw][co][t][c], one partial per
 // pixel range of the dW GEMM), dw_off[o][c][t] (from
-// [N*bands][o][t][c]), db, db_off (from [ch][N]).
+// [N*bands][o][t][c]), db, db_off (from [ch][N]).  Each thread sums one
+// element's partials in ascending order with up to 32 loads in flight; the
+// dw_off elements, which have the most partials (one per image and band),
+// come first so that they are not left for the end of the launch.
 template <typename T>
 __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ dwpart, int ndw, T* dw, int Cout,
                                                       const float* __restrict__ dwoffpart, T* dwoff, int Oc, int nwp,
@@ -1165,26 +1168,24 @@ __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ 
   const size_t n1 = (size_t)Cout * ck, n2 = (size_t)Oc * ck, n3 = (size_t)Cout + Oc;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2 + n3; e += (size_t)gridDim.x * 256) {
     if (e < n1 + n2) {
-      const bool first = e < n1;
-      const size_t f = first ? e : e - n1;  // partial order: [o][t][c]
-      const int fi = (int)f;                // weight tensors: below 2^31 elements
+      const bool woff = e < n2;
+      const size_t f = woff ? e : e - n2;  // partial order: [o][t][c]
+      const int fi = (int)f;               // weight tensors: below 2^31 elements
       const int r = fi / Cin, c = fi - r * Cin;
       const int o = r / K2, t = r - o * K2;
-      const float* src = first ? dwpart : dwoffpart;
-      const size_t stride = first ? n1 : n2;
-      const int cnt = first ? ndw : nwp;
-      // loads eight partials ahead, adds them in ascending z
+      const float* src = woff ? dwoffpart : dwpart;
+      const size_t stride = woff ? n2 : n1;
+      const int cnt = woff ? nwp : ndw;
       float s = 0.f;
-      int z = 0;
-      for (; z + 8 <= cnt; z += 8) {
-        float v[8];
+      for (int z = 0; z < cnt; z += 32) {
+        float v[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(z + u) * stride + f];
+        for (int u = 0; u < 32; ++u) v[u] = z + u < cnt ? src[(size_t)(z + u) * stride + f] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < 32; ++u)
+          if (z + u < cnt) s += v[u];
       }
-      for (; z < cnt; ++z) s += src[(size_t)z * stride + f];
-      (first ? dw : dwoff)[((size_t)o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
+      (woff ? dwoff : dw)[((size_t)o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
     } else {
       const int ch = (int)(e - n1 - n2);
       T* dst = ch < Cout ? db : dboff;
