@@ -730,7 +730,34 @@ __global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part
   const int o = blockIdx.x, img = blockIdx.y;
   const size_t base = ((size_t)img * Oc + o) * HoWo;
   float s = 0.f;
-  if ((HoWo & 3) == 0 && (n & 3) == 0) {
+  if ((HoWo & 3) == 0 && (n & 3) == 0 && chunks <= 4) {
+    // up to four chunks: two passes of four pixels per thread with all their
+    // 16-byte loads in flight together, summed in chunk order
+    for (int q0 = threadIdx.x * 4; q0 < HoWo; q0 += 256 * 4 * 2) {
+      float4 u[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = q0 + h * 256 * 4;
+          u[h][k] = (q < HoWo && k < chunks) ? *(const float4*)(part + (size_t)k * n + base + q)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = q0 + h * 256 * 4;
+        if (q >= HoWo) break;
+        float4 v = u[h][0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+          if (k < chunks) {
+            v.x += u[h][k].x; v.y += u[h][k].y; v.z += u[h][k].z; v.w += u[h][k].w;
+          }
+        *(float4*)(doff + base + q) = v;
+        s += (v.x + v.y) + (v.z + v.w);
+      }
+    }
+  } else if ((HoWo & 3) == 0 && (n & 3) == 0) {
     // four pixels per thread per pass; each chunk's partial one 16-byte load
     for (int q = threadIdx.x * 4; q < HoWo; q += 256 * 4) {
       float4 v = *(const float4*)(part + base + q);
