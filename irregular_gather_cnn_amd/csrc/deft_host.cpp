@@ -278,11 +278,12 @@ int backward_halo(const uint32_t* hist, int len) {
 // Planner: pick (tile, halo, chunk) minimising a byte-cost estimate of the
 // fused kernel: the columns it must write, the input staged into LDS (served
 // mostly from L2, weighted down), the taps outside the halo, each of which
-// reads its four corners per channel from global memory (mostly L2 hits:
-// measured on 64 x 64 fp32, a third of the taps outside the halo costs the
-// kernel about 4 %, so they are weighted by their bytes alone), and a fixed
-// cost per channel-chunk pass, divided by the fraction of the machine the
-// launch keeps busy.  A region so large that only one workgroup fits a CU
+// reads its four corners per channel from global memory (weighted by 0.4 of
+// those bytes: measured on 64 x 64 fp32 with offsets of about a pixel, a
+// third of the taps outside the halo costs the kernel about 4 %, while on the
+// 28 x 28 four-group layer with offsets of about 4 px, halo 1 against halo 8
+// costs 60 %), and a fixed cost per channel-chunk pass, divided by the
+// fraction of the machine the launch keeps busy.  A region so large that only one workgroup fits a CU
 // leaves four waves to hide the gather latency: measured 1.7 to 1.8 times
 // slower than two per CU, whatever the halo saves.
 int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len) {
@@ -303,7 +304,7 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
         const double pt = (double)t[0] * t[1];
         const double per_tile_stage = (double)p.reg_h * p.reg_w * s.cg + (double)p.foot_h * p.foot_w * d.c_in;
         const double stage_bytes = (double)p.num_wg * per_tile_stage * s.esz;
-        const double miss_bytes = miss * samples * 4.0 * s.esz;
+        const double miss_bytes = 0.4 * miss * samples * 4.0 * s.esz;
         const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
         const double slots = (double)kNumCUs * occ;
         const double waves = std::ceil(p.num_wg / slots);
