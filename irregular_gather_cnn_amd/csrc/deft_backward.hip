@@ -646,43 +646,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
 }
 
-// Taps beyond the halo (need > halo, not fully outside): every wave scans 64
-// taps (lane = tap); for each miss, the wave (lanes = channels) computes the
-// offset gradient from global memory and adds the dX contributions with
-// global atomics.  Runs after k_sample_bwd has written dX.
+// Taps beyond the halo (need > halo, not fully outside): a workgroup scans
+// 256 pixels of one (image, group, tap) plane, lane = pixel; for each miss,
+// the wave (lanes = channels) computes the offset gradient from global memory
+// and adds the dX contributions with global atomics.  Runs after k_sample_bwd
+// has written dX.  Grid: N*G*K2 planes x ceil(Ho*Wo / 256) blocks.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int HoWo = p.Ho * p.Wo;
-  const size_t total = (size_t)p.N * p.G * p.K2 * HoWo;
+  const int bpp = (HoWo + 255) / 256;  // blocks per plane
+  const int plane = blockIdx.x / bpp, blk = blockIdx.x - plane * bpp;  // uniform
+  const int r2 = plane / p.K2, t = plane - r2 * p.K2;
+  const int n = r2 / p.G, g = r2 - n * p.G;
+  const int ti = t / p.KW, tj = t - ti * p.KW;
   const size_t HW = (size_t)p.H * p.W;
   const T* __restrict__ x = (const T*)p.x;
   const T* __restrict__ dcol = (const T*)p.dcol;
-  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 64; base < total; base += (size_t)gridDim.x * 256) {
-    const size_t pid = base + lane;
+  const float* __restrict__ offp = p.off + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo;
+  const int wpix0 = blk * 256 + (threadIdx.x & ~63);  // first pixel of this wave
+  {
+    const int pix = wpix0 + lane;
     bool miss = false;
-    if (pid < total) {
-      const int pi = (int)pid;  // total < 2^31 (checked on the host)
-      const int r = pi / HoWo, pix = pi - r * HoWo;
-      const int r2 = r / p.K2, t = r - r2 * p.K2;
-      const int n = r2 / p.G, g = r2 - n * p.G;
+    if (pix < HoWo) {
       const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
-      const int ti = t / p.KW, tj = t - ti * p.KW;
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
-      const float* o = p.off + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
-      const TapIndex ix = tap_index(by, bx, o[0], o[HoWo], p.H, p.W);
+      const TapIndex ix = tap_index(by, bx, offp[pix], offp[HoWo + pix], p.H, p.W);
       miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
     }
     unsigned long long mask = __ballot(miss);
     while (mask) {
       const int l = __ffsll((long long)mask) - 1;
       mask &= mask - 1;
-      const int qi = (int)(base + l);
-      const int r = qi / HoWo, pix = qi - r * HoWo;
-      const int r2 = r / p.K2, t = r - r2 * p.K2;
-      const int n = r2 / p.G, g = r2 - n * p.G;
+      const int pix = wpix0 + l;
       const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
-      const int ti = t / p.KW, tj = t - ti * p.KW;
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
       const size_t oidx = ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
       float* dd = p.doffp + oidx;  // chunk-0 partial; the other chunks' stay 0 for a miss
@@ -1292,8 +1289,10 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     if (b.num_wg) DEFT_LAUNCH("sample_backward", kern, dim3(b.num_wg), dim3(256), p.lb_total, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t pairs = (size_t)d.n * d.offset_groups * p.taps * p.ho * p.wo;
-    DEFT_LAUNCH("sample_backward_miss", k_sample_bwd_miss<T>, dim3(grid_cap(pairs, 2048)), dim3(256), 0, st, b);
+    // one workgroup per 256 pixels of each (image, group, tap) plane
+    const size_t mgrid = (size_t)d.n * d.offset_groups * p.taps * (size_t)((p.ho * p.wo + 255) / 256);
+    if (mgrid > 0x7fffffffu) return hipErrorInvalidValue;
+    if (mgrid) DEFT_LAUNCH("sample_backward_miss", k_sample_bwd_miss<T>, dim3((unsigned)mgrid), dim3(256), 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = p.cg / p.chunk_b;
