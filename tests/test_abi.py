@@ -82,6 +82,11 @@ def test_planner_sizes_halo_from_histogram():
     # 1e-5 of the taps may stay outside
     assert L.deft_plan_get_info(L.deft_plan_create(d, [10 ** 6, 5, 0, 0, 0, 0, 0, 0]))["bwd_halo"] == 0
     assert L.deft_plan_get_info(L.deft_plan_create(d, [10 ** 6, 20, 0, 0, 0, 0, 0, 0]))["bwd_halo"] == 1
+    # degenerate histograms: every tap fully outside, or every tap in the open-ended bin (no halo helps)
+    assert L.deft_plan_get_info(L.deft_plan_create(d, [0, 0, 0, 0, 0, 0, 0, 50]))["bwd_halo"] == 0
+    assert L.deft_plan_get_info(L.deft_plan_create(d, [0, 0, 0, 0, 0, 0, 50, 0]))["bwd_halo"] == 0
+    # a tail reaching the open-ended bin: the last bin a halo can take in
+    assert L.deft_plan_get_info(L.deft_plan_create(d, [10, 10, 10, 10, 10, 10, 10, 0]))["bwd_halo"] == 5
 
 
 def test_forward_halo_avoids_single_workgroup_occupancy():
