@@ -56,8 +56,13 @@ enum deft_status {
   DEFT_ERR_ALIGN = -7,        /* a device pointer is not 16-byte aligned */
   DEFT_ERR_HIP = -8,          /* a HIP runtime call or launch failed */
   DEFT_ERR_PLAN = -9,         /* forced tile/halo/chunk outside the supported range */
-  DEFT_ERR_UNSUPPORTED = -10  /* channels per offset group not a multiple of 16, or size limits */
+  DEFT_ERR_UNSUPPORTED = -10, /* channels per offset group not a multiple of 16, or size limits */
+  DEFT_ERR_SCRATCH = -11      /* deft_forward_noalloc: the plan's forward scratch exceeds
+                                 DEFT_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the static device scratch of deft_forward_noalloc (per GPU). */
+#define DEFT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Layer descriptor.  Main-convolution groups are 1; offset_groups = G. */
 typedef struct deft_desc {
@@ -149,6 +154,26 @@ size_t deft_workspace_bytes(const deft_plan* p, int training);
 int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
                  const void* w, const void* b, void* y, float* offsets_out, void* workspace,
                  size_t ws_bytes, void* stream);
+
+/* deft_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, checks, kernels and results as deft_forward, but with no
+ * workspace argument.  The scratch that deft_forward takes from the workspace
+ * lives in a static device array of the library, DEFT_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, which every GPU the library runs on holds until the
+ * process ends.  The call allocates nothing: on the first call with a device
+ * current it looks up that device's copy of the array (hipGetSymbolAddress)
+ * and keeps the address.  `stream` must belong to the current device.
+ * DEFT_ERR_SCRATCH, before anything is launched, when
+ * deft_workspace_bytes(p, 0) exceeds DEFT_NOALLOC_SCRATCH_BYTES (at C = 256,
+ * 56 x 56, bf16 that is about 16.4 MB per image: up to 3 images).  Every
+ * call on one GPU shares that GPU's array and leaves its contents there
+ * (the next call overwrites what it reads before reading it): calls that
+ * overlap on one GPU, on different streams or threads, race and must be
+ * serialised by the caller.  The columns it leaves in the array are not
+ * available to deft_backward (inference only). */
+int deft_forward_noalloc(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
+                         const void* w, const void* b, void* y, float* offsets_out, void* stream);
 
 /* deft_forward that also observes the offset distribution: the fused
  * sampling launch adds the required-halo histogram of every tap it samples to

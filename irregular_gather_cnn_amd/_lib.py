@@ -17,9 +17,11 @@ LIB_PATH = os.path.join(_PKG, "libdeft.so")
 DEFT_F32, DEFT_BF16 = 0, 1
 STATUS = {0: "DEFT_OK", -1: "DEFT_ERR_BAD_DESC", -2: "DEFT_ERR_GROUPS", -3: "DEFT_ERR_SHAPE",
           -4: "DEFT_ERR_NULLPTR", -5: "DEFT_ERR_WORKSPACE", -6: "DEFT_ERR_DTYPE", -7: "DEFT_ERR_ALIGN",
-          -8: "DEFT_ERR_HIP", -9: "DEFT_ERR_PLAN", -10: "DEFT_ERR_UNSUPPORTED"}
+          -8: "DEFT_ERR_HIP", -9: "DEFT_ERR_PLAN", -10: "DEFT_ERR_UNSUPPORTED",
+          -11: "DEFT_ERR_SCRATCH"}
 EXPORTED = ["deft_desc_validate", "deft_plan_create", "deft_plan_create_forced", "deft_plan_get_info",
             "deft_plan_destroy", "deft_workspace_bytes", "deft_forward", "deft_forward_hist", "deft_forward_unfused",
+            "deft_forward_noalloc",
             "deft_backward",
             "deft_debug_sample_index", "deft_debug_sample", "deft_halo_histogram", "deft_error_string",
             "deft_last_hip_error", "deft_timing_start", "deft_timing_stop", "deft_timing_count",
@@ -76,6 +78,7 @@ def load() -> ctypes.CDLL:
         "deft_workspace_bytes": (sz, [vp, i]),
         "deft_forward": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "deft_forward_unfused": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "deft_forward_noalloc": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "deft_forward_hist": (i, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp]),
         "deft_dwconv1d_forward": (i, [vp, vp, vp, i, i, i, i, i, vp]),
         "deft_dwpw1d_forward": (i, [vp, vp, vp, vp, i, i, i, i, i, i, vp]),
@@ -162,6 +165,15 @@ def deft_workspace_bytes(plan, training: int) -> int:
 def deft_forward(plan, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, stream=None) -> None:
     _check(load().deft_forward(plan, _ptr(x), _ptr(w_off), _ptr(b_off), _ptr(w), _ptr(b), _ptr(y),
                                _ptr(offsets_out), _ptr(workspace), int(ws_bytes), _ptr(stream)), "deft_forward")
+
+
+def deft_forward_noalloc(plan, x, w_off, b_off, w, b, y, offsets_out, stream=None) -> None:
+    _check(load().deft_forward_noalloc(plan, _ptr(x), _ptr(w_off), _ptr(b_off), _ptr(w), _ptr(b), _ptr(y),
+                                       _ptr(offsets_out), _ptr(stream)), "deft_forward_noalloc")
+
+
+# Bytes of the static scratch behind deft_forward_noalloc (DEFT_NOALLOC_SCRATCH_BYTES in deft.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def deft_forward_hist(plan, x, w_off, b_off, w, b, y, offsets_out, workspace, ws_bytes, hist, hist_len,

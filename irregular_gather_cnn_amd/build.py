@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdeft.so")
 SOURCES = ["deft_sample.hip", "deft_gemm.hip", "deft_gemm_dl.hip", "deft_igemm.hip", "deft_dwconv.hip",
-           "deft_dwpw.hip", "deft_backward.hip", "deft_host.cpp"]
+           "deft_dwpw.hip", "deft_backward.hip", "deft_noalloc.hip", "deft_host.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -390,6 +390,8 @@ thread_local Timing g_timing;
 }  // namespace
 
 namespace deft {
+int report_hip_error(hipError_t e) { return hip_fail(e); }
+
 void timing_before(hipStream_t s, const char* name) {
   Timing& t = g_timing;
   if (!t.active || 2 * (size_t)t.used + 1 >= t.ev.size()) return;
@@ -711,6 +713,9 @@ const char* deft_error_string(int code) {
     case DEFT_ERR_HIP: return "HIP runtime error (see deft_last_hip_error)";
     case DEFT_ERR_PLAN: return "forced tile/halo/chunk outside the supported range";
     case DEFT_ERR_UNSUPPORTED: return "unsupported shape (channels per offset group must be a multiple of 16)";
+    case DEFT_ERR_SCRATCH:
+      return "the forward needs more scratch than the no-allocation entry point's static buffer holds "
+             "(DEFT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }

@@ -45,6 +45,9 @@ struct deft_plan {
 
 namespace deft {
 
+// Records a HIP error for deft_last_hip_error and returns DEFT_ERR_HIP.
+int report_hip_error(hipError_t e);
+
 // Timing hook (deft_timing_start): brackets a launch with events when active.
 void timing_before(hipStream_t s, const char* name);
 void timing_after(hipStream_t s);
