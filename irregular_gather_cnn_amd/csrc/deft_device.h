@@ -65,6 +65,7 @@ __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const uint4 a, const u
 // [kb, ke), z = batch / split index.
 struct TileCoord {
   int m0, n0, kb, ke, z;
+  int me = 0x7fffffff;  // end of the rows this tile owns (row-balanced tilings)
 };
 
 // Row (within the 32x32 block) of accumulator register r of lane `lane`;
@@ -290,6 +291,18 @@ __device__ __forceinline__ void load_lds16(const rsrc_t r, unsigned char* dst, i
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_t*)dst);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
+}
+
+// The same with a wave-uniform byte offset added (the buffer range check
+// applies to voff + soff) and the destination given as an LDS byte address.
+__device__ __forceinline__ void load_lds16_so(const rsrc_t r, uint32_t lds_addr, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_addr), "v"(voff), "s"(r),
+               "s"(soff)
+               : "memory");
+}
+// LDS byte address of a pointer into dynamic shared memory.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_t*)p);
 }
 
 template <int N>

@@ -4,26 +4,29 @@
 // The three contractions of the layer (DefT explainer page, "The argument in
 // one glance": the main convolution stays a GEMM; its backward adds dCol and
 // dW) stream the 2-byte column matrix through HBM, so at the layer's shapes
-// they are bound by memory bandwidth as much as by the matrix cores.  This
-// kernel keeps both sides busy:
+// they are bound by memory bandwidth as much as by the matrix cores.  Common
+// to the kernels here:
 //   * operands go from HBM/L2 straight into LDS with buffer loads that write
-//     LDS (no register round trip), four 32-deep k stages in flight;
+//     LDS (no register round trip);
 //   * a buffer resource bounds every load, so rows, columns and k beyond the
 //     operand read as zero (out-of-range offsets are set to 0x80000000);
-//   * an operand stored k-contiguous ("row" form) is staged as 64-byte rows
-//     and read with ds_read_b128; an operand stored contiguous along m or n
-//     ("k-major" form, e.g. dY [Cout][pixels] or the columns seen from dW) is
-//     staged as it lies and turned into MFMA fragments by ds_read_b64_tr_b16,
-//     so no transpose pass over HBM is needed;
+//   * an operand stored k-contiguous ("row" form) is staged as rows of the
+//     stage depth and read with ds_read_b128; an operand stored contiguous
+//     along m or n ("k-major" form, e.g. dY [Cout][pixels] or the columns seen
+//     from dW) is staged as it lies and turned into MFMA fragments by
+//     ds_read_b64_tr_b16, so no transpose pass over HBM is needed;
 //   * 16-byte chunks are XOR-swizzled so fragment reads are free of bank
 //     conflicts;
 //   * results whose output is contiguous along m leave through LDS: each wave
-//     transposes its 128x128 block there and writes whole 16-byte chunks.
-// 256 threads = 2x2 waves; the tile shape, ring depth and occupancy are set
-// per operation (GemmCfg): 256x256 tiles, 128x128 per wave (16 32x32x16 MFMA
-// blocks), one workgroup per CU for dW; 256x128 tiles, two per CU, for dCol;
-// 128x256 tiles, two per CU, with a shallower ring for the L2-resident weights,
-// for the forward.
+//     transposes its block there and writes whole 16-byte chunks.
+// Kernels:
+//   * k_gemm_dl: 2 x 2 waves, per-operation tile and ring (dCol; the forward
+//     on shapes with few rows per CU);
+//   * k_gemm_ws: 8 waves, waves 0-3 staging only A and 4-7 only B (dW);
+//   * k_gemm_vd: 4 waves, one workgroup per CU with an equal share of the
+//     output rows, 64-deep stages (the forward at the layer's main shapes).
+#include <algorithm>
+
 #include "deft_device.h"
 #include "deft_internal.h"
 
@@ -57,28 +60,37 @@ __device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Row-form swizzle (64-byte rows, 4 chunks): 16 consecutive rows reading the
-// same logical chunk hit 16 distinct 16-byte bank slots.
-__device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
+// Row-form swizzle, rows of 2*BK bytes (BK/8 16-byte chunks): the rows a
+// 16-lane phase of a fragment read touches (16 consecutive rows, one logical
+// chunk each) hit 16 distinct 16-byte slots of a 256-byte bank window.
+// 64-byte rows (BK 32) put 4 rows in a window, 128-byte rows (BK 64) two.
+template <int BK>
+__device__ __forceinline__ int swz_row(int r) {
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  if constexpr (BK == 32) return (r >> 2) & 3;
+  else return (r >> 1) & 7;
+}
 // k-major swizzle (rows of 2*ROWS bytes): the four k rows a 16-lane group of
 // a transposed read touches land in four distinct 64-byte bank windows.
 __device__ __forceinline__ int swz_kmaj(int k) { return 4 * (k & 3); }
 
 // Issues the loads of one operand's stage: rows [0, ROWS) (row form) or k
-// rows [0, kBK) (k-major form, ROWS columns) of the tile, `op_off` giving the
-// byte offset of each 16-byte chunk or kOOB.
-template <bool KMAJ, int ROWS, class F>
+// rows [0, BK) (k-major form, ROWS columns) of the tile, `op_off` giving the
+// byte offset of each 16-byte chunk or kOOB.  The four staging waves of the
+// operand share the stage (`wave` 0..3).
+template <bool KMAJ, int ROWS, int BK, class F>
 __device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* base, int wave, int lane,
                                               int k0, const F& op_off) {
-  constexpr int kPer = ROWS * kBK * 2 / 1024 / 4;
+  constexpr int kPer = ROWS * BK * 2 / 1024 / 4;
+  constexpr int kCh = BK / 8;  // 16-byte chunks per row
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = wave * kPer + i;
     unsigned char* dst = base + b * 1024;
     int off;
     if constexpr (!KMAJ) {
-      const int row = 16 * b + (lane >> 2);
-      const int c = (lane & 3) ^ swz_row(row);
+      const int row = (64 / kCh) * b + lane / kCh;
+      const int c = (lane % kCh) ^ swz_row<BK>(row);
       off = op_off(row, k0 + 8 * c);
     } else {
       const int pos = b * 1024 + lane * 16;
@@ -89,15 +101,20 @@ __device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* bas
     load_lds16(r, dst, off);
   }
 }
+template <bool KMAJ, int ROWS, class F>
+__device__ __forceinline__ void issue_operand(const rsrc_t r, unsigned char* base, int wave, int lane,
+                                              int k0, const F& op_off) {
+  issue_operand<KMAJ, ROWS, kBK>(r, base, wave, lane, k0, op_off);
+}
 
-// MFMA fragment (8 consecutive k of row/column `rc` of the tile) for k-chunk
-// pair `ks` (16 k) of a stage.
-template <bool KMAJ, int ROWS>
+// MFMA fragment (8 consecutive k of row/column `rc` of the tile) for 16-k
+// step `ks` of a stage.
+template <bool KMAJ, int ROWS, int BK>
 __device__ __forceinline__ uint4 fragment(const unsigned char* base, int rc0, int ks, int lane) {
   if constexpr (!KMAJ) {
     const int row = rc0 + (lane & 31);
     const int c = 2 * ks + (lane >> 5);
-    return *(const uint4*)(base + row * (kBK * 2) + ((c ^ swz_row(row)) << 4));
+    return *(const uint4*)(base + row * (BK * 2) + ((c ^ swz_row<BK>(row)) << 4));
   } else {
     const int g = lane >> 4, j = lane & 15;
     const int n = rc0 + 16 * (g & 1) + 4 * (j & 3);
@@ -110,6 +127,10 @@ __device__ __forceinline__ uint4 fragment(const unsigned char* base, int rc0, in
     }
     return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
   }
+}
+template <bool KMAJ, int ROWS>
+__device__ __forceinline__ uint4 fragment(const unsigned char* base, int rc0, int ks, int lane) {
+  return fragment<KMAJ, ROWS, kBK>(base, rc0, ks, lane);
 }
 
 template <class Op>
@@ -310,6 +331,368 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Op::Cfg::OC
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave GEMM with operand-specialised staging.  Waves 0-3 stage only A
+// and waves 4-7 only B, each operand into its own LDS ring; all eight waves
+// compute, 2 x 4 of them, each a WM x WN block.  A wave's vector-memory
+// counter retires its loads in issue order, so a wave that had issued both a
+// far-ahead load of the HBM-streamed operand and a near load of the
+// L2-resident one could not wait for the near one without also waiting for
+// the far one: the streamed operand's ring depth would buy no lookahead.
+// With one operand per wave, each ring's depth is that operand's lookahead.
+// One workgroup per CU (two waves per SIMD).
+template <int BM_, int BN_, int SA_, int SB_, int BK_ = 64>
+struct WsCfg {
+  static constexpr int BM = BM_, BN = BN_, SA = SA_, SB = SB_, BK = BK_;
+  static constexpr int KS = BK / 16;  // 16-k MFMA steps per stage
+  static constexpr int WM = BM / 2, WN = BN / 4, MI = WM / 32, NI = WN / 32;
+  static constexpr int kABytes = BM * BK * 2, kBBytes = BN * BK * 2;
+  static constexpr int kPerA = kABytes / 1024 / 4;  // 1 KB loads per staging wave per stage
+  static constexpr int kPerB = kBBytes / 1024 / 4;
+  static_assert(kPerA * 4096 == kABytes && kPerB * 4096 == kBBytes, "stage = whole 1 KB loads per wave");
+  static constexpr int kLdsMain = SA * kABytes + SB * kBBytes;
+  static constexpr int kEpiStride = WM * 2 + 16;  // bytes per transposed row of a wave's block
+  static constexpr int kLdsEpi = 8 * WN * kEpiStride;
+  static constexpr int kLds = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
+};
+
+template <class Op>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_ws(const Op op) {
+  using C = typename Op::Cfg;
+  constexpr int MI = C::MI, NI = C::NI, BK = C::BK, KS = C::KS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TileCoord tc = op.tile(blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS destinations go to M0
+  const int wm = wave >> 2, wn = wave & 3;
+  const bool stages_a = wave < 4;
+  const int lw = wave & 3;
+  const rsrc_t ra = op.rsrc_a(), rb = op.rsrc_b();
+  unsigned char* ringA = smem;
+  unsigned char* ringB = smem + C::SA * C::kABytes;
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // this wave's operand: ring depth and loads per stage
+  const int depth = stages_a ? C::SA : C::SB;
+  const int per = stages_a ? C::kPerA : C::kPerB;
+  auto issue = [&](int st) {
+    const int k0 = tc.kb + st * BK;
+    if (stages_a)
+      issue_operand<Op::A_KMAJ, C::BM, BK>(ra, ringA + (st % C::SA) * C::kABytes, lw, lane, k0,
+                                           [&](int x, int y) { return op.a_off(tc, x, y); });
+    else
+      issue_operand<Op::B_KMAJ, C::BN, BK>(rb, ringB + (st % C::SB) * C::kBBytes, lw, lane, k0,
+                                           [&](int x, int y) { return op.b_off(tc, x, y); });
+  };
+  // row blocks of this wave that hold rows of the tile (row-balanced tiles
+  // leave the last ones empty: they are neither read nor multiplied)
+  const int tile_rows = min(tc.me - tc.m0, C::BM);  // me may be INT_MAX (no row limit)
+  const int miv = __builtin_amdgcn_readfirstlane(max(0, min(MI, (tile_rows - wm * C::WM + 31) / 32)));
+  auto read_step = [&](int st, int ks, uint4* fa, uint4* fb) {
+    const unsigned char* a = ringA + (st % C::SA) * C::kABytes;
+    const unsigned char* b = ringB + (st % C::SB) * C::kBBytes;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      if (i < miv) fa[i] = fragment<Op::A_KMAJ, C::BM, BK>(a, wm * C::WM + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) fb[j] = fragment<Op::B_KMAJ, C::BN, BK>(b, wn * C::WN + j * 32, ks, lane);
+  };
+  auto mfma_step = [&](const uint4* fa, const uint4* fb) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      if (i < miv) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                              __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j], 0, 0, 0);
+      }
+  };
+  // interleave the next step's LDS reads with the MFMAs of the current one
+  constexpr int kReads = MI * (Op::A_KMAJ ? 2 : 1) + NI * (Op::B_KMAJ ? 2 : 1);
+  auto interleave = [&]() {
+#pragma unroll
+    for (int u = 0; u < kReads; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI) / kReads > 0 ? (MI * NI) / kReads : 1, 0);
+    }
+  };
+
+  const int nk = (tc.ke - tc.kb + BK - 1) / BK;
+  uint4 fa[2][MI], fb[2][NI];
+  for (int st = 0; st < depth && st < nk; ++st) issue(st);
+  if (nk > 0) {
+    wait_vm_atmost(per * (min(depth, nk) - 1));  // this wave's part of stage 0 has landed
+    __syncthreads();
+    read_step(0, 0, fa[0], fb[0]);
+  }
+  // Each stage holds KS 16-k steps; the fragments of the next step are read
+  // while the MFMAs of the current one run.  Before the last step of stage
+  // it, the barrier that publishes stage it+1 (and frees stage it's ring
+  // slots for the loads of stage it+depth) is passed while the MFMAs already
+  // issued drain.
+  for (int it = 0; it < nk; ++it) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+        read_step(it, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        mfma_step(fa[cur], fb[cur]);
+        interleave();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave is done reading stage it
+        if (it + 1 < nk) {
+          // this wave's stages issued after it+1: up to it+depth-1
+          wait_vm_atmost(per * max(0, min(depth - 2, nk - 2 - it)));
+          __syncthreads();
+          if (it + depth < nk) issue(it + depth);  // into the slot of stage it
+          read_step(it + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        }
+        mfma_step(fa[cur], fb[cur]);
+        interleave();
+      }
+    }
+  }
+
+  const int mw = tc.m0 + wm * C::WM, nw = tc.n0 + wn * C::WN;
+  if constexpr (Op::LDS_EPILOGUE) {
+    __syncthreads();  // the rings are free
+    constexpr int kEpiStride = C::kEpiStride;
+    unsigned char* reg = smem + wave * C::WN * kEpiStride;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int nl = j * 32 + (lane & 31);
+        const float add = op.column_add(nw + nl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ml = i * 32 + 8 * q + 4 * (lane >> 5);
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * q] + add, acc[i][j][4 * q + 1] + add);
+          v.y = pack_bf16x2(acc[i][j][4 * q + 2] + add, acc[i][j][4 * q + 3] + add);
+          *(uint2*)(reg + nl * kEpiStride + ml * 2) = v;
+        }
+      }
+    __syncthreads();
+    constexpr int kCh = C::WM / 8, kRows = 64 / kCh;
+#pragma unroll 4
+    for (int it = 0; it < C::WN / kRows; ++it) {
+      const int nl = it * kRows + lane / kCh, c = lane % kCh;
+      const uint4 v = *(const uint4*)(reg + nl * kEpiStride + c * 16);
+      op.store_chunk(tc, nw + nl, mw + c * 8, v);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) op.store_acc(tc, mw + i * 32, nw + j * 32, acc[i][j], lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave GEMM with buffer-to-LDS staging (one workgroup per CU, one wave
+// per SIMD), 64-deep k stages.  A (streamed from HBM) has a 3-slot ring and
+// is loaded two stages ahead, B (L2-resident) a 2-slot ring loaded one stage
+// ahead; every wave stages its quarter of both.  After the barrier that
+// frees the slots of stage it-1, a wave issues B(it+1) and then A(it+2), so
+// before the next barrier it waits only for loads issued before B(it+1):
+// the far A load never holds up the near B one (a wave's memory counter
+// retires its loads in issue order).  Each wave owns all BM rows and a
+// quarter of the BN columns (MI x NI 32x32 blocks, accumulators in AGPRs).
+template <int BM_, int BN_>
+struct VdCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, KS = 4, SA = 3, SB = 2;
+  static constexpr int WM = BM, WN = BN / 4, MI = WM / 32, NI = WN / 32;
+  static constexpr int kABytes = BM * BK * 2, kBBytes = BN * BK * 2;
+  static constexpr int kPerA = kABytes / 1024 / 4, kPerB = kBBytes / 1024 / 4;  // 1 KB loads per wave
+  static_assert(kPerA * 4096 == kABytes && kPerB * 4096 == kBBytes, "stage = whole 1 KB loads per wave");
+  static_assert(BM % 32 == 0 && BN % 128 == 0, "tile");
+  static constexpr int kLdsMain = SA * kABytes + SB * kBBytes;
+  static constexpr int kEpiStride = WM * 2 + 16;
+  static constexpr int kLdsEpi = 4 * WN * kEpiStride;
+  static constexpr int kLds = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
+};
+
+template <class Op>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_vd(const Op op) {
+  using C = typename Op::Cfg;
+  constexpr int MI = C::MI, NI = C::NI, BK = C::BK, KS = C::KS, SA = C::SA, SB = C::SB;
+  static_assert(!Op::A_KMAJ && !Op::B_KMAJ, "row-form operands");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TileCoord tc = op.tile(blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const rsrc_t ra = op.rsrc_a(), rb = op.rsrc_b();
+  unsigned char* ringA = smem;
+  unsigned char* ringB = smem + SA * C::kABytes;
+  const int tile_rows = min(tc.me - tc.m0, C::BM);  // me may be INT_MAX (no row limit)
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (tc.ke - tc.kb + BK - 1) / BK;
+  // Load b of a wave's share of a stage fills LDS bytes [1024 b, 1024 b +
+  // 1024) of the slot: rows 8b..8b+7, lane -> row 8b + lane/8, slot chunk
+  // lane%8 holding logical chunk (lane%8) ^ swz(row).  Its operand byte
+  // offset is fixed up to the stage's k0, passed as the scalar offset (K is a
+  // multiple of 64 here).  Every wave issues the same loads in every
+  // iteration (stages past the last read zero through the range check), so
+  // the waits are constant.
+  constexpr int kCh = BK / 8;
+  int va[C::kPerA], vb[C::kPerB];
+#pragma unroll
+  for (int i = 0; i < C::kPerA; ++i) {
+    const int row = (64 / kCh) * (wn * C::kPerA + i) + lane / kCh;
+    const int o = op.a_row(tc, row);
+    va[i] = o == kOOB ? kOOB : o + 16 * ((lane % kCh) ^ swz_row<BK>(row));
+  }
+#pragma unroll
+  for (int i = 0; i < C::kPerB; ++i) {
+    const int row = (64 / kCh) * (wn * C::kPerB + i) + lane / kCh;
+    const int o = op.b_row(tc, row);
+    vb[i] = o == kOOB ? kOOB : o + 16 * ((lane % kCh) ^ swz_row<BK>(row));
+  }
+  auto soff_of = [&](int st) { return st < nk ? (tc.kb + st * BK) * 2 : 0x7fff0000; };
+  const uint32_t ldsA = lds_addr_of(ringA) + wn * C::kPerA * 1024;
+  const uint32_t ldsB = lds_addr_of(ringB) + wn * C::kPerB * 1024;
+  auto issueA = [&](int st) {
+    const uint32_t base = ldsA + (st % SA) * C::kABytes;
+    const int so = soff_of(st);
+#pragma unroll
+    for (int i = 0; i < C::kPerA; ++i) load_lds16_so(ra, base + i * 1024, va[i], so);
+  };
+  auto issueB = [&](int st) {
+    const uint32_t base = ldsB + (st % SB) * C::kBBytes;
+    const int so = soff_of(st);
+#pragma unroll
+    for (int i = 0; i < C::kPerB; ++i) load_lds16_so(rb, base + i * 1024, vb[i], so);
+  };
+  uint4 fa[2][MI], fb[2][NI];
+  // B fragments first: every MFMA of a step uses one, while the A fragment
+  // of row block i is needed only from its (i*NI)-th MFMA on
+  auto read_step = [&](int st, int ks, uint4* fa_, uint4* fb_) {
+    const unsigned char* a = ringA + (st % SA) * C::kABytes;
+    const unsigned char* b = ringB + (st % SB) * C::kBBytes;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) fb_[j] = fragment<false, C::BN, BK>(b, wn * C::WN + j * 32, ks, lane);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) fa_[i] = fragment<false, C::BM, BK>(a, i * 32, ks, lane);
+  };
+  auto mfma_step = [&](const uint4* fa_, const uint4* fb_) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa_[i]),
+                                                            __builtin_bit_cast(bf16x8_t, fb_[j]), acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int u = 0; u < MI * NI; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  if (nk <= 0) return;  // (uniform) no k range
+  // prologue: B(0), A(0), then what the barrier before iteration 0 would
+  // have issued in the steady state (A(1), B(1), A(2)); stage 0 lands first
+  issueB(0);
+  issueA(0);
+  issueA(1);
+  issueB(1);
+  issueA(2);
+  wait_vm<2 * C::kPerA + C::kPerB>();
+  __syncthreads();
+  read_step(0, 0, fa[0], fb[0]);
+  for (int it = 0; it < nk; ++it) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+        read_step(it, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        mfma_step(fa[cur], fb[cur]);
+        interleave();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave is done reading stage it
+        // stage it+1 has landed once only A(it+2), issued after B(it+1), is
+        // outstanding
+        wait_vm<C::kPerA>();
+        __syncthreads();
+        // slots of stage it are free: B(it+2) first, then A(it+3)
+        issueB(it + 2);
+        issueA(it + 3);
+        read_step(it + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        mfma_step(fa[cur], fb[cur]);
+        interleave();
+      }
+    }
+  }
+  wait_vm<0>();  // the out-of-range tail loads
+
+  const int mw = tc.m0, nw = tc.n0 + wn * C::WN;
+  if constexpr (Op::LDS_EPILOGUE) {
+    __syncthreads();  // the rings are free
+    constexpr int kEpiStride = C::kEpiStride;
+    unsigned char* reg = smem + wn * C::WN * kEpiStride;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int nl = j * 32 + (lane & 31);
+        const float add = op.column_add(nw + nl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ml = i * 32 + 8 * q + 4 * (lane >> 5);
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * q] + add, acc[i][j][4 * q + 1] + add);
+          v.y = pack_bf16x2(acc[i][j][4 * q + 2] + add, acc[i][j][4 * q + 3] + add);
+          *(uint2*)(reg + nl * kEpiStride + ml * 2) = v;
+        }
+      }
+    __syncthreads();
+    constexpr int kCh = C::WM / 8, kRows = 64 / kCh;
+    static_assert(C::WN % kRows == 0, "epilogue passes");
+#pragma unroll 4
+    for (int it = 0; it < C::WN / kRows; ++it) {
+      const int nl = it * kRows + lane / kCh, c = lane % kCh;
+      if (lane < kRows * kCh && c * 8 < tile_rows) {  // kCh need not divide 64
+        const uint4 v = *(const uint4*)(reg + nl * kEpiStride + c * 16);
+        op.store_chunk(tc, nw + nl, mw + c * 8, v);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) op.store_acc(tc, mw + i * 32, nw + j * 32, acc[i][j], lane);
+  }
+}
+
+template <class Op>
+hipError_t run_vd(const char* name, const Op& op, int grid, hipStream_t st) {
+  auto kern = k_gemm_vd<Op>;
+  constexpr int lds = Op::Cfg::kLds;
+  static_assert(lds <= 160 * 1024, "LDS");
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  if (grid == 0) return hipSuccess;
+  DEFT_LAUNCH(name, kern, dim3(grid), dim3(256), lds, st, op);
+  return hipGetLastError();
+}
+
 __host__ __device__ inline uint32_t rsrc_bytes(size_t bytes) {
   return bytes > 0x7ffffff0u ? 0x7ffffff0u : (uint32_t)bytes;
 }
@@ -360,6 +743,63 @@ struct DlFwdT {
 using DlFwd = DlFwdT<GemmCfg<128, 256, 3, 2, 2>>;
 using DlFwdMid = DlFwdT<GemmCfg<128, 128, 4, 2>>;
 using DlFwdSmall = DlFwdT<GemmCfg<64, 128, 4, 2>>;
+
+// Forward with the rows balanced over one workgroup per CU: the M = N*Ho*Wo
+// output rows are split into whole 8-row units, each workgroup taking an
+// equal contiguous share (at most 256 rows; MFMA blocks past its share read
+// zero rows and are not stored), all output channels in 256-wide column
+// tiles.  Every CU then streams the same number of column rows, where
+// 128-row tiles left some CUs with two tiles and others with one.
+template <class CfgT>
+struct FwdBalT {
+  using Cfg = CfgT;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false, LDS_EPILOGUE = true;
+  const bf16_t* cols;  // [M][K]
+  const bf16_t* wt;    // [N][K]
+  const bf16_t* bias;  // nullable
+  bf16_t* y;
+  int M, N, K, HoWo, gm, gn, units;
+  FastDiv div_howo;
+  __device__ rsrc_t rsrc_a() const { return make_rsrc(cols, rsrc_bytes((size_t)M * K * 2)); }
+  __device__ rsrc_t rsrc_b() const { return make_rsrc(wt, rsrc_bytes((size_t)N * K * 2)); }
+  __device__ TileCoord tile(int bid) const {
+    // the column tiles of one row range sit on one XCD (they share its rows)
+    const int lb = xcd_swizzle(bid, gm * gn);
+    const int mr = lb / gn, nt = lb - mr * gn;
+    const int u0 = (int)((long long)mr * units / gm), u1 = (int)((long long)(mr + 1) * units / gm);
+    TileCoord t{8 * u0, nt * Cfg::BN, 0, K, 0};
+    t.me = 8 * u1;
+    return t;
+  }
+  __device__ int a_off(const TileCoord& tc, int row, int k) const {
+    const int m = tc.m0 + row;
+    return (m < tc.me && k < K) ? (m * K + k) * 2 : kOOB;
+  }
+  // byte offset of row `row` of the tile's A (B) rows, or kOOB
+  __device__ int a_row(const TileCoord& tc, int row) const {
+    const int m = tc.m0 + row;
+    return m < tc.me ? m * K * 2 : kOOB;
+  }
+  __device__ int b_row(const TileCoord& tc, int row) const {
+    const int n = tc.n0 + row;
+    return n < N ? n * K * 2 : kOOB;
+  }
+  __device__ int b_off(const TileCoord& tc, int row, int k) const {
+    const int n = tc.n0 + row;
+    return (n < N && k < K) ? (n * K + k) * 2 : kOOB;
+  }
+  __device__ float column_add(int n) const { return (bias && n < N) ? bf16_to_f32(bias[n]) : 0.f; }
+  // 8 consecutive pixels q = m..m+7 of output channel n (never split by an
+  // image boundary: HoWo % 8 == 0 on this path)
+  __device__ void store_chunk(const TileCoord& tc, int n, int m, const uint4 v) const {
+    if (n >= N || m >= tc.me) return;
+    const int img = fdiv(m, div_howo), p = m - img * HoWo;
+    store16_nt(y + ((size_t)img * N + n) * HoWo + p, v);
+  }
+  __device__ void store_acc(const TileCoord&, int, int, const f32x16_t&, int) const {}
+};
+
+using FwdVd = FwdBalT<VdCfg<224, 256>>;
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
@@ -418,8 +858,9 @@ struct DlDcol {
 };
 
 // ---- dW partial of split z: part[z][co][e] = sum_{q in split} dY[img(q)][co][p(q)] cols[q][e] ----
-struct DlDw {
-  using Cfg = Cfg256;
+template <class CfgT>
+struct DlDwT {
+  using Cfg = CfgT;
   static constexpr bool A_KMAJ = false, B_KMAJ = true, LDS_EPILOGUE = false;
   const bf16_t* dy;    // [img][M][HoWo]
   const bf16_t* cols;  // [P][N]
@@ -465,6 +906,24 @@ struct DlDw {
 };
 
 template <class Op>
+hipError_t run_ws(const char* name, const Op& op, int grid, hipStream_t st) {
+  auto kern = k_gemm_ws<Op>;
+  constexpr int lds = Op::Cfg::kLds;
+  static_assert(lds <= 160 * 1024, "LDS");
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  if (grid == 0) return hipSuccess;
+  DEFT_LAUNCH(name, kern, dim3(grid), dim3(512), lds, st, op);
+  return hipGetLastError();
+}
+
+// dW on the eight-wave kernel: dY (L2 / Infinity Cache, read by the 9 column
+// tiles of each split) is staged by waves 0-3, the columns (HBM) by waves
+// 4-7, four stages deep each.
+using DlDw = DlDwT<Cfg256>;
+using DwWs = DlDwT<WsCfg<256, 256, 4, 4, 32>>;
+
+template <class Op>
 hipError_t run_dl(const char* name, const Op& op, int grid, hipStream_t st) {
   auto kern = k_gemm_dl<Op>;
   constexpr int lds = Op::Cfg::kLds;
@@ -490,12 +949,13 @@ bool gemm_dl_supported(const deft_plan& p) {
 
 void gemm_dl_dw_split(const deft_plan& p, int* splits, int* kper) {
   const int P = p.d.n * p.ho * p.wo;
-  const int per = tiles(p.d.c_out, DlDw::Cfg::BM) * tiles(p.ck, DlDw::Cfg::BN);
-  int s = 256 / per;
+  const int per = tiles(p.d.c_out, DwWs::Cfg::BM) * tiles(p.ck, DwWs::Cfg::BN);
+  int s = p.cus / per;
   if (s < 1) s = 1;
   int k = (P + s - 1) / s;
-  k = (k + kBK - 1) / kBK * kBK;
-  if (k < kBK) k = kBK;
+  constexpr int bk = DwWs::Cfg::BK;
+  k = (k + bk - 1) / bk * bk;
+  if (k < bk) k = bk;
   *kper = k;
   *splits = (P + k - 1) / k;
 }
@@ -514,6 +974,22 @@ static hipError_t dl_forward_with(const deft_plan& p, const void* wt, const void
 hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols, const void* b, void* y,
                            hipStream_t st) {
   const int M = p.d.n * p.ho * p.wo, N = p.d.c_out;
+  // Row-balanced four-wave kernel: one workgroup per CU, each an equal share
+  // of whole 8-row units (at most 224 rows) and 256 output channels.  Used
+  // where the shares fill most of a 224-row tile (it computes all 7 row
+  // blocks) and k comes in whole 64-deep stages.
+  {
+    const int units = M / 8, gn = tiles(N, FwdVd::Cfg::BN);
+    const int gm = std::min(units, std::max((p.cus + gn - 1) / gn, tiles(units, FwdVd::Cfg::BM / 8)));
+    if (p.ck % FwdVd::Cfg::BK == 0 && gm > 0 && 8 * (units / gm) >= 160) {
+      FwdVd op;
+      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
+      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
+      op.div_howo = make_fastdiv(op.HoWo);
+      op.units = units; op.gn = gn; op.gm = gm;
+      return run_vd("gemm_forward", op, gm * gn, st);
+    }
+  }
   auto count = [&](int bm, int bn) { return tiles(M, bm) * tiles(N, bn); };
   if (count(DlFwd::Cfg::BM, DlFwd::Cfg::BN) >= 384) return dl_forward_with<DlFwd>(p, wt, cols, b, y, st);
   if (count(DlFwdMid::Cfg::BM, DlFwdMid::Cfg::BN) >= 384) return dl_forward_with<DlFwdMid>(p, wt, cols, b, y, st);
@@ -531,13 +1007,14 @@ hipError_t dl_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void
 }
 
 hipError_t dl_gemm_dw(const deft_plan& p, const void* dy, const void* cols, float* part, hipStream_t st) {
-  DlDw op;
+  DwWs op;
   op.dy = (const bf16_t*)dy; op.cols = (const bf16_t*)cols; op.part = part;
   op.M = p.d.c_out; op.N = p.ck; op.P = p.d.n * p.ho * p.wo; op.HoWo = p.ho * p.wo;
   op.div_howo = make_fastdiv(op.HoWo);
-  op.tilesM = tiles(op.M, DlDw::Cfg::BM); op.tilesN = tiles(op.N, DlDw::Cfg::BN);
-  gemm_dl_dw_split(p, &op.splits, &op.kper);
-  return run_dl("gemm_dw", op, op.tilesM * op.tilesN * op.splits, st);
+  op.tilesM = tiles(op.M, DwWs::Cfg::BM); op.tilesN = tiles(op.N, DwWs::Cfg::BN);
+  op.splits = p.dw_splits;  // the plan sized the partials' workspace for these
+  op.kper = p.dw_kper;
+  return run_ws("gemm_dw", op, op.tilesM * op.tilesN * op.splits, st);
 }
 
 }  // namespace deft

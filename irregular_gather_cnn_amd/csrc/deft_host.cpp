@@ -24,8 +24,41 @@ int hip_fail(hipError_t e) {
   return DEFT_ERR_HIP;
 }
 
-constexpr int kMaxLds = 160 * 1024;     // gfx950 LDS per workgroup
-constexpr int kNumCUs = 256;
+// Compute units and LDS bytes per workgroup of the current device, read once
+// per device; without a device (planning on a host with no GPU) those of
+// MI355X: 256 CUs, 160 KB.
+struct DeviceLimits {
+  int cus = 256, max_lds = 160 * 1024;
+};
+DeviceLimits device_limits() {
+  static DeviceLimits cache[64];
+  static bool known[64] = {false};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return DeviceLimits{};
+  }
+  if (!known[dev]) {
+    DeviceLimits l;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) l.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+      l.max_lds = v;
+    (void)hipGetLastError();
+    cache[dev] = l;
+    known[dev] = true;
+  }
+  return cache[dev];
+}
+
+// A plan for descriptor d on the current device (fields not yet laid out).
+deft_plan blank_plan(const deft_desc& d, const DeviceLimits& lim) {
+  deft_plan p;
+  p.d = d;
+  p.cus = lim.cus;
+  p.max_lds = lim.max_lds;
+  return p;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int align16(int v) { return (v + 15) & ~15; }
@@ -102,7 +135,7 @@ bool layout_backward(deft_plan& p) {
     ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
   }
   const int total = lx + ldx + ldc + 16 + 4 * 49 * 4 + 48 * 8;  // + list counter and per-tap tables
-  if (total > kMaxLds) return false;
+  if (total > p.max_lds) return false;
   p.btile_h = ch; p.btile_w = cw;
   p.btiles_h = (d.h + ch - 1) / ch; p.btiles_w = (d.w + cw - 1) / cw;
   p.num_btiles = d.n * p.btiles_h * p.btiles_w;
@@ -130,9 +163,12 @@ bool layout_backward(deft_plan& p) {
   int bands = 1;
   while (bands < s.ho) {
     const int rows = (s.ho + bands - 1) / bands;
-    if (woff_lds(rows) <= kMaxLds / 2 && (double)d.n * slices * bands >= 512) break;
+    if (woff_lds(rows) <= p.max_lds / 2 && (double)d.n * slices * bands >= 512) break;
     ++bands;
   }
+  // the offset-weight backward stages whole input rows: a band of the rows
+  // it settled on must fit the LDS, else this shape has no backward here
+  if (woff_lds((s.ho + bands - 1) / bands) > p.max_lds) return false;
   p.woff_bands = bands;
   return true;
 }
@@ -197,7 +233,7 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
     p.lds_info = p.lds_off + align16(ocw * pt * 4);
     p.lds_total = p.lds_info + align16(p.gw * s.taps * pt * 8) + p.gw * s.taps * pt * 16;  // tap table + weights
   }
-  if (p.lds_total > kMaxLds) return false;
+  if (p.lds_total > p.max_lds) return false;
   p.num_btiles = 0; p.list_cap = 0; p.woff_bands = 1;
   if (!layout_backward(p)) p.chunk_b = 0;
   // workspace
@@ -286,8 +322,9 @@ int backward_halo(const uint32_t* hist, int len) {
 // fraction of the machine the launch keeps busy.  A region so large that only one workgroup fits a CU
 // leaves four waves to hide the gather latency: measured 1.7 to 1.8 times
 // slower than two per CU, whatever the halo saves.
-int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len) {
+int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int hist_len, bool need_bwd = true) {
   const Shape s = shape_of(d);
+  const DeviceLimits lim = device_limits();
   static const int tiles[][2] = {{8, 8}, {4, 16}, {16, 4}, {8, 4}, {4, 8}, {4, 4}, {2, 16}, {16, 2}, {2, 8}, {1, 16}};
   double best_cost = 1e300;
   bool found = false;
@@ -297,16 +334,15 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
     for (int halo = 0; halo <= 16; ++halo) {
       for (int chunk = 64; chunk >= 16; chunk /= 2) {
         if (s.cg % chunk) continue;
-        deft_plan p;
-        p.d = d;
-        if (!layout_plan(p, t[0], t[1], halo, chunk) || p.chunk_b == 0) continue;
+        deft_plan p = blank_plan(d, lim);
+        if (!layout_plan(p, t[0], t[1], halo, chunk) || (need_bwd && p.chunk_b == 0)) continue;
         const double miss = miss_fraction(hist, hist_len, halo);
         const double pt = (double)t[0] * t[1];
         const double per_tile_stage = (double)p.reg_h * p.reg_w * s.cg + (double)p.foot_h * p.foot_w * d.c_in;
         const double stage_bytes = (double)p.num_wg * per_tile_stage * s.esz;
         const double miss_bytes = 0.4 * miss * samples * 4.0 * s.esz;
-        const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
-        const double slots = (double)kNumCUs * occ;
+        const int occ = std::max(1, std::min(4, p.max_lds / std::max(p.lds_total, 1)));
+        const double slots = (double)p.cus * occ;
         const double waves = std::ceil(p.num_wg / slots);
         const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
         // each channel-chunk pass of a workgroup pays a staging round trip and
@@ -323,7 +359,7 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
       }
     }
   }
-  if (!found) return DEFT_ERR_UNSUPPORTED;
+  if (!found) return need_bwd ? plan_auto(best, d, hist, hist_len, false) : DEFT_ERR_UNSUPPORTED;
   // Direct gather where supported: no LDS halo; the tile only sets the
   // forward's launch shape.  Every tile of 32..64 pixels is a candidate (fewer only when the
   // output is smaller).  Cost: the columns of every pixel slot the launch
@@ -344,11 +380,10 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
     for (int th = 1; th <= 16; ++th)
       for (int tw = 1; th * tw <= 64; ++tw) {
         if (th * tw < min_pt) continue;
-        deft_plan p;
-        p.d = d;
-        if (!layout_plan(p, th, tw, best.halo, s.cg, true) || p.chunk_b == 0) continue;
-        const int occ = std::max(1, std::min(4, kMaxLds / std::max(p.lds_total, 1)));
-        const double slots = (double)kNumCUs * occ;
+        deft_plan p = blank_plan(d, lim);
+        if (!layout_plan(p, th, tw, best.halo, s.cg, true) || (need_bwd && p.chunk_b == 0)) continue;
+        const int occ = std::max(1, std::min(4, p.max_lds / std::max(p.lds_total, 1)));
+        const double slots = (double)p.cus * occ;
         const double waves = std::ceil(p.num_wg / slots);
         const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
         const double padded = (double)p.num_wg * th * tw;
@@ -366,9 +401,9 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
   }
   // the backward's halo is set by the tap distances alone
   const int bh = backward_halo(hist, hist_len);
-  deft_plan q;
-  q.d = d;
-  if (layout_plan(q, best.tile_h, best.tile_w, best.halo, best.chunk, best.direct != 0, bh) && q.chunk_b != 0)
+  deft_plan q = blank_plan(d, lim);
+  if (layout_plan(q, best.tile_h, best.tile_w, best.halo, best.chunk, best.direct != 0, bh) &&
+      (q.chunk_b != 0 || !need_bwd))
     best = q;
   best.est_miss = miss_fraction(hist, hist_len, best.bhalo);
   return DEFT_OK;
@@ -436,7 +471,7 @@ int deft_plan_create_forced(const deft_desc* d, int tile_h, int tile_w, int halo
   if ((chunk == -1 || chunk == -2) && !direct_ok(*d)) return DEFT_ERR_PLAN;
   deft_plan* p = new (std::nothrow) deft_plan();
   if (!p) return DEFT_ERR_UNSUPPORTED;
-  p->d = *d;
+  *p = blank_plan(*d, device_limits());
   p->num_btiles = 0;
   bool ok = false;
   if (chunk == -1 || chunk == -2) {
@@ -603,8 +638,9 @@ int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, v
   if (p->direct) {
     // sampling from given offsets always uses the LDS tile + halo kernel
     // (it has no workspace for the channel-minor copy)
-    deft_plan q{};
-    q.d = p->d;
+    deft_plan q = blank_plan(p->d, DeviceLimits{});
+    q.cus = p->cus;
+    q.max_lds = p->max_lds;
     bool ok = false;
     for (int c = 64; c >= 16 && !ok; c /= 2)
       if (p->cg % c == 0) ok = layout_plan(q, p->tile_h, p->tile_w, p->halo, c);

@@ -9,6 +9,8 @@
 
 struct deft_plan {
   deft_desc d;
+  int cus = 256;               // compute units of the device the plan was made for
+  int max_lds = 160 * 1024;    // its LDS bytes per workgroup
   int ho, wo, oc, taps, ck, cg;
   // fused sampling kernel
   int tile_h, tile_w, halo, chunk, chunk_a, gw, gsplit;
