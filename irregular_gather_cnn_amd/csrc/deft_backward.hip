@@ -31,6 +31,7 @@
 //                     dW_off, db, db_off.
 // Global atomics are avoided on every hot path: on gfx950 they run far below
 // the bandwidth of plain stores.
+#include <algorithm>
 #include <type_traits>
 
 #include "deft_device.h"
@@ -1008,16 +1009,22 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
   const int crow = c0 + (lane & 31);
-  // the sampling part of dX for this lane's outputs, loaded up front so the
-  // loads overlap the dOffset tile and the MFMAs
-  float sv[2][16];
+  // The sampling part of dX for the outputs this lane writes at the end (8
+  // consecutive pixels of one channel per piece, 4 pieces), loaded up front
+  // so the loads overlap the dOffset tile and the MFMAs.  Whole pieces need
+  // HW % 8 == 0 (then a piece never straddles a channel plane).
+  const bool vec8 = (HW & 7) == 0;
+  float4 sv[4][2];
+  if (vec8) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = pix0 + j * 32 + (lane & 31);
-#pragma unroll
-    for (int r2 = 0; r2 < 16; ++r2) {
-      const int cc = c0 + acc_row(lane, r2);
-      sv[j][r2] = (active && q < HW && cc < p.Cin) ? p.dxs[((size_t)n * p.Cin + cc) * HW + q] : 0.f;
+    for (int k = 0; k < 4; ++k) {
+      const int cl = k * 8 + (lane >> 3), q = pix0 + (lane & 7) * 8, cc = c0 + cl;
+      sv[k][0] = sv[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && q < HW && cc < p.Cin) {
+        const float* src = p.dxs + ((size_t)n * p.Cin + cc) * HW + q;
+        sv[k][0] = *(const float4*)src;
+        sv[k][1] = *(const float4*)(src + 4);
+      }
     }
   }
   int4* kinfo = (int4*)(smem + ((64 * bstr * (int)sizeof(T) + 15) & ~15));  // [KKC]
@@ -1081,8 +1088,35 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
       }
     }
   }
-  if (!active) return;
   T* dx = (T*)p.dx;
+  if (vec8) {
+    // through LDS: each wave's 32 channels x 64 pixels (fp32, rows padded
+    // to 68 floats), then per lane 8 consecutive pixels of one channel: one
+    // 32-byte read, the sampling part added, one 16-byte (bf16) store
+    __syncthreads();  // the B tile is no longer read
+    float* ep = (float*)smem + wave * 32 * 68;
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) ep[acc_row(lane, r2) * 68 + j * 32 + (lane & 31)] = acc[j][r2];
+    }
+    // a wave reads back only its own block: its LDS operations execute in
+    // issue order, so only the compiler has to be kept from reordering
+    asm volatile("" ::: "memory");
+    if (!active) return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int cl = k * 8 + (lane >> 3), ql = (lane & 7) * 8, q = pix0 + ql, cc = c0 + cl;
+      if (q >= HW || cc >= p.Cin) continue;
+      const float4 a0 = *(const float4*)(ep + cl * 68 + ql), a1 = *(const float4*)(ep + cl * 68 + ql + 4);
+      float f[8] = {a0.x + sv[k][0].x, a0.y + sv[k][0].y, a0.z + sv[k][0].z, a0.w + sv[k][0].w,
+                    a1.x + sv[k][1].x, a1.y + sv[k][1].y, a1.z + sv[k][1].z, a1.w + sv[k][1].w};
+      store8(dx + ((size_t)n * p.Cin + cc) * HW + q, f);
+    }
+    return;
+  }
+  if (!active) return;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = pix0 + j * 32 + (lane & 31);
@@ -1092,7 +1126,7 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
       const int cc = c0 + acc_row(lane, r2);
       if (cc < p.Cin) {
         const size_t idx = ((size_t)n * p.Cin + cc) * HW + q;
-        dx[idx] = Elem<T>::from_f32(acc[j][r2] + sv[j][r2]);
+        dx[idx] = Elem<T>::from_f32(acc[j][r2] + p.dxs[idx]);
       }
     }
   }
@@ -1314,7 +1348,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
     w.WoP = (p.wo + kc - 1) / kc * kc;
     w.XR = (w.band_rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
-    // staged row: columns [-XL, XS - XL) of x; XL = 8 keeps x = 0 16-byte aligned
+    // staged row: columns [-XL, XS - XL) of x, XL = pad_w (the fp32 path's
+    // column of x = 0; the bf16 path indexes pixels from x = -PW directly)
     const int span = (w.WoP - 1) * d.stride_w + (d.kw - 1) * d.dil_w + 1;  // from x = -PW
     w.XL = d.pad_w;
     w.XS = span;  // pixels per staged row, from x = -PW
@@ -1356,7 +1391,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     q.num_wg = d.n * q.pix_blocks * q.cblocks;
     q.wofft = wofft; q.doff = doff; q.dxs = dxs; q.dx = a.dx;
     q.div_w = make_fastdiv(d.w); q.div_sh = make_fastdiv(d.stride_h); q.div_sw = make_fastdiv(d.stride_w);
-    const int lds = ((64 * (q.KKC + (d.dtype == DEFT_BF16 ? 8 : 4)) * (int)sizeof(T) + 15) & ~15) + q.KKC * 16;
+    const int lds = std::max(((64 * (q.KKC + (d.dtype == DEFT_BF16 ? 8 : 4)) * (int)sizeof(T) + 15) & ~15) + q.KKC * 16,
+                             8 * 32 * 68 * 4);  // B tile + tap table, or the epilogue's fp32 blocks
     auto kern = k_dx_final<T>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
