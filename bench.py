@@ -116,18 +116,68 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
 
-    # timed region: exactly K steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: exactly K steps, with an event between consecutive steps
+    # for the per-step spread (events are recorded on the launch stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    warm = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     log("timed: %d steps, %.3f ms/step (host wall %.3f s)" % (args.steps, ms_step, wall))
+
+    def spread(v):
+        q = np.percentile(np.asarray(v, np.float64), [10, 50, 90])
+        return {"p10": round(float(q[0]), 4), "median": round(float(q[1]), 4), "p90": round(float(q[2]), 4)}
+
+    # cold caches: before every step, outside its events, 512 MiB are written
+    # (twice the 256 MB Infinity Cache, far more than the L2s), so the step
+    # starts with none of its inputs cached and the caches full of dirty lines
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        step()
+        b_.record()
+        torch.cuda.synchronize()
+        cold.append(a_.elapsed_time(b_))
+    del flush
+    step_spread = {"warm": spread(warm), "cold": spread(cold)}
+    log("per-step ms: %s" % step_spread)
+
+    # measured HBM rates on this device: a 1 GiB device copy (read + write)
+    # and a 1 GiB fill (write only)
+    def hbm_rates():
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dstc = torch.empty_like(src)
+        dstc.copy_(src)
+        src.fill_(0)
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for _ in range(5):
+            dstc.copy_(src)
+        b_.record()
+        torch.cuda.synchronize()
+        copy = 5 * 2 * nb / (a_.elapsed_time(b_) * 1e-3) / 1e9
+        a_.record()
+        for _ in range(5):
+            src.fill_(3)
+        b_.record()
+        torch.cuda.synchronize()
+        fill = 5 * nb / (a_.elapsed_time(b_) * 1e-3) / 1e9
+        del src, dstc
+        return {"copy_gbs": round(copy, 1), "fill_gbs": round(fill, 1), "bytes": nb}
+    hbm_meas = hbm_rates()
+    log("measured HBM: %s" % hbm_meas)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -248,6 +298,19 @@ def main():
             ofn = lambda: olayer.forward(ot["x"], ot["w_off"], ot["b_off"], ot["w"], ot["b"], y=oy,
                                          offsets=oof if owl.train else None)
             fwd_ms_o = time_forward(ofn)
+            train_ms_o = None
+            if owl.train:
+                # the whole training step at this configuration (forward + backward)
+                ody = torch.from_numpy(make_inputs(owl, with_dy=True)["dy"]).to(otd).to(dev)
+                og = dict(dx=torch.empty_like(ot["x"]), dw_off=torch.empty_like(ot["w_off"]),
+                          dw=torch.empty_like(ot["w"]), db_off=torch.empty_like(ot["b_off"]),
+                          db=torch.empty_like(ot["b"]))
+
+                def ostep():
+                    ofn()
+                    olayer.backward(ot["x"], ot["w_off"], ot["w"], oof, ody, out=og)
+                train_ms_o = time_forward(ostep)
+                del ody, og
             L.deft_timing_start(8 * args.steps)
             for _ in range(args.steps):
                 ofn()
@@ -259,6 +322,8 @@ def main():
             owork = kernel_work(owl)
             rec = {"fwd_ms": round(fwd_ms_o, 4), "plan": {k: olayer.info[k] for k in ("tile_h", "tile_w", "halo",
                                                                                           "gather_direct")}}
+            if train_ms_o is not None:
+                rec["fwd_bwd_ms"] = round(train_ms_o, 4)
             for kname in ("fused_offset_sample", "gemm_forward"):
                 if kname in oper:
                     avg = sum(oper[kname]) / len(oper[kname])
@@ -316,6 +381,16 @@ def main():
             del xd, wd, wp, yd, zd
         log("dilated depthwise conv (32x1024x512 fp32), fused depthwise+pointwise: %s" % dwc)
 
+    # the fused sampling kernel together with the prologue launch it cannot
+    # run without (channel-minor copy of x and weight layouts): bytes of both
+    # over the time of both
+    prologue_frac = None
+    if "fused_offset_sample" in kernels:
+        pk = [k for k in ("x_channel_minor", "prep_forward") if k in kernels]
+        tb = sum(work[k][0] for k in ["fused_offset_sample"] + pk if k in work)
+        tt = sum(kernels[k]["avg_ms"] for k in ["fused_offset_sample"] + pk)
+        prologue_frac = round(tb / (tt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
     total_flop = sum(f for k, (b_, f) in work.items())
     gflops = total_flop / (ms_step * 1e-3) / 1e9
 
@@ -333,7 +408,17 @@ def main():
             t_cpu += time.perf_counter() - c0
             done += 1
         cpu_ms = t_cpu / done * wl.n * 1e3
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for ln in fh:
+                    if ln.startswith("model name"):
+                        model = ln.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": oracle.threads(), "kind": "oracle",
+               "cpu_model": model,
                "sample": "fp64 forward+backward of %d of the %d images (%.1f s), scaled x%d/%d to one full step"
                          % (done, wl.n, t_cpu, wl.n, done)}
         log("cpu baseline: %s" % cpu)
@@ -349,7 +434,10 @@ def main():
                    "plan": {k: info[k] for k in ("tile_h", "tile_w", "halo", "chunk", "gather_direct", "bwd_tile_h",
                                                  "bwd_tile_w", "bwd_chunk", "bwd_halo")}},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "layer_gflops": round(gflops, 1),
+        "step_ms_spread": step_spread,
+        "hbm_measured": hbm_meas,
         "fused_sample_hbm_frac": kernels.get("fused_offset_sample", {}).get("hbm_frac"),
+        "fused_sample_with_prologue_hbm_frac": prologue_frac,
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
         "fusion": fusion,
         "depthwise_dilated_1d": dwc or None,

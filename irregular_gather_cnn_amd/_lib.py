@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdeft.so")
+# DEFT_LIB names another build of the same library (e.g. a measurement
+# variant); the default is the in-tree libdeft.so
+LIB_PATH = os.environ.get("DEFT_LIB") or os.path.join(_PKG, "libdeft.so")
 
 DEFT_F32, DEFT_BF16 = 0, 1
 STATUS = {0: "DEFT_OK", -1: "DEFT_ERR_BAD_DESC", -2: "DEFT_ERR_GROUPS", -3: "DEFT_ERR_SHAPE",

@@ -29,10 +29,10 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
+    out = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [_hipcc()] + FLAGS + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -42,19 +42,27 @@ def _compile(src: str) -> str:
     return out
 
 
-def build() -> str:
-    """Compile all sources and link libdeft.so; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(lib: str = LIB, defines=()) -> str:
+    """Compile all sources and link `lib` (default: the in-tree libdeft.so);
+    `defines` are extra -D options.  Returns the library's path."""
+    obj_dir = OBJ if not defines else OBJ + "_" + "_".join(d.replace("=", "") for d in defines)
+    os.makedirs(obj_dir, exist_ok=True)
+    extra = ["-D" + d for d in defines]
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, extra), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % (r.stdout + r.stderr))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    # python build.py [OUT.so [DEFINE ...]], e.g. a variant with the hardware
+    # workgroup order: python build.py libdeft_noswizzle.so DEFT_XCD_SWIZZLE=0
+    if len(sys.argv) > 1:
+        print(build(os.path.abspath(sys.argv[1]), tuple(sys.argv[2:])))
+    else:
+        print(build())

@@ -125,7 +125,13 @@ __device__ __forceinline__ float blend4(const float* w, float v00, float v01, fl
 // round-robin over its 8 XCDs.  This maps the hardware id to a logical id
 // such that each XCD receives a contiguous range of logical ids (bijective
 // for any grid size), so neighbouring tiles share that XCD's L2.
+// (A build with DEFT_XCD_SWIZZLE=0 keeps the hardware order, to measure what
+// the mapping does for L2 hits.)
+#ifndef DEFT_XCD_SWIZZLE
+#define DEFT_XCD_SWIZZLE 1
+#endif
 __device__ __forceinline__ int xcd_swizzle(int wg, int num_wg) {
+  if (!DEFT_XCD_SWIZZLE) return wg;
   const int q = num_wg >> 3, r = num_wg & 7;
   const int xcd = wg & 7, slot = wg >> 3;
   return xcd * q + (xcd < r ? xcd : r) + slot;

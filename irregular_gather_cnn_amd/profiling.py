@@ -6,8 +6,9 @@ Two kinds of text summaries live under ``profiles/``:
   ``*_kernel_stats.csv`` the tool writes), one row per kernel;
 * HBM traffic per dispatch from two ``rocprofv3 --pmc`` runs (``FETCH_SIZE``,
   then ``WRITE_SIZE``, in KiB per dispatch).  Those counters do not read the
-  bytes one-to-one, so each is scaled by what it reads for a plain device copy
-  of known size that the same run performs (``bench.py --calib-copy-mib``).
+  bytes one-to-one, so each is scaled by what it reads for the largest plain
+  device copy the same run performs: bench.py's 1 GiB copy that measures the
+  device's HBM rate (``--calib-copy-mib`` adds a copy of another size).
   Every traffic row records a hash of the kernel's sources, so a reader can
   tell whether the kernel changed after the counters were taken.
 
@@ -15,6 +16,8 @@ Usage (after the rocprofv3 runs, on any machine)::
 
     python -m irregular_gather_cnn_amd.profiling stats STATS_CSV OUT_MD "COMMAND"
     python -m irregular_gather_cnn_amd.profiling traffic FETCH_DIR WRITE_DIR COPY_MIB OUT_MD "COMMANDS"
+    python -m irregular_gather_cnn_amd.profiling sq OUT_MD TITLE "COMMANDS" PMC_DIR...
+    python -m irregular_gather_cnn_amd.profiling tcc ON_DIR OFF_DIR OUT_MD "COMMANDS"
 """
 from __future__ import annotations
 
@@ -38,9 +41,10 @@ KERNELS = {
     "fused_gather_gemm": (r"k_igemm\b", ["deft_igemm.hip", "deft_device.h"]),
     "dwconv1d": (r"k_dwconv1d\b", ["deft_dwconv.hip"]),
     "dwpw1d": (r"k_dwpw1d\b", ["deft_dwpw.hip"]),
-    "gemm_forward": (r"k_gemm_dl<.*DlFwd|k_gemm<.*FwdOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "gemm_forward": (r"k_gemm_(dl|vd)<.*(DlFwd|FwdBal)|k_gemm<.*FwdOp",
+                     ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
-    "gemm_dw": (r"k_gemm_dl<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "gemm_dw": (r"k_gemm_(dl|ws)<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "sample_backward": (r"k_sample_bwd<|k_sample_bwd_mf\b", ["deft_backward.hip", "deft_device.h"]),
     "sample_backward_miss": (r"k_sample_bwd_miss<", ["deft_backward.hip", "deft_device.h"]),
     "sample_backward_list": (r"k_sample_bwd_list\b", ["deft_backward.hip", "deft_device.h"]),
@@ -180,12 +184,100 @@ def write_stats_md(stats_csv, path, command):
         fh.write("\n".join(lines) + "\n")
 
 
+def counters_table(dirs):
+    """{kernel: {counter: value per dispatch averaged over its dispatches}} from pmc runs."""
+    out = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        rows = _rows(d)
+        names = sorted({r["Counter_Name"] for r in rows})
+        for c in names:
+            for sym, grid, v in _per_dispatch(rows, c).values():
+                name = bench_name_of(sym)
+                if name:
+                    out[name][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in out.items()}
+
+
+SQ_COLS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+           "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_LDS_IDX_ACTIVE",
+           "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def write_sq_md(path, table, title, commands, simds=1024, xcds=8):
+    def g(t, c):
+        return t.get(c)
+
+    def pct(a, b):
+        return "%.0f %%" % (100.0 * a / b) if a is not None and b else "-"
+
+    cols = [c for c in SQ_COLS if any(c in t for t in table.values())]
+    lines = ["# " + title, "", "Commands (from the repository root, on the GPU machine; R = the repository root):", "",
+             "```"] + commands + ["```", "",
+             "Each value is the counter summed over its hardware instances for one dispatch, averaged over the "
+             "dispatches of the kernel in the run. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d "
+             "XCDs x %d SIMDs): GRBM_GUI_ACTIVE is summed over the %d XCDs and SQ_VALU_MFMA_BUSY_CYCLES over the "
+             "SIMDs (32 busy cycles per 32x32x16 bf16 MFMA), so this is the share of the dispatch's active cycles "
+             "in which an average SIMD's matrix unit was busy (MFMAs on padded rows count as busy)."
+             % (xcds, simds, xcds), "",
+             "| kernel | " + " | ".join(c.replace("SQ_", "") for c in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    order = sorted(table, key=lambda k: -(table[k].get("GRBM_GUI_ACTIVE") or table[k].get("SQ_WAVE_CYCLES") or 0))
+    for k in order:
+        t = table[k]
+        lines.append("| %s | " % k + " | ".join("%d" % t[c] if c in t else "-" for c in cols) + " |")
+    lines += ["", "Derived ratios:", "",
+              "| kernel | waiting / wave cycles | waiting on a dependency / wave cycles | LDS bank-conflict cycles / "
+              "LDS active cycles | VALU instructions per MFMA | MFMA busy |", "|---|---|---|---|---|---|"]
+    for k in order:
+        t = table[k]
+        mf = g(t, "SQ_INSTS_MFMA")
+        vpm = "%.0f" % (g(t, "SQ_INSTS_VALU") / mf) if mf and g(t, "SQ_INSTS_VALU") is not None else "-"
+        busy = g(t, "SQ_VALU_MFMA_BUSY_CYCLES")
+        act = g(t, "GRBM_GUI_ACTIVE")
+        lines.append("| %s | %s | %s | %s | %s | %s |" % (
+            k, pct(g(t, "SQ_WAIT_ANY"), g(t, "SQ_WAVE_CYCLES")), pct(g(t, "SQ_WAIT_INST_ANY"), g(t, "SQ_WAVE_CYCLES")),
+            pct(g(t, "SQ_LDS_BANK_CONFLICT"), g(t, "SQ_LDS_IDX_ACTIVE")), vpm,
+            pct(busy, act / xcds * simds if act else None)))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def write_tcc_md(path, on, off, commands):
+    lines = ["# L2 (TCC) hits and misses per dispatch, XCD-aware block order on and off", "",
+             "Commands (from the repository root, on the GPU machine; R = the repository root):", "", "```"] + \
+            commands + ["```", "",
+                        "Each value is TCC_HIT_sum / TCC_MISS_sum for one dispatch, averaged over the kernel's "
+                        "dispatches. 'off' is a build whose workgroup order is the hardware's (consecutive "
+                        "workgroups on different XCDs); everything else is identical.", "",
+                        "| kernel | hits (on) | misses (on) | hit rate (on) | hits (off) | misses (off) | "
+                        "hit rate (off) |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(set(on) | set(off)):
+        a, b = on.get(k, {}), off.get(k, {})
+
+        def hr(t):
+            h, m = t.get("TCC_HIT_sum"), t.get("TCC_MISS_sum")
+            return "%.1f %%" % (100.0 * h / (h + m)) if h is not None and m is not None and h + m else "-"
+        lines.append("| %s | %s | %s | %s | %s | %s | %s |" % (
+            k, "%d" % a["TCC_HIT_sum"] if "TCC_HIT_sum" in a else "-",
+            "%d" % a["TCC_MISS_sum"] if "TCC_MISS_sum" in a else "-", hr(a),
+            "%d" % b["TCC_HIT_sum"] if "TCC_HIT_sum" in b else "-",
+            "%d" % b["TCC_MISS_sum"] if "TCC_MISS_sum" in b else "-", hr(b)))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         write_stats_md(argv[1], argv[2], argv[3])
     elif len(argv) >= 6 and argv[0] == "traffic":
         table, calib = traffic_table(argv[1], argv[2], int(argv[3]))
         write_traffic_md(argv[4], table, calib, argv[5].split("\n"))
+    elif len(argv) >= 5 and argv[0] == "sq":
+        # sq OUT_MD TITLE COMMANDS DIR...
+        write_sq_md(argv[1], counters_table(argv[4:]), argv[2], argv[3].split("\n"))
+    elif len(argv) == 5 and argv[0] == "tcc":
+        # tcc ON_DIR OFF_DIR OUT_MD COMMANDS
+        write_tcc_md(argv[3], counters_table([argv[1]]), counters_table([argv[2]]), argv[4].split("\n"))
     else:
         print(__doc__)
         return 2
