@@ -19,12 +19,17 @@
  * below as O1..O5, and the backward pass B1..B6 is the exact derivative of it
  * (the page only mentions training time).
  *
- * Everything is fp64 (inputs arrive already upcast, exactly, from fp32 or
+ * Arithmetic is fp64 (inputs arrive already upcast, exactly, from fp32 or
  * bf16).  Loops are the definitions written out; OpenMP splits independent
  * output elements only, so every output's summation order is the one written.
- * The one exception is oracle_sample_index_f32, which defines the integer
- * tap-index / corner-mask stage in fp32 (one fp32 add, then floor); this file
- * must be compiled with -ffp-contract=off and without -ffast-math.
+ * Integer decisions are the exception: which cell of four neighbours a
+ * sample point falls in, and whether it is fully outside, are taken on the
+ * fp32 coordinate (the fp32 offset added to the integer grid position in one
+ * fp32 add), the precision the layer hands offsets over in; see
+ * sample_point and oracle_sample_index_f32.  The value is continuous across
+ * a cell edge, but its derivative in the offset is not, so the backward pass
+ * depends on that choice.  This file must be compiled with -ffp-contract=off
+ * and without -ffast-math.
  *
  * Notation: K = kh*kw taps, tap k = i*kw + j; G offset groups of Cg = Cin/G
  * channels; Oc = 2*G*K offset channels, channel 2*(g*K+k) holds dy and
@@ -90,39 +95,53 @@ void oracle_offset_conv(const odesc* d, const double* x, const double* w_off,
         }
 }
 
-/* O3 + O4 for one sample point (py, px): bilinear interpolation of channel c
- * of image n with zero padding per corner.  A point is "fully outside" unless
- * -1 < py < H and -1 < px < W (NaN compares false, so it is outside); a fully
- * outside point reads 0 and has zero weights.  Otherwise y0 = floor(py),
- * x0 = floor(px), ly = py - y0, lx = px - x0 and the value is the
- * (1-ly)(1-lx), (1-ly)lx, ly(1-lx), ly*lx weighted sum of the four corners. */
-static int fully_outside(const odesc* d, double py, double px) {
-  return !(py > -1.0 && py < (double)d->h && px > -1.0 && px < (double)d->w);
+/* O2 + O3: the sample point of tap k = (i, j) of output (ho, wo) for the
+ * offset group g: the base grid position plus (dy, dx) read from offset
+ * channels 2(gK+k) and 2(gK+k)+1, in fp64 (py, px).  Its cell (y0, x0) and
+ * the fully-outside test are decided on the fp32 coordinate, exactly as in
+ * oracle_sample_index_f32: fy = base + (float)dy in one fp32 add; fully
+ * outside unless -1 < fy < H and -1 < fx < W (NaN compares false, so it is
+ * outside); otherwise y0 = floor(fy), x0 = floor(fx).  Where fy rounds across
+ * an integer that py does not reach, ly = py - y0 below falls outside [0, 1]
+ * by less than one fp32 ulp of the coordinate. */
+typedef struct {
+  double py, px;
+  int y0, x0, outside;
+} tap_pt;
+
+static tap_pt sample_point(const odesc* d, const double* off, int n, int g, int k, int ho,
+                           int wo) {
+  const int K = d->kh * d->kw, Oc = 2 * d->groups * K;
+  const int Ho = out_h(d), Wo = out_w(d);
+  const int i = k / d->kw, j = k % d->kw;
+  const int by = ho * d->stride_h - d->pad_h + i * d->dil_h;
+  const int bx = wo * d->stride_w - d->pad_w + j * d->dil_w;
+  const double dy = off[(((size_t)n * Oc + 2 * (g * K + k)) * Ho + ho) * Wo + wo];
+  const double dx = off[(((size_t)n * Oc + 2 * (g * K + k) + 1) * Ho + ho) * Wo + wo];
+  tap_pt t;
+  t.py = (double)by + dy;
+  t.px = (double)bx + dx;
+  const volatile float fy = (float)by + (float)dy;
+  const volatile float fx = (float)bx + (float)dx;
+  t.outside = !(fy > -1.0f && fy < (float)d->h && fx > -1.0f && fx < (float)d->w);
+  t.y0 = t.outside ? 0 : (int)floorf(fy);
+  t.x0 = t.outside ? 0 : (int)floorf(fx);
+  return t;
 }
 
-static double bilinear(const odesc* d, const double* x, int n, int c, double py, double px) {
-  if (fully_outside(d, py, px)) return 0.0;
-  const double fy = floor(py), fx = floor(px);
-  const int y0 = (int)fy, x0 = (int)fx;
-  const double ly = py - fy, lx = px - fx;
+/* O3 + O4 for one sample point: bilinear interpolation of channel c of image
+ * n with zero padding per corner.  A fully outside point reads 0 and has zero
+ * weights.  Otherwise ly = py - y0, lx = px - x0 and the value is the
+ * (1-ly)(1-lx), (1-ly)lx, ly(1-lx), ly*lx weighted sum of the four corners
+ * (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1). */
+static double bilinear(const odesc* d, const double* x, int n, int c, tap_pt t) {
+  if (t.outside) return 0.0;
+  const int y0 = t.y0, x0 = t.x0;
+  const double ly = t.py - y0, lx = t.px - x0;
   return (1.0 - ly) * (1.0 - lx) * xz(d, x, n, c, y0, x0) +
          (1.0 - ly) * lx * xz(d, x, n, c, y0, x0 + 1) +
          ly * (1.0 - lx) * xz(d, x, n, c, y0 + 1, x0) +
          ly * lx * xz(d, x, n, c, y0 + 1, x0 + 1);
-}
-
-/* O2 + O3: the sample point of tap k = (i, j) of output (ho, wo) for the
- * offset group g: the base grid position plus (dy, dx) read from offset
- * channels 2(gK+k) and 2(gK+k)+1. */
-static void sample_point(const odesc* d, const double* off, int n, int g, int k, int ho,
-                         int wo, double* py, double* px) {
-  const int K = d->kh * d->kw, Oc = 2 * d->groups * K;
-  const int Ho = out_h(d), Wo = out_w(d);
-  const int i = k / d->kw, j = k % d->kw;
-  const double dy = off[(((size_t)n * Oc + 2 * (g * K + k)) * Ho + ho) * Wo + wo];
-  const double dx = off[(((size_t)n * Oc + 2 * (g * K + k) + 1) * Ho + ho) * Wo + wo];
-  *py = (double)(ho * d->stride_h - d->pad_h + i * d->dil_h) + dy;
-  *px = (double)(wo * d->stride_w - d->pad_w + j * d->dil_w) + dx;
 }
 
 /* O4 for every (n, pixel, channel, tap): the deformed column buffer. */
@@ -135,10 +154,8 @@ void oracle_sample_cols(const odesc* d, const double* x, const double* off, doub
       for (int wo = 0; wo < Wo; ++wo)
         for (int c = 0; c < d->c_in; ++c)
           for (int k = 0; k < K; ++k) {
-            double py, px;
-            sample_point(d, off, n, c / Cg, k, ho, wo, &py, &px);
             col[((((size_t)n * Ho + ho) * Wo + wo) * d->c_in + c) * K + k] =
-                bilinear(d, x, n, c, py, px);
+                bilinear(d, x, n, c, sample_point(d, off, n, c / Cg, k, ho, wo));
           }
 }
 
@@ -184,9 +201,9 @@ void oracle_forward(const odesc* d, const double* x, const double* w_off, const 
  *   B2  dcol[n][p][c][k] = sum_co W[co][c][k] dY[n][co][p]
  *   B3  dx_s: each in-image corner of each not-fully-outside tap receives
  *       dcol times that corner's bilinear weight
- *   B4  ddy, ddx: derivative of the bilinear value in py, px (one-sided at
- *       integer coordinates, following the floor convention), summed over the
- *       channels of the tap's offset group
+ *   B4  ddy, ddx: derivative of the bilinear value in py, px within the
+ *       point's cell (y0, x0) (so one-sided at a cell edge, on the side the
+ *       fp32 floor chose), summed over the channels of the tap's offset group
  *   B5  db_off = sum doff; dW_off = doff against the plain im2col of x;
  *       dx_o = transposed convolution of doff with W_off
  *   B6  dx = dx_s + dx_o */
@@ -239,13 +256,11 @@ void oracle_backward(const odesc* d, const double* x, const double* w_off, const
       for (int ho = 0; ho < Ho; ++ho)
         for (int wo = 0; wo < Wo; ++wo)
           for (int k = 0; k < K; ++k) {
-            double py, px;
-            sample_point(d, off, n, c / Cg, k, ho, wo, &py, &px);
-            if (fully_outside(d, py, px)) continue;
+            const tap_pt t = sample_point(d, off, n, c / Cg, k, ho, wo);
+            if (t.outside) continue;
             const double g = dcol[(((size_t)n * P + (size_t)ho * Wo + wo) * d->c_in + c) * K + k];
-            const double fy = floor(py), fx = floor(px);
-            const int y0 = (int)fy, x0 = (int)fx;
-            const double ly = py - fy, lx = px - fx;
+            const int y0 = t.y0, x0 = t.x0;
+            const double ly = t.py - y0, lx = t.px - x0;
             const int cy[4] = {y0, y0, y0 + 1, y0 + 1};
             const int cx[4] = {x0, x0 + 1, x0, x0 + 1};
             const double cw[4] = {(1.0 - ly) * (1.0 - lx), (1.0 - ly) * lx, ly * (1.0 - lx),
@@ -263,12 +278,11 @@ void oracle_backward(const odesc* d, const double* x, const double* w_off, const
       for (int k = 0; k < K; ++k)
         for (int ho = 0; ho < Ho; ++ho)
           for (int wo = 0; wo < Wo; ++wo) {
-            double py, px, gy = 0.0, gx = 0.0;
-            sample_point(d, off, n, g, k, ho, wo, &py, &px);
-            if (!fully_outside(d, py, px)) {
-              const double fy = floor(py), fx = floor(px);
-              const int y0 = (int)fy, x0 = (int)fx;
-              const double ly = py - fy, lx = px - fx;
+            double gy = 0.0, gx = 0.0;
+            const tap_pt t = sample_point(d, off, n, g, k, ho, wo);
+            if (!t.outside) {
+              const int y0 = t.y0, x0 = t.x0;
+              const double ly = t.py - y0, lx = t.px - x0;
               for (int c = g * Cg; c < (g + 1) * Cg; ++c) {
                 const double v00 = xz(d, x, n, c, y0, x0), v01 = xz(d, x, n, c, y0, x0 + 1);
                 const double v10 = xz(d, x, n, c, y0 + 1, x0), v11 = xz(d, x, n, c, y0 + 1, x0 + 1);

@@ -237,6 +237,9 @@ FD_SHAPES = [
     Shape(1, 4, 7, 5, 3, stride=(2, 2), pad=(0, 1)),
     Shape(2, 4, 6, 6, 2, dil=(2, 2), pad=(2, 1), groups=2),
     Shape(1, 4, 5, 7, 3, stride=(1, 2), groups=2),
+    # non-square and larger kernels (the shapes the GPU edge tests use)
+    Shape(1, 4, 6, 5, 2, kh=3, kw=2, pad=(1, 1)),
+    Shape(1, 4, 7, 7, 2, kh=5, kw=5, pad=(2, 2)),
 ]
 
 
@@ -330,6 +333,37 @@ def test_grad_offsets_on_affine_image(oracle):
             ex = float(np.sum(wk * bb[gi * cg:(gi + 1) * cg]))
             assert np.allclose(g["doff"][0, 2 * (gi * s.taps + k)][inside], ey, atol=1e-12)
             assert np.allclose(g["doff"][0, 2 * (gi * s.taps + k) + 1][inside], ex, atol=1e-12)
+
+
+def test_grad_offsets_cell_chosen_on_fp32_coordinate(oracle):
+    """The offset gradient is one-sided at a cell edge, so it depends on which
+    cell the sample point is put in; that choice is made on the fp32
+    coordinate (the index stage's rule).  On x[y,x] = y^2 + 10 x^2 with one
+    1x1 tap, W = 1 and dY = 1, a point in cell (y0, x0) has ddy = 2*y0 + 1
+    and ddx = 10*(2*x0 + 1).  dy = 1 - 2^-24 on base row 2 sums to 3.0 in
+    fp32 (cell row 3: 7, where an fp64 floor would give row 2: 5); on base row
+    0 the fp32 sum stays below 1 (cell row 0: 1).  The value itself is
+    continuous across the edge."""
+    s = Shape(1, 1, 6, 6, 1, kh=1, kw=1, pad=(0, 0))
+    yy, xx = np.meshgrid(np.arange(6.0), np.arange(6.0), indexing="ij")
+    x = (yy ** 2 + 10 * xx ** 2)[None, None]
+    e = float(np.float32(1.0 - 2.0 ** -24))
+    off = np.zeros((1, 2, 6, 6))
+    off[0, 0, 2, 1] = e      # row 2 + e -> 3.0 in fp32
+    off[0, 0, 0, 0] = e      # row 0 + e stays in cell 0
+    off[0, 1, 1, 2] = e      # column 2 + e -> 3.0 in fp32
+    g = oracle.backward(s, x, np.zeros((2, 1, 1, 1)), np.ones((1, 1, 1, 1)), off, np.ones((1, 1, 6, 6)))
+    cases = {(2, 1): (3, 1), (0, 0): (0, 0), (1, 2): (1, 3), (4, 4): (4, 4)}
+    for (ho, wo), (y0, x0) in cases.items():
+        assert g["doff"][0, 0, ho, wo] == 2 * y0 + 1, (ho, wo)
+        assert g["doff"][0, 1, ho, wo] == 10 * (2 * x0 + 1), (ho, wo)
+    iy, ix, _ = oracle.sample_index_f32(s, off.astype(np.float32))
+    for (ho, wo), (y0, x0) in cases.items():
+        assert (iy[0, 0, 0, ho, wo], ix[0, 0, 0, ho, wo]) == (y0, x0)
+    # bilinear interpolation of y^2 between rows 2 and 3 is 4 + 5*e
+    col = oracle.sample_cols(s, x, off)
+    assert abs(col[0, 2 * 6 + 1, 0, 0] - (4 + 5 * e + 10)) < 1e-6
+    assert abs(col[0, 1 * 6 + 2, 0, 0] - (1 + 10 * (4 + 5 * e))) < 1e-5
 
 
 # --- the fp32 index stage ---------------------------------------------------------
