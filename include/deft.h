@@ -147,10 +147,18 @@ void deft_plan_destroy(deft_plan* p);
  * columns are kept for deft_backward (training = 1). */
 size_t deft_workspace_bytes(const deft_plan* p, int training);
 
-/* Forward.  x, w_off, w, y and workspace are required; b_off and b may be
- * NULL (zero bias).  offsets_out (fp32 [N][Oc][Ho][Wo]) may be NULL; when
- * given, the fused kernel also writes the offsets it computed there (needed
- * by deft_backward).  The deformed columns are left in the workspace. */
+/* Forward of the layer (DefT explainer page, "Following a deformable layer
+ * through DefT": the offset convolution predicts each tap's fractional
+ * displacement, the four neighbours of every displaced tap are blended
+ * bilinearly into the deformed columns, and the main convolution multiplies
+ * them; "This paper's idea": the offset convolution and the interpolation run
+ * as one kernel, so the offsets stay on chip).  x, w_off, w, y and workspace
+ * are required; b_off and b may be NULL (zero bias).  offsets_out (fp32
+ * [N][Oc][Ho][Wo]) may be NULL; when given, the fused kernel also writes the
+ * offsets it computed there (needed by deft_backward).  The deformed columns
+ * are left in the workspace.  DEFT_ERR_NULLPTR, DEFT_ERR_WORKSPACE (NULL or
+ * smaller than deft_workspace_bytes(p, 0)), DEFT_ERR_ALIGN; checks run before
+ * any launch. */
 int deft_forward(const deft_plan* p, const void* x, const void* w_off, const void* b_off,
                  const void* w, const void* b, void* y, float* offsets_out, void* workspace,
                  size_t ws_bytes, void* stream);
@@ -202,16 +210,25 @@ int deft_forward_unfused(const deft_plan* p, const void* x, const void* w_off, c
                          const void* w, const void* b, void* y, float* offsets, void* workspace,
                          size_t ws_bytes, void* stream);
 
-/* Backward of the forward that last ran on this workspace (it must have been
- * sized with training = 1 and the forward must have written offsets_out,
- * passed here as `offsets`).  dy [N][Cout][Ho][Wo].  Writes (overwrites) dx,
- * dw_off, dw; db_off and db may be NULL.  Gradients are accumulated in fp32
- * and rounded once to the dtype. */
+/* Backward of the layer.  The DefT explainer page speaks of training only
+ * through its cost ("This paper's idea", "Why it works": the layer's share of
+ * training time), so this is the exact derivative of deft_forward: dW and db
+ * of the main convolution, dCol, the bilinear scatter of dCol into dX with the
+ * offset gradient from the corner differences, and the offset convolution's
+ * dW_off, db_off and its contribution to dX.  It belongs to the forward that
+ * last ran on this workspace (sized with training = 1; that forward must have
+ * written offsets_out, passed here as `offsets`).  dy [N][Cout][Ho][Wo].
+ * Writes (overwrites) dx, dw_off, dw; db_off and db may be NULL.  Gradients
+ * are accumulated in fp32 and rounded once to the dtype.  DEFT_ERR_NULLPTR,
+ * DEFT_ERR_WORKSPACE, DEFT_ERR_ALIGN, DEFT_ERR_PLAN (a plan without a
+ * backward: bwd_chunk 0); checks run before any launch. */
 int deft_backward(const deft_plan* p, const void* x, const void* w_off, const void* w,
                   const float* offsets, const void* dy, void* workspace, size_t ws_bytes,
                   void* dx, void* dw_off, void* db_off, void* dw, void* db, void* stream);
 
-/* The integer tap-index / corner-mask stage on its own, from fp32 offsets:
+/* The integer tap-index / corner-mask stage on its own (DefT explainer page,
+ * "Following a deformable layer through DefT", step 1: every filter position
+ * at every output location gets its own sampling point), from fp32 offsets:
  * for every (n, g, k, ho, wo), laid out [N][G][kh*kw][Ho][Wo]:
  * py = float(ho*s - p + i*d) + dy (one fp32 add), px likewise; fully outside
  * taps give y0 = x0 = 0, mask = 0; otherwise y0 = floor(py), x0 = floor(px)
@@ -221,9 +238,12 @@ int deft_backward(const deft_plan* p, const void* x, const void* w_off, const vo
 int deft_debug_sample_index(const deft_desc* d, const float* offsets, int32_t* y0, int32_t* x0,
                             uint8_t* mask, void* stream);
 
-/* The sampling stage alone from given fp32 offsets (unfused path), writing
- * the deformed columns [N][Ho*Wo][kh*kw][Cin] (tap-major, channel-minor) of
- * the descriptor's dtype to `cols`. */
+/* The sampling stage alone from given fp32 offsets, as the separate
+ * interpolation operator of the three-operator layer (DefT explainer page,
+ * "What people did before this paper"), writing the deformed columns
+ * [N][Ho*Wo][kh*kw][Cin] (tap-major, channel-minor) of the descriptor's dtype
+ * to `cols`.  DEFT_ERR_NULLPTR, DEFT_ERR_ALIGN (x and cols 16-byte, offsets
+ * 4-byte aligned), DEFT_ERR_PLAN; checks run before any launch. */
 int deft_debug_sample(const deft_plan* p, const void* x, const float* offsets, void* cols,
                       void* stream);
 

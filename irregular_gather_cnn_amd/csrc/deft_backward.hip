@@ -299,6 +299,17 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
   T* dst = (T*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;
   acc_t* dxl = (acc_t*)(smem + p.lds_dx);  // [CH*CW][CC], then one spill slot per lane
   acc_t* spill = dxl + p.CH * p.CW * p.CC + lane;
+  // Non-finite contributions (a NaN or infinite dCol) cannot be held in fixed
+  // point: each sets a flag of its element instead, four bits per element
+  // (1 NaN, 2 +Inf, 4 -Inf), eight elements per word, after the spill slots.
+  // The element is then written as the IEEE sum of those contributions
+  // would be: NaN if any was NaN or both infinities occurred, else the
+  // infinity.
+  uint32_t* nflags = (uint32_t*)(dxl + p.CH * p.CW * p.CC + 64);
+  auto flag_nonfinite = [&](int el, float v) {
+    const uint32_t f = v != v ? 1u : (v > 0.f ? 2u : 4u);
+    atomicOr(nflags + (el >> 3), f << (4 * (el & 7)));
+  };
   const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
   const int epi = 64 / lpe;    // rows per load instruction
   const size_t pstride = (size_t)p.N * p.Oc * HoWo;
@@ -311,6 +322,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     __syncthreads();
     stage_region<T>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
     for (int k = tid; k < p.CH * p.CW * p.CC; k += 256) dxl[k] = 0;
+    for (int k = tid; k < (p.CH * p.CW * p.CC + 7) / 8; k += 256) nflags[k] = 0;
     __syncthreads();
     int eb = wave * BLK;
     int4 my = make_int4(0, 0, 0, 0);
@@ -363,10 +375,14 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
             for (int qq = 0; qq < 4; ++qq) {
               if (cm & (1u << qq)) {
                 const float xv = gs * w[qq];
+                const int off = ((qq >> 1) * p.CW + (qq & 1)) * p.CC;
+                if (!(fabsf(xv) <= 3.402823466e38f)) {
+                  flag_nonfinite((int)(d0 + off - dxl), xv);
+                  continue;
+                }
                 const float fh = floorf(xv);
                 const uint32_t lo = (uint32_t)((xv - fh) * 4294967296.0f);
-                atomicAdd(d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC,
-                          ((unsigned long long)(uint32_t)(int)fh << 32) | lo);
+                atomicAdd(d0 + off, ((unsigned long long)(uint32_t)(int)fh << 32) | lo);
               }
             }
           }
@@ -395,7 +411,12 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               acc_t* da = ((cm >> qq) & 1u) ? d0 + ((qq >> 1) * p.CW + (qq & 1)) * p.CC : spill;
-              atomicAdd(da, (uint32_t)cvt_rpi(gs[u] * w[qq]));
+              const float xv = gs[u] * w[qq];
+              if (!(fabsf(xv) <= 3.402823466e38f)) {  // rare: flagged, and the fixed-point add is skipped
+                if (da != spill) flag_nonfinite((int)(da - dxl), xv);
+                continue;
+              }
+              atomicAdd(da, (uint32_t)cvt_rpi(xv));
             }
           }
         }
@@ -407,9 +428,13 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     for (int k = tid; k < p.CC * chn * cwn; k += 256) {
       const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
       const int y = r / cwn, xx = r - y * cwn;
-      const acc_t a = dxl[(y * p.CW + xx) * p.CC + cc];
+      const int el = (y * p.CW + xx) * p.CC + cc;
+      const acc_t a = dxl[el];
       const double sv = kWide ? (double)(long long)a : (double)(int)(uint32_t)a;
-      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = (float)(sv * inv);
+      float v = (float)(sv * inv);
+      const uint32_t f = (nflags[el >> 3] >> (4 * (el & 7))) & 15u;
+      if (f) v = ((f & 1u) || (f & 6u) == 6u) ? __builtin_nanf("") : ((f & 2u) ? __builtin_inff() : -__builtin_inff());
+      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = v;
     }
   }
 }

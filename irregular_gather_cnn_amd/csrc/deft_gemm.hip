@@ -271,7 +271,10 @@ struct DcolOp {
         const int e0 = mb + 8 * j + 4 * (lane >> 5);
         if (e0 < M)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[4 * j + r]));
+          for (int r = 0; r < 4; ++r) {
+            const float a = fabsf(acc[4 * j + r]);
+            if (a <= 3.402823466e38f) mx = fmaxf(mx, a);  // NaN and Inf are flagged by the scatter instead
+          }
       }
     }
     for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s));

@@ -843,7 +843,10 @@ struct DlDcol {
         if (nw + j * 32 + (lane & 31) >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (mw + i * 32 + acc_row(lane, r) < M) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+          if (mw + i * 32 + acc_row(lane, r) < M) {
+            const float a = fabsf(acc[i][j][r]);
+            if (a <= 3.402823466e38f) mx = fmaxf(mx, a);  // NaN and Inf are flagged by the scatter instead
+          }
       }
     for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
     if (lane == 0 && __float_as_uint(mx) > __hip_atomic_load(maxbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))

@@ -131,7 +131,8 @@ bool layout_backward(deft_plan& p) {
     ldx = 4 * 4096;
     ldc = 4 * 32 * (cb + 16) * 2;  // with the tiles, also holds the final 2 x [channel][65] fp32 sums
   } else {
-    ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8));  // fixed-point dX of the core + spill slots
+    // fixed-point dX of the core, spill slots, non-finite flags (4 bits per element)
+    ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8) + (ch * cw * cb + 7) / 8 * 4);
     ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
   }
   const int total = lx + ldx + ldc + 16 + 4 * 49 * 4 + 48 * 8;  // + list counter and per-tap tables
@@ -279,13 +280,16 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
 }
 
 // Share of (not fully outside) taps whose corner lies beyond `halo` pixels.
+// Without a histogram, or with one that counted no tap at all, default
+// shares.
 double miss_fraction(const uint32_t* hist, int len, int halo) {
-  if (!hist || len < 3) return halo >= 2 ? 0.01 : (halo == 1 ? 0.3 : 0.7);
-  double in = 0, tot = 0;
-  for (int i = 0; i < len - 1; ++i) {
-    tot += hist[i];
+  double in = 0, tot = 0, all = 0;
+  for (int i = 0; hist && i < len; ++i) {
+    all += hist[i];
+    if (i < len - 1) tot += hist[i];
     if (i <= halo && i < len - 2) in += hist[i];
   }
+  if (!hist || len < 3 || all <= 0) return halo >= 2 ? 0.01 : (halo == 1 ? 0.3 : 0.7);
   return tot > 0 ? 1.0 - in / tot : 0.0;
 }
 
@@ -296,11 +300,13 @@ double miss_fraction(const uint32_t* hist, int len, int halo) {
 // of the sampling backward by about one percent.  So it is the smallest halo
 // that leaves no more than 1e-5 of the taps outside, apart from those in the
 // histogram's open-ended last distance bin, which no halo it describes can
-// take in (capped at 16).  Without a histogram: 4 pixels.
+// take in (capped at 16).  Without a histogram, or with one that counted no
+// tap: 4 pixels.
 int backward_halo(const uint32_t* hist, int len) {
   if (!hist || len < 3) return 4;
   double tot = 0;
   for (int i = 0; i < len - 1; ++i) tot += hist[i];
+  if (tot + hist[len - 1] <= 0) return 4;  // a histogram that counted no tap says nothing
   const double allowed = hist[len - 2] + 1e-5 * tot;
   double in = 0;
   const int hmax = std::min(16, len - 3);

@@ -20,9 +20,9 @@ struct deft_plan {
   int reg_h, reg_w;            // largest halo region (input pixels)
   int pstr, pstr_a;            // LDS pixel strides (elements)
   int lds_region, lds_off, lds_info, lds_total;  // byte offsets / total
-  int direct;
-  int bwd_mf;   // bf16 sampling backward with the scatter on the MFMA units
-  int stage_d;  // direct: footprint-staging loads per wave per channel chunk                  // 1: corners gathered from a channel-minor copy of x (no LDS halo)
+  int direct;                  // 1: corners gathered from a channel-minor copy of x (no LDS halo)
+  int bwd_mf;                  // bf16 sampling backward with the scatter on the MFMA units
+  int stage_d;                 // direct: footprint-staging loads per wave per channel chunk
   int oc_pad;                  // rows of the prepared offset-conv weight
   double est_miss;
   // workspace layout (byte offsets, 256-aligned)

@@ -252,7 +252,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       if (p.off_out && ty < thn && tx < twn)
         p.off_out[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx] = v;
     }
-    if (p.offsets_only) return;  // uniform: the whole workgroup leaves together
+    if (p.offsets_only) {  // uniform: the whole workgroup leaves together
+      // (the histogram of the offsets it computed still counts)
+      if (p.hist) {
+        __syncthreads();
+        tile_halo_hist(p, off_l, p.GW, oh0, ow0, thn, twn);
+      }
+      return;
+    }
   } else {
     const int tot = ocw * PT;
     for (int e = tid; e < tot; e += 256) {
@@ -581,7 +588,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       if (p.off_out && ty < thn && tx < twn)
         p.off_out[(((size_t)n * p.Oc + obase + o) * p.Ho + oh0 + ty) * p.Wo + ow0 + tx] = v;
     }
-    if constexpr (MODE == kOffsetsMode) return;
+    if constexpr (MODE == kOffsetsMode) {
+      // the offsets alone (the gather-fused forward samples in its GEMM);
+      // their histogram still counts
+      if (p.hist) {
+        __syncthreads();
+        tile_halo_hist(p, off_l, 1, oh0, ow0, thn, twn);
+      }
+      return;
+    }
     __syncthreads();
   }
 

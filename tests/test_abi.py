@@ -87,6 +87,34 @@ def test_planner_sizes_halo_from_histogram():
     assert L.deft_plan_get_info(L.deft_plan_create(d, [0, 0, 0, 0, 0, 0, 50, 0]))["bwd_halo"] == 0
     # a tail reaching the open-ended bin: the last bin a halo can take in
     assert L.deft_plan_get_info(L.deft_plan_create(d, [10, 10, 10, 10, 10, 10, 10, 0]))["bwd_halo"] == 5
+    # a histogram that counted no tap at all (e.g. a forward whose launch emitted none) carries no
+    # information: the same plan as without a histogram
+    none = L.deft_plan_get_info(L.deft_plan_create(d))
+    empty = L.deft_plan_get_info(L.deft_plan_create(d, [0] * 16))
+    assert empty["bwd_halo"] == none["bwd_halo"] == 4
+    assert empty["est_miss_fraction"] == none["est_miss_fraction"]
+    assert (empty["tile_h"], empty["tile_w"], empty["halo"]) == (none["tile_h"], none["tile_w"], none["halo"])
+
+
+@pytest.mark.fake_pointers
+@pytest.mark.parametrize("kw,dtype", [(dict(w=320), L.DEFT_F32), (dict(w=400, dil=(4, 4), pad=(4, 4)), L.DEFT_BF16)])
+def test_wide_image_plan_without_backward(kw, dtype):
+    """Images so wide that not even a one-row band of the offset-weight
+    backward's staged input fits the LDS: the plan is made (the forward runs)
+    but has no backward, and deft_backward refuses it before any launch."""
+    d = desc(n=1, c_in=32, h=4, c_out=16, dtype=dtype, **kw)
+    p = L.deft_plan_create(d)
+    info = L.deft_plan_get_info(p)
+    assert info["bwd_chunk"] == 0 and info["ws_forward"] > 0
+    big = 1 << 40
+    with pytest.raises(L.DeftError) as e:
+        # pointers are never dereferenced: validation refuses the plan first
+        L.deft_backward(p, 16, 16, 16, 16, 16, 16, big, 16, 16, None, 16, None)
+    assert e.value.code == -9
+    L.deft_plan_destroy(p)
+    # a slightly narrower image keeps its backward
+    d2 = desc(n=1, c_in=32, h=4, c_out=16, dtype=dtype, **dict(kw, w=kw["w"] // 2))
+    assert L.deft_plan_get_info(L.deft_plan_create(d2))["bwd_chunk"] > 0
 
 
 def test_forward_halo_avoids_single_workgroup_occupancy():
@@ -183,6 +211,7 @@ def test_forced_gather_gemm_plan():
 FAKE = 1 << 40  # 16-byte aligned, never dereferenced (validation fails first)
 
 
+@pytest.mark.fake_pointers
 def test_forward_validation_before_launch():
     d = desc()
     p = L.deft_plan_create(d)
@@ -207,6 +236,7 @@ def test_forward_validation_before_launch():
     assert lib.deft_forward(None, *ok[1:]) == -4
 
 
+@pytest.mark.fake_pointers
 def test_forward_hist_validation_before_launch():
     d = desc()
     p = L.deft_plan_create(d)
@@ -228,6 +258,7 @@ def test_forward_hist_validation_before_launch():
     assert lib.deft_forward_hist(None, *ok[1:]) == -4
 
 
+@pytest.mark.fake_pointers
 def test_unfused_forward_validation_before_launch():
     d = desc()
     p = L.deft_plan_create(d)
@@ -251,6 +282,7 @@ def test_unfused_forward_validation_before_launch():
     assert lib.deft_forward_unfused(e, None, None, None, None, None, None, None, None, 0, None) == 0
 
 
+@pytest.mark.fake_pointers
 def test_empty_batch_is_a_no_op():
     d = desc(n=0)
     p = L.deft_plan_create(d)
@@ -260,6 +292,7 @@ def test_empty_batch_is_a_no_op():
     assert lib.deft_debug_sample(p, None, None, None, None) == 0
 
 
+@pytest.mark.fake_pointers
 def test_backward_validation_before_launch():
     d = desc()
     p = L.deft_plan_create(d)
@@ -278,6 +311,7 @@ def test_backward_validation_before_launch():
     assert lib.deft_backward(*a) == -7
 
 
+@pytest.mark.fake_pointers
 def test_other_entry_points_validate():
     lib = L.load()
     d = desc()
@@ -290,6 +324,7 @@ def test_other_entry_points_validate():
     assert lib.deft_debug_sample(p, FAKE, FAKE, None, None) == -4
 
 
+@pytest.mark.fake_pointers
 def test_dwconv1d_validation_before_launch():
     lib = L.load()
     ok = [FAKE, FAKE, FAKE, 2, 16, 8, 3, 2, None]
@@ -312,6 +347,7 @@ def test_dwconv1d_validation_before_launch():
     assert call(3, 0) == 0 and call(4, 0) == 0  # empty: nothing launched
 
 
+@pytest.mark.fake_pointers
 def test_dwpw1d_validation_before_launch():
     lib = L.load()
     ok = [FAKE, FAKE, FAKE, FAKE, 2, 16, 64, 32, 3, 2, None]

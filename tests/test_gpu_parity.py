@@ -200,6 +200,7 @@ def test_fused_equals_unfused_and_plan_invariance(name):
     ("bf16_n16_c256_56x56", None),                 # direct gather, the headline forward
     ("bf16_n16_c512_28x28_g4_wide", None),         # 4 groups, wide offsets, pushed taps
     ("bf16_n16_c512_28x28_g4_wide", (8, 8, 2, 0)),  # LDS halo, several groups per workgroup
+    ("bf16_n16_c256_56x56", (7, 7, 2, -2)),        # gather fused into the GEMM: the offset-conv launch counts
     ("fp32_n8_c128_64x64", None),
     ("fp32_n8_c128_64x64", (3, 7, 1, 16)),         # ragged tiles
 ])
@@ -314,6 +315,8 @@ def test_edge_shapes_forward(case, dtype):
     # the unfused three-operator forward computes the same values in the same order
     assert torch.equal(off3, off)
     assert torch.equal(y3, y)
+    assert rel(host(off3), off_ref) <= 1e-5
+    assert rel(host(y3), y_ref) <= TOL[dtype]
 
 
 # --- backward -------------------------------------------------------------------------
@@ -508,9 +511,9 @@ def test_backward_after_unfused_forward(dtype):
 @pytest.mark.parametrize("name", ["train_bf16_n16_c256_56x56_s1", "train_bf16_n16_c256_56x56_s2"])
 def test_training_step_full_size(name):
     """Full-size forward + backward in the benchmark's launch configuration.
-    Per-image outputs (y, dx) are compared with the oracle on two sampled
-    images; the weight and bias gradients, which sum over all images, against
-    the sum of the oracle's per-image backward passes over all 16 images."""
+    dx is compared with the oracle's per-image backward on every image, y on
+    two sampled images; the weight and bias gradients, which sum over all
+    images, against the sum of the oracle's per-image backward passes."""
     wl = WORKLOADS[name]
     say("training step full size", name)
     inp, layer, y, off, g = run_backward(wl)
@@ -525,12 +528,45 @@ def test_training_step_full_size(name):
         say("  oracle image %d done" % n)
         for k in sums:
             sums[k] = ref[k] if sums[k] is None else sums[k] + ref[k]
+        e_dx = rel(host(g["dx"][sl]), ref["dx"])
+        say("  image %d: dx %.2e" % (n, e_dx))
+        assert e_dx <= tol, n
         if n in (0, wl.n - 1):
             y_ref, _ = oracle.forward(s1, inp["x"][sl], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
-            e_y, e_dx = rel(y_h[sl], y_ref), rel(host(g["dx"][sl]), ref["dx"])
-            say("  image %d: y %.2e dx %.2e" % (n, e_y, e_dx))
-            assert e_y <= tol and e_dx <= tol
+            e_y = rel(y_h[sl], y_ref)
+            say("  image %d: y %.2e" % (n, e_y))
+            assert e_y <= tol, n
     for k, v in sums.items():
         e = rel(host(g[k]), v)
         say("  %s rel %.2e" % (k, e))
         assert e <= tol, k
+
+
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+def test_nonfinite_dy_reaches_the_gradients(bad):
+    """A NaN (or +Inf) in dY: the fp32 backward, whose sampling part of dX is
+    summed in fixed point, marks every gradient element whose exact sum is
+    non-finite as the oracle does (NaN, or the infinity), and the finite
+    elements still agree with the oracle."""
+    wl = WORKLOADS["tiny_fp32_n1_c16_16x16"].scaled(train=True, n=2, c_in=32, c_out=24, h=12, w=13)
+    say("non-finite dY", bad)
+    inp = make_inputs(wl, with_dy=True)
+    inp["dy"][0, 3, 4, 5] = np.nan if bad == "nan" else np.inf
+    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
+    layer = make_layer(wl, training=True)
+    y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"])
+    g = layer.backward(t["x"], t["w_off"], t["w"], off, t["dy"])
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    for k in ("dx", "dw_off", "db_off", "dw", "db"):
+        a, b = host(g[k]).astype(np.float64), np.asarray(ref[k], np.float64)
+        say("  %s: %d NaN / %d inf (oracle %d / %d)" % (k, np.isnan(a).sum(), np.isinf(a).sum(), np.isnan(b).sum(),
+                                                         np.isinf(b).sum()))
+        assert np.isnan(b).any() or np.isinf(b).any(), k  # the case reaches every gradient
+        assert np.array_equal(np.isnan(a), np.isnan(b)), k
+        assert np.array_equal(np.isposinf(a), np.isposinf(b)), k
+        assert np.array_equal(np.isneginf(a), np.isneginf(b)), k
+        fin = np.isfinite(b)
+        if fin.any():
+            assert rel(a[fin], b[fin]) <= TOL["f32"], k
