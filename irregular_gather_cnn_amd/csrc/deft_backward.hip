@@ -8,10 +8,10 @@
 //                     group) the list of (output pixel, tap) pairs whose
 //                     corners touch the core within the halo; dY sums for db;
 //                     W2 / W_off^T layouts; zeroing.
-//   k_sample_bwd_mf -- bf16, per (core, group, 64-channel chunk): dX of the
-//                     core as MFMA products of sparse bilinear-weight tiles
-//                     with the listed entries' dCol rows, summed over the
-//                     waves in a fixed order and written once; the unique
+//   k_sample_bwd_mf -- bf16, per (core, group, 64- or 32-channel chunk): dX
+//                     of the core as MFMA products of sparse bilinear-weight
+//                     tiles with the listed entries' dCol rows, each wave
+//                     owning a 32 x 32 block of it, written once; the unique
 //                     owner of each pair reduces dOffset over the chunk's
 //                     channels into that chunk's partial.
 //   k_sample_bwd   -- the same without MFMA (fp32, small chunks): lanes =
@@ -51,7 +51,7 @@ struct BwdParams {
   const float* off;
   const void* dcol;
   const uint32_t* maxbits;  // max |dcol| as fp32 bits
-  float* dxs;    // [N][Cin][H][W] fp32: the sampling part of dX
+  float* dxs;    // [N][H][W][Cin] fp32 (channel-minor): the sampling part of dX
   float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials, zeroed beforehand
   int4* lists;   // [num_tg][list_cap]: one list per (core, group)
   int* counts;   // [num_tg]: entries in each list
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
     }
     __syncthreads();
     for (int k = tid; k < p.CC * chn * cwn; k += 256) {
-      const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
+      const int r = k / p.CC, cc = k - r * p.CC;
       const int y = r / cwn, xx = r - y * cwn;
       const int el = (y * p.CW + xx) * p.CC + cc;
       const acc_t a = dxl[el];
@@ -434,241 +434,291 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
       float v = (float)(sv * inv);
       const uint32_t f = (nflags[el >> 3] >> (4 * (el & 7))) & 15u;
       if (f) v = ((f & 1u) || (f & 6u) == 6u) ? __builtin_nanf("") : ((f & 2u) ? __builtin_inff() : -__builtin_inff());
-      p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = v;
+      p.dxs[((size_t)n * HW + (size_t)(Y0 + y) * p.W + X0 + xx) * p.Cin + cglob + cc] = v;
     }
   }
 }
 
-// bf16 sampling backward with the scatter on the MFMA units.  Per block of 32
-// list entries a wave forms, 16 entries at a time, the sparse matrix of
-// bilinear weights A [core pixel][entry] in LDS (each entry puts its weights
-// on at most four pixels; the fp32 weight split as bf16 hi + lo, two MFMAs,
-// so the weights keep 16 significant bits) and multiplies it with the
-// entries' dCol rows B [entry][channel] (read as fragments with transposed
-// LDS reads): dX_core += A B in fp32 registers.  The four waves take every
-// fourth block; their partial sums are added in a fixed order at the end.
-// No atomics; dOffset as in the other variant.  Needs a core of at most 64
-// pixels and a chunk of 32 or 64 channels.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sample_bwd_mf(const BwdParams p) {
+// One DPP row shift: lane i of each 16-lane row reads lane i - N of the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x110 + N, 0xf, 0xf, true));
+}
+
+// bf16 sampling backward with the scatter on the MFMA units.  The core's list
+// is walked in blocks of BLK entries (BLK = 2048 / CC: 32 entries for a
+// 64-channel chunk, 64 for a 32-channel one).  Lane (entry, piece) of a block
+// loads 16 bytes (8 channels) of the entry's dCol row, two blocks before it is
+// used (the list entries four blocks before), and with them
+//   - computes the entry's offset gradient over those 8 channels (the four
+//     corner dot products on the packed bf16 dot instruction, exact products
+//     summed in fp32), summed over the entry's lanes by row shifts; the unique
+//     owner of the pair stores it as this chunk's partial;
+//   - writes the piece to the block's staged dCol tile [entry][channel];
+//   - for pieces 0..3, writes the bilinear weight of corner q = piece to the
+//     block's weight tile A [core pixel][entry] (the fp32 weight split into
+//     bf16 hi + lo, two MFMAs, so the weights keep 16 significant bits), after
+//     clearing the weight it wrote into that tile two blocks before.
+// After one barrier, wave w multiplies the rows of A of its 32-pixel half with
+// the staged columns of its 32-channel half (a 32-channel chunk: the two wave
+// pairs take the two halves of the block's entries instead, added in a fixed
+// order at the end): dX[pixel][channel] += A B in fp32 registers.  The tiles
+// are double-buffered, so one barrier per block suffices.  Each wave owns its
+// output block and writes it once, from the registers, into the channel-minor
+// fp32 dX [N][H][W][Cin].
+//
+// A non-finite dCol value would reach every pixel of the core through the
+// zero weights (0 x NaN = NaN).  A lane whose partial offset gradient is not
+// finite (a non-finite dCol value always makes it so) records instead, for
+// each non-finite value and each corner of the entry inside the core, the
+// class of the product (NaN, +Inf or -Inf) in 4-bit LDS flags and stages a
+// zero in its place; the write-out adds the flagged value.
+template <int CC>
+__global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
+  constexpr int PPE = CC / 8;        // lanes (16-byte pieces) per list entry
+  constexpr int BLK = 256 / PPE;     // list entries per block
+  constexpr int KS = BLK / 16;       // MFMA k-steps per block
+  constexpr int KSPLIT = 64 / CC;    // wave pairs sharing an output block
+  constexpr int ROWB = BLK * 2;      // bytes per weight-tile row
+  constexpr int NCH = BLK / 8;       // 16-byte chunks per weight-tile row
+  constexpr int RP = 128 / BLK;      // weight-tile rows per 256 bytes (the swizzle period)
+  constexpr int TILE = 64 * ROWB;    // one weight tile (hi or lo)
+  constexpr int STG = BLK * CC * 2;  // one staged dCol tile
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lw = xcd_swizzle(blockIdx.x, p.num_wg);
-  const int nchunks = p.Cg / p.CC;
+  const int nchunks = p.Cg / CC;
   const int tg = lw / nchunks, chunk = lw - tg * nchunks;
   const int tile = tg / p.G, g = tg - tile * p.G;
   const int tpi = p.bt_h * p.bt_w;
   const int n = tile / tpi, trem = tile - n * tpi;
   const int Y0 = (trem / p.bt_w) * p.CH, X0 = (trem % p.bt_w) * p.CW;
   const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
-  const int obase = 2 * g * p.K2;
   const int HoWo = p.Ho * p.Wo;
-  bf16_t* xl = (bf16_t*)smem;  // [(CH+2)*(CW+2)][xstr]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
-  const int4* list = p.lists + (size_t)tg * p.list_cap;
-  const bf16_t* __restrict__ x = (const bf16_t*)p.x;
-  const bf16_t* __restrict__ dcol = (const bf16_t*)p.dcol;
-  const int L = p.counts[tg];
-
-  constexpr int BLK = 32, VEC = 8, KQ = BLK / VEC;
   const int XW = p.CW + 2;
   const int PX = p.CH * p.CW;
-  const bool mb1 = PX > 32, nb1 = p.CC > 32;
-  const size_t HW = (size_t)p.H * p.W;
-  bf16_t* dst = (bf16_t*)(smem + p.lds_dc) + (size_t)wave * BLK * p.dcstr;  // [BLK][dcstr]
-  unsigned char* at = smem + p.lds_dx + wave * 4096;  // A hi [64][16], then A lo [64][16] (32-byte rows)
-  const int lpe = p.CC / VEC;  // lanes per dCol row (16-byte pieces)
-  const int epi = 64 / lpe;    // rows per load instruction
-  const size_t pstride = (size_t)p.N * p.Oc * HoWo;
-  const FastDiv drh = make_fastdiv(p.CH + 2);
-  const StageGeom sg = stage_geom<bf16_t>(p.W, X0 - 1, XW, (size_t)p.Cin * HW);
-  const int c0 = chunk * p.CC;
-  const int cglob = g * p.Cg + c0;
-  float* doffp = p.doffp + (size_t)chunk * pstride + ((size_t)n * p.Oc + obase) * HoWo;
-  // The input region around the core is needed only by dOffset.  From the
-  // channel-minor copy (direct-gather forward) it is copied by buffer-to-LDS
-  // loads issued here and awaited just before the first dOffset, so the copy
-  // overlaps the first block's loads and MFMAs; otherwise it is staged now.
-  bool x_ready = true;
+  const int cglob = g * p.Cg + chunk * CC;
+  const int L = p.counts[tg];
+  const int nblk = (L + BLK - 1) / BLK;
+  const int4* __restrict__ list = p.lists + (size_t)tg * p.list_cap;
+  const bf16_t* __restrict__ dcol = (const bf16_t*)p.dcol + (size_t)n * HoWo * p.Ck + cglob;
+  float* doffp = p.doffp + (size_t)chunk * p.N * p.Oc * HoWo + ((size_t)n * p.Oc + 2 * g * p.K2) * HoWo;
+  bf16_t* xl = (bf16_t*)smem;                     // [(CH+2)*(CW+2)][CC]: rows Y0-1..Y0+CH, cols X0-1..X0+CW
+  unsigned char* wtile = smem + p.lds_dx;         // [2 buffers][hi, lo][64 pixels][BLK entries] bf16
+  unsigned char* stg = smem + p.lds_dc;           // [2 buffers][BLK entries][CC channels] bf16
+  uint32_t* nfl = (uint32_t*)(smem + p.lds_cnt);  // [64 pixels][CC] 4-bit flags, then an "any flag" word
+  constexpr int NFW = 64 * CC / 8;
+
+  const int e = tid / PPE, v = tid % PPE;  // this lane's entry in a block and 8-channel piece
+  // Every load and store of the block loop is issued by every lane: entries
+  // past the list read zeros through the buffer range checks, and stores of
+  // lanes with nothing to store go past their buffer's range, where they are
+  // dropped.  The loop then has no branches around memory operations, and
+  // the waits for the loads in flight stay exact.
+  const __amdgpu_buffer_rsrc_t lrs = make_brsrc(list, (uint32_t)L * 16u);
+  const __amdgpu_buffer_rsrc_t drs = make_brsrc(dcol, (uint32_t)((size_t)HoWo * p.Ck * 2));
+  const __amdgpu_buffer_rsrc_t ors = make_brsrc(doffp, (uint32_t)(2 * p.K2 * HoWo * 4));
+  auto load_entry = [&](int b) {
+    return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(lrs, (b * BLK + e) * 16, 0, 0));
+  };
+  // dCol row of (output pixel, tap): (pix*K2 + tap)*Cin within the image
+  auto load_piece = [&](int b, const int4 en) {
+    const int off = b * BLK + e < L ? ((en.x * p.K2 + (en.y & 255)) * p.Cin + v * 8) * 2 : kOOB;
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+  };
+
+  // the input region around the core (read by the offset gradient): from the
+  // channel-minor copy of x with buffer-to-LDS loads, else staged from x
   if (p.xh) {
     const int HWi = p.H * p.W;
     const rsrc_t xr = make_rsrc(p.xh + (size_t)n * (HWi + 1) * p.Cin, (uint32_t)((size_t)(HWi + 1) * p.Cin * 2));
-    const int pps = p.xstr >> 3;  // 16-byte slots per staged pixel (the last ones padding)
-    const int nslots = (p.CH + 2) * XW * pps;
+    const int nslots = (p.CH + 2) * XW * PPE;
     for (int s0 = wave * 64; s0 < nslots; s0 += 256) {
-      const int sl = s0 + lane, px = sl / pps, pc = sl - px * pps;
+      const int sl = s0 + lane, px = sl / PPE, pc = sl - px * PPE;
       const int ry = px / XW, rx = px - ry * XW;
       const int y = Y0 - 1 + ry, xx = X0 - 1 + rx;
       const int pix = ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) ? y * p.W + xx : HWi;
-      const int voff = pc * 8 < p.CC ? (pix * p.Cin + cglob + pc * 8) * 2 : kOOB;
-      if (sl < nslots) load_lds16(xr, (unsigned char*)xl + s0 * 16, voff);  // lanes past the region write nothing
+      if (sl < nslots) load_lds16(xr, (unsigned char*)xl + s0 * 16, (pix * p.Cin + cglob + pc * 8) * 2);
     }
-    x_ready = false;
   } else {
-    stage_region<bf16_t>(xl, x, p.Cin, p.H, p.W, n, cglob, p.CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg, p.xstr);
-    __syncthreads();
+    const size_t HW = (size_t)p.H * p.W;
+    const FastDiv drh = make_fastdiv(p.CH + 2);
+    const StageGeom sg = stage_geom<bf16_t>(p.W, X0 - 1, XW, (size_t)p.Cin * HW);
+    stage_region<bf16_t>(xl, (const bf16_t*)p.x, p.Cin, p.H, p.W, n, cglob, CC, Y0 - 1, X0 - 1, p.CH + 2, XW, drh, sg,
+                         CC);
   }
+  // ring slots: list entries of blocks b..b+3, dCol pieces of blocks b, b+1
+  int4 e0 = load_entry(0), e1 = load_entry(1), e2 = load_entry(2), e3 = load_entry(3);
+  uint4 d0 = load_piece(0, e0), d1 = load_piece(1, e1);
+  for (int i = tid; i < 4 * TILE / 16; i += 256) ((uint4*)wtile)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i <= NFW; i += 256) nfl[i] = 0u;
+  // vmcnt(0) as the builtin, so that the compiler's own waits in the loop
+  // below know that nothing from here is still in flight
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
 
-  f32x16_t acc[2][2];
+  const int ph = wave & 1;                      // pixel half of the MFMA output block
+  const int chh = KSPLIT == 1 ? wave >> 1 : 0;  // channel half
+  const int kh = KSPLIT == 2 ? wave >> 1 : 0;   // half of the block's entries (32-channel chunks)
+  const int arow = ph * 32 + (lane & 31);
+  const int gq = lane >> 4, j16 = lane & 15;
+  const int bcol = chh * 32 + 16 * (gq & 1) + 4 * (j16 & 3);
+  // this lane's staged piece: 64-channel rows have their pieces swizzled by
+  // bit 1 of the row, so the transposed reads of four rows hit distinct banks
+  const int swz = CC == 64 ? (e & 2) : 0;
+  const int soff = e * (CC * 2) + ((v ^ swz) << 4);
+  f32x16_t acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  int w0 = -1, w1 = -1;  // the weight this lane last wrote into each weight buffer
 
-  // list entries are fetched one block ahead of the dCol rows they address
-  int4 my = make_int4(0, 0, 0, 0), mynext = make_int4(0, 0, 0, 0);
-  uint4 q[KQ];
-  auto load_list = [&](int b0) {
-    if (b0 < L) mynext = lane < min(BLK, L - b0) ? list[b0 + lane] : make_int4(0, 0, 0, 0);
-  };
-  auto load_block = [&](int b0) {
-    const int nb = min(BLK, L - b0);
-    my = mynext;
-    load_list(b0 + 4 * BLK);
-#pragma unroll
-    for (int k = 0; k < KQ; ++k) {
-      const int r = k * epi + lane / lpe, v = lane % lpe;
-      const int pix = __shfl(my.x, r & 63), t = __shfl(my.y, r & 63) & 255;
-      q[k] = make_uint4(0, 0, 0, 0);
-      if (k * epi < BLK && r < nb)
-        q[k] = *(const uint4*)(dcol + ((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cglob + v * VEC);
+  // One block: en, dq hold its list entry and dCol piece and are refilled
+  // with those of blocks b + 4 and b + 2 (whose list entry is en2).
+  auto step = [&](const int b, int4& en, uint4& dq, const int4& en2, int& wold, const int buf) {
+    const bool valid = b * BLK + e < L;
+    const uint32_t info = (uint32_t)en.y;
+    const float ly = __int_as_float(en.z), lx = __int_as_float(en.w);
+    const float hy = 1.0f - ly, hx = 1.0f - lx;
+    const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+
+    // offset gradient over this lane's channels
+    const bf16_t* c00 = xl + (cy * XW + cx) * CC + v * 8;
+    const uint4 x00 = *(const uint4*)c00, x01 = *(const uint4*)(c00 + CC);
+    const uint4 x10 = *(const uint4*)(c00 + XW * CC), x11 = *(const uint4*)(c00 + (XW + 1) * CC);
+    const float d00 = dot2_bf16(dq, x00, 0.f), d01 = dot2_bf16(dq, x01, 0.f);
+    const float d10 = dot2_bf16(dq, x10, 0.f), d11 = dot2_bf16(dq, x11, 0.f);
+    float gy = hx * (d10 - d00) + lx * (d11 - d01);
+    float gx = hy * (d01 - d00) + ly * (d11 - d10);
+    const bool bad = valid & !(fabsf(gy) + fabsf(gx) <= 3.402823466e38f);
+    gy += row_shr<1>(gy);
+    gx += row_shr<1>(gx);
+    gy += row_shr<2>(gy);
+    gx += row_shr<2>(gx);
+    if (PPE == 8) {
+      gy += row_shr<4>(gy);
+      gx += row_shr<4>(gx);
     }
-  };
-  int eb = wave * BLK;
-  load_list(eb);
-  if (eb < L) load_block(eb);
-  for (; eb < L; eb += 4 * BLK) {
-    const int nb = min(BLK, L - eb);
-    // rows past the block's entries are written too (as zeros): the MFMA
-    // reads all 32 rows, and stale LDS must not meet a zero weight as NaN
-#pragma unroll
-    for (int k = 0; k < KQ; ++k) {
-      const int r = k * epi + lane / lpe, v = lane % lpe;
-      if (k * epi < BLK && r < BLK) *(uint4*)(dst + r * p.dcstr + v * VEC) = q[k];
+    {
+      const bool own = valid & (v == PPE - 1) & (((info >> 8) & 1u) != 0u);
+      const int o = own ? ((2 * (int)(info & 255u)) * HoWo + en.x) * 4 : kOOB;
+      // (the builtin stores 32-bit integers: pass the bits)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gy), ors, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gx), ors, own ? o + HoWo * 4 : kOOB, 0, 0);
     }
-    const int4 cur = my;
-    // the rows are read by other lanes below: a wave's LDS operations execute
-    // in issue order, so only the compiler has to be kept from reordering
-    asm volatile("" ::: "memory");
-    if (eb + 4 * BLK < L) load_block(eb + 4 * BLK);
-    const int nbs = __builtin_amdgcn_readfirstlane(nb);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks * 16 >= nbs) break;
-      // the weight matrix of entries ks*16 .. ks*16+15: zero, then each
-      // (entry, corner) lane writes its weight at (corner pixel, entry)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *(uint4*)(at + (i * 64 + lane) * 16) = make_uint4(0, 0, 0, 0);
-      {
-        const int j = lane & 15, qc = lane >> 4, e = ks * 16 + j;
-        const uint32_t info = (uint32_t)__shfl(cur.y, e);
-        const float ly = __int_as_float(__shfl(cur.z, e)), lx = __int_as_float(__shfl(cur.w, e));
-        if (e < nbs && ((info >> (9 + qc)) & 1u)) {
-          const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
-          const float wy = (qc >> 1) ? ly : 1.0f - ly, wx = (qc & 1) ? lx : 1.0f - lx;
-          const float w = wy * wx;
-          const bf16_t hi = f32_to_bf16(w);
-          const bf16_t lo = f32_to_bf16(w - bf16_to_f32(hi));
-          const int P = (cy - 1 + (qc >> 1)) * p.CW + (cx - 1 + (qc & 1));
-          const int a = P * 32 + (((j >> 3) ^ ((P >> 2) & 1)) << 4) + (j & 7) * 2;
-          *(bf16_t*)(at + a) = hi;
-          *(bf16_t*)(at + 2048 + a) = lo;
+
+    // non-finite dCol values: flag the products, stage zeros
+    uint4 dqs = dq;
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+      if (bad) {
+        const uint32_t cm = (info >> 9) & 15u;
+        uint4 keep = make_uint4(~0u, ~0u, ~0u, ~0u);
+#pragma unroll 1
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t wv = k < 4 ? (k < 2 ? dq.x : dq.y) : (k < 6 ? dq.z : dq.w);
+          const float gv = bf16_to_f32((wv >> (16 * (k & 1))) & 0xffffu);
+          if (fabsf(gv) <= 3.402823466e38f) continue;
+#pragma unroll 1
+          for (int qq = 0; qq < 4; ++qq) {
+            if (!((cm >> qq) & 1u)) continue;
+            const int P = (cy - 1 + (qq >> 1)) * p.CW + (cx - 1 + (qq & 1));
+            const float wgt = ((qq >> 1) ? ly : hy) * ((qq & 1) ? lx : hx);
+            const uint32_t code = (gv != gv || wgt == 0.f) ? 1u : (gv > 0.f ? 2u : 4u);
+            atomicOr(&nfl[P * (CC / 8) + v], code << (4 * k));
+          }
+          const uint32_t m = ~(0xffffu << (16 * (k & 1)));
+          if (k < 2) keep.x &= m; else if (k < 4) keep.y &= m; else if (k < 6) keep.z &= m; else keep.w &= m;
         }
-      }
-      asm volatile("" ::: "memory");
-      uint4 ahi[2], alo[2], bq[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = mb * 32 + (lane & 31);
-        const int a = row * 32 + (((lane >> 5) ^ ((row >> 2) & 1)) << 4);
-        ahi[mb] = *(const uint4*)(at + a);
-        alo[mb] = *(const uint4*)(at + 2048 + a);
-      }
-      bq[1] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int nb_ = 0; nb_ < 2; ++nb_) {
-        if (nb_ == 1 && !nb1) break;  // columns past a 32-channel chunk are not read
-        const int gq = lane >> 4, j = lane & 15;
-        const int col = nb_ * 32 + 16 * (gq & 1) + 4 * (j & 3);
-        uint2 h[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int krow = ks * 16 + 8 * (gq >> 1) + 4 * t + (j >> 2);
-          h[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                               (__attribute__((address_space(3))) bf16x4_t*)(
-                                                   (unsigned char*)dst + krow * p.dcstr * 2 + col * 2)));
-        }
-        bq[nb_] = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if (mb == 1 && !mb1) break;
-#pragma unroll
-        for (int nb_ = 0; nb_ < 2; ++nb_) {
-          if (nb_ == 1 && !nb1) break;
-          mfma_chunk(acc[mb][nb_], ahi[mb], bq[nb_], bf16_t());
-          mfma_chunk(acc[mb][nb_], alo[mb], bq[nb_], bf16_t());
-        }
+        dqs = make_uint4(dq.x & keep.x, dq.y & keep.y, dq.z & keep.z, dq.w & keep.w);
+        nfl[NFW] = 1u;
       }
     }
-    if (!x_ready) {  // every wave passes this barrier once (below if it has no block)
-      wait_vm<0>();
-      __syncthreads();
-      x_ready = true;
+
+    // this block's tiles: the weight of corner q = v (after clearing the one
+    // this lane wrote into the same buffer two blocks before), the dCol piece
+    unsigned char* wb = wtile + buf * 2 * TILE;
+    unsigned char* sb = stg + buf * STG;
+    if (v < 4) {
+      if (wold >= 0) {
+        *(bf16_t*)(wb + wold) = 0;
+        *(bf16_t*)(wb + TILE + wold) = 0;
+      }
+      wold = -1;
+      if (valid & (((info >> (9 + v)) & 1u) != 0u)) {
+        const unsigned P = (unsigned)((cy - 1 + (v >> 1)) * p.CW + (cx - 1 + (v & 1)));
+        const float w = ((v >> 1) ? ly : hy) * ((v & 1) ? lx : hx);
+        const bf16_t hi = f32_to_bf16(w);
+        const bf16_t lo = f32_to_bf16(w - bf16_to_f32(hi));
+        wold = (int)(P * ROWB + ((((unsigned)e >> 3) ^ ((P / RP) % NCH)) << 4) + (e & 7) * 2);
+        *(bf16_t*)(wb + wold) = hi;
+        *(bf16_t*)(wb + TILE + wold) = lo;
+      }
     }
-    doffset_owned<bf16_t>(cur, nb, lane, dst, p.dcstr, xl, p.xstr, XW, p.CC, HoWo, doffp);
-    __builtin_amdgcn_wave_barrier();
-  }
-  if (!x_ready) {
-    wait_vm<0>();
+    *(uint4*)(sb + soff) = dqs;
+    // refill the slots (their values are no longer read)
+    dq = load_piece(b + 2, en2);
+    en = load_entry(b + 4);
     __syncthreads();
-  }
-  // the four waves' partial sums, added in a fixed order: waves 0 and 1
-  // store theirs ([channel][pixel], two regions), waves 2 and 3 add them to
-  // their own and store back, and the write-out adds the two regions:
-  // (acc0 + acc2) + (acc1 + acc3)
-  __syncthreads();
-  constexpr int RS = 65;
-  const int rsz = p.CC * RS;
-  float* R = (float*)(smem + p.lds_dx);  // [2][CC][RS] over the weight tiles and dCol rows
-  float* Rw = R + (wave & 1) * rsz;
-  // (every one of the 64 pixel slots of a channel row is written; slots past
-  // the core's pixels are never read)
-  if (wave < 2) {
+
 #pragma unroll
-    for (int nb_ = 0; nb_ < 2; ++nb_) {
-      if (nb_ == 1 && !nb1) break;
+    for (int ks = kh * (KS / KSPLIT); ks < (kh + 1) * (KS / KSPLIT); ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+      const int aoff = arow * ROWB + ((c ^ ((arow / RP) % NCH)) << 4);
+      const uint4 ahi = *(const uint4*)(wb + aoff), alo = *(const uint4*)(wb + TILE + aoff);
+      uint2 h[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)] = acc[mb][nb_][r];
+      for (int t = 0; t < 2; ++t) {
+        const int krow = ks * 16 + 8 * (gq >> 1) + 4 * t + (j16 >> 2);
+        const int phys = (bcol >> 3) ^ (CC == 64 ? (krow & 2) : 0);
+        h[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                             (__attribute__((address_space(3))) bf16x4_t*)(
+                                                 sb + krow * (CC * 2) + (phys << 4) + (bcol & 7) * 2)));
+      }
+      const uint4 bq = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+      mfma_chunk(acc, ahi, bq, bf16_t());
+      mfma_chunk(acc, alo, bq, bf16_t());
     }
+  };
+  int b = 0;
+  for (; b + 4 <= nblk; b += 4) {
+    step(b, e0, d0, e2, w0, 0);
+    step(b + 1, e1, d1, e3, w1, 1);
+    step(b + 2, e2, d0, e0, w0, 0);
+    step(b + 3, e3, d1, e1, w1, 1);
   }
-  __syncthreads();
-  if (wave >= 2) {
+  if (b < nblk) step(b, e0, d0, e2, w0, 0);
+  if (b + 1 < nblk) step(b + 1, e1, d1, e3, w1, 1);
+  if (b + 2 < nblk) step(b + 2, e2, d0, e0, w0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // the refills past the list
+
+  if (KSPLIT == 2) {  // the two halves of the entries, added in a fixed order
+    __syncthreads();  // every wave is done with the weight tiles
+    float* red = (float*)wtile;  // [pixel half][16][64]
+    if (kh == 1) {
 #pragma unroll
-    for (int nb_ = 0; nb_ < 2; ++nb_) {
-      if (nb_ == 1 && !nb1) break;
-      float v[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[mb][r] = Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          Rw[(nb_ * 32 + (lane & 31)) * RS + mb * 32 + acc_row(lane, r)] = v[mb][r] + acc[mb][nb_][r];
+      for (int r = 0; r < 16; ++r) red[(ph * 16 + r) * 64 + lane] = acc[r];
     }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += red[(ph * 16 + r) * 64 + lane];
   }
-  __syncthreads();
-  for (int k = tid; k < p.CC * chn * cwn; k += 256) {
-    const int cc = k / (chn * cwn), r = k - cc * (chn * cwn);
-    const int y = r / cwn, xx = r - y * cwn;
-    const int ri = cc * RS + y * p.CW + xx;
-    p.dxs[((size_t)n * p.Cin + cglob + cc) * HW + (size_t)(Y0 + y) * p.W + X0 + xx] = R[ri] + R[rsz + ri];
+  if (ph * 32 >= PX) return;
+  const bool anyflag = nfl[NFW] != 0u;
+  const int cc = chh * 32 + (lane & 31);
+  const float rcw = 1.0f / (float)p.CW;
+  float* dxo = p.dxs + ((size_t)n * p.H * p.W) * p.Cin + cglob + cc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int P = ph * 32 + acc_row(lane, r);
+    const int y = (int)(((float)P + 0.5f) * rcw), x = P - y * p.CW;
+    if (P >= PX || y >= chn || x >= cwn) continue;
+    float val = acc[r];
+    if (anyflag) {
+      const uint32_t f = (nfl[P * (CC / 8) + (cc >> 3)] >> (4 * (cc & 7))) & 15u;
+      if (f) val += ((f & 1u) || (f & 6u) == 6u) ? __builtin_nanf("") : ((f & 2u) ? __builtin_inff() : -__builtin_inff());
+    }
+    dxo[((size_t)(Y0 + y) * p.W + X0 + x) * p.Cin] = val;
   }
 }
 
@@ -719,15 +769,15 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
         const int cg = g * p.Cg + c;
         const float gcv = Elem<T>::to_f32(dcol[((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cg]);
         const T* pl = x + ((size_t)n * p.Cin + cg) * HW;
-        float* dl = p.dxs + ((size_t)n * p.Cin + cg) * HW;
+        float* dl = p.dxs + (size_t)n * HW * p.Cin + cg;  // channel-minor: pixel stride Cin
         const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
         const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
         const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
         const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
-        if (r0 && q0) atomicAdd(dl + (size_t)y0 * p.W + x0, w[0] * gcv);
-        if (r0 && q1) atomicAdd(dl + (size_t)y0 * p.W + x0 + 1, w[1] * gcv);
-        if (r1 && q0) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0, w[2] * gcv);
-        if (r1 && q1) atomicAdd(dl + (size_t)(y0 + 1) * p.W + x0 + 1, w[3] * gcv);
+        if (r0 && q0) atomicAdd(dl + ((size_t)y0 * p.W + x0) * p.Cin, w[0] * gcv);
+        if (r0 && q1) atomicAdd(dl + ((size_t)y0 * p.W + x0 + 1) * p.Cin, w[1] * gcv);
+        if (r1 && q0) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0) * p.Cin, w[2] * gcv);
+        if (r1 && q1) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0 + 1) * p.Cin, w[3] * gcv);
         gy += gcv * ((1.0f - ix.lx) * (v10 - v00) + ix.lx * (v11 - v01));
         gx += gcv * ((1.0f - ix.ly) * (v01 - v00) + ix.ly * (v11 - v10));
       }
@@ -997,17 +1047,19 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
 
 // ---------------------------------------------------------------------------
 // Final dX: dx[n][c][y][x] = dtype(dX_offset + the sampling part of dX).
-// dX_offset is a GEMM with rows c (one 32-channel block per wave), columns =
-// 64 input pixels, depth kk = o*K2 + tap (padded to KKP, in chunks of KKC);
-// its B tile [pixel][kk] (dOffset at the output pixel whose tap lands on the
-// input pixel, or 0) is built in LDS.
+// dX_offset is a GEMM with rows = 64 input pixels, columns c (one 32-channel
+// block per wave), depth kk = o*K2 + tap (padded to KKP, in chunks of KKC);
+// its pixel operand [pixel][kk] (dOffset at the output pixel whose tap lands
+// on the input pixel, or 0) is built in LDS.  With pixels as rows, a lane's
+// accumulators hold one channel, and the lanes of a row 32 consecutive
+// channels: the channel-minor sampling part is read in 128-byte runs.
 struct DxParams {
   int N, Cin, H, W, Ho, Wo, KH, KW, SH, SW, PH, PW, DH, DW, K2, Oc, KKP, KKC;
   int pix_blocks, cblocks, num_wg;
   FastDiv div_w, div_sh, div_sw;
   const void* wofft;  // [Cin][KKP]
   const float* doff;
-  const float* dxs;   // sampling part of dX, fp32
+  const float* dxs;   // sampling part of dX, fp32, channel-minor [N][H][W][Cin]
   void* dx;
 };
 
@@ -1034,24 +1086,17 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
   const int crow = c0 + (lane & 31);
-  // The sampling part of dX for the outputs this lane writes at the end (8
-  // consecutive pixels of one channel per piece, 4 pieces), loaded up front
-  // so the loads overlap the dOffset tile and the MFMAs.  Whole pieces need
-  // HW % 8 == 0 (then a piece never straddles a channel plane).
-  const bool vec8 = (HW & 7) == 0;
-  float4 sv[4][2];
-  if (vec8) {
+  // The sampling part of dX at this lane's accumulator elements (channel
+  // crow; pixels pix0 + j*32 + acc_row(lane, r)), loaded up front so the
+  // loads overlap the dOffset tile and the MFMAs, and added after them.
+  float sv[2][16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int cl = k * 8 + (lane >> 3), q = pix0 + (lane & 7) * 8, cc = c0 + cl;
-      sv[k][0] = sv[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (active && q < HW && cc < p.Cin) {
-        const float* src = p.dxs + ((size_t)n * p.Cin + cc) * HW + q;
-        sv[k][0] = *(const float4*)src;
-        sv[k][1] = *(const float4*)(src + 4);
-      }
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = pix0 + j * 32 + acc_row(lane, r);
+      sv[j][r] = active && crow < p.Cin && q < HW ? p.dxs[((size_t)n * HW + q) * p.Cin + crow] : 0.f;
     }
-  }
   int4* kinfo = (int4*)(smem + ((64 * bstr * (int)sizeof(T) + 15) & ~15));  // [KKC]
   for (int kb = 0; kb < p.KKP; kb += p.KKC) {
     const int len = min(p.KKC, p.KKP - kb);
@@ -1108,23 +1153,31 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint4 b = *(const uint4*)(bt + (j * 32 + (lane & 31)) * bstr + kl);
-          mfma_chunk(acc[j], a, b, T());
+          mfma_chunk(acc[j], b, a, T());  // rows = pixels, columns = channels
         }
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] += sv[j][r];
   T* dx = (T*)p.dx;
-  if (vec8) {
+  // whole 8-pixel pieces need HW % 8 == 0 (a piece never straddles a plane)
+  if ((HW & 7) == 0) {
     // through LDS: each wave's 32 channels x 64 pixels (fp32, rows padded
     // to 68 floats), then per lane 8 consecutive pixels of one channel: one
-    // 32-byte read, the sampling part added, one 16-byte (bf16) store
+    // 32-byte read, one 16-byte (bf16) store
     __syncthreads();  // the B tile is no longer read
     float* ep = (float*)smem + wave * 32 * 68;
     if (active) {
+      // four consecutive pixels of the lane's channel per 16-byte write
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) ep[acc_row(lane, r2) * 68 + j * 32 + (lane & 31)] = acc[j][r2];
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(float4*)(ep + (lane & 31) * 68 + j * 32 + acc_row(lane, 4 * r4)) =
+              make_float4(acc[j][4 * r4], acc[j][4 * r4 + 1], acc[j][4 * r4 + 2], acc[j][4 * r4 + 3]);
     }
     // a wave reads back only its own block: its LDS operations execute in
     // issue order, so only the compiler has to be kept from reordering
@@ -1135,26 +1188,20 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
       const int cl = k * 8 + (lane >> 3), ql = (lane & 7) * 8, q = pix0 + ql, cc = c0 + cl;
       if (q >= HW || cc >= p.Cin) continue;
       const float4 a0 = *(const float4*)(ep + cl * 68 + ql), a1 = *(const float4*)(ep + cl * 68 + ql + 4);
-      float f[8] = {a0.x + sv[k][0].x, a0.y + sv[k][0].y, a0.z + sv[k][0].z, a0.w + sv[k][0].w,
-                    a1.x + sv[k][1].x, a1.y + sv[k][1].y, a1.z + sv[k][1].z, a1.w + sv[k][1].w};
+      float f[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       store8(dx + ((size_t)n * p.Cin + cc) * HW + q, f);
     }
     return;
   }
   if (!active) return;
+  if (crow >= p.Cin) return;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = pix0 + j * 32 + (lane & 31);
-    if (q >= HW) continue;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r2 = 0; r2 < 16; ++r2) {
-      const int cc = c0 + acc_row(lane, r2);
-      if (cc < p.Cin) {
-        const size_t idx = ((size_t)n * p.Cin + cc) * HW + q;
-        dx[idx] = Elem<T>::from_f32(acc[j][r2] + p.dxs[idx]);
-      }
+      const int q = pix0 + j * 32 + acc_row(lane, r2);
+      if (q < HW) dx[((size_t)n * p.Cin + crow) * HW + q] = Elem<T>::from_f32(acc[j][r2]);
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1316,7 +1363,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   int cb = 0;
   while ((1 << cb) < p.list_cap + 1) ++cb;
   b.capbits = cb;
-  b.xstr = p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
+  b.xstr = p.bwd_mf ? p.chunk_b : p.chunk_b + (d.dtype == DEFT_BF16 ? 8 : 4);
   b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
   b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
   b.lists = lists;
@@ -1342,7 +1389,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
 
   // sampling backward, the taps beyond the halo, then dOffset
   {
-    auto kern = p.bwd_mf ? k_sample_bwd_mf : k_sample_bwd<T>;
+    auto kern = !p.bwd_mf ? k_sample_bwd<T> : p.chunk_b == 64 ? k_sample_bwd_mf<64> : k_sample_bwd_mf<32>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
     if (e != hipSuccess) return e;
     if (b.num_wg) DEFT_LAUNCH("sample_backward", kern, dim3(b.num_wg), dim3(256), p.lb_total, st, b);

@@ -104,10 +104,11 @@ Shape shape_of(const deft_desc& d) {
 }
 
 // Backward tiling: the sampling backward gives each workgroup a core tile of
-// input pixels; it gathers the (output pixel, tap) pairs whose corners touch
-// the core (within the halo) into a list, then per channel chunk scatters
-// dCol x weight into an fp32 LDS copy of the core (lanes = channels) and
-// writes the core's dX once.  A pair straddling two cores is read by both, so
+// input pixels; the (output pixel, tap) pairs whose corners touch the core
+// (within the halo) are gathered into a list, then per channel chunk dCol x
+// weight is summed into the core (bf16: as MFMA products of weight tiles with
+// the staged dCol rows; fp32: in a fixed-point LDS copy of the core, lanes =
+// channels) and the core's dX is written once.  A pair straddling two cores is read by both, so
 // larger cores read dCol fewer times; the LDS holds the core plus a one-pixel
 // ring of the input (for the offset gradient) and the fp32 core.
 bool layout_backward(deft_plan& p) {
@@ -120,22 +121,28 @@ bool layout_backward(deft_plan& p) {
   while (cb > 16 && s.cg % cb) cb /= 2;
   if (s.cg % cb) return false;
   const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
-  const int xstr = cb + vec;
-  const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
   // bf16 with a core of at most 64 pixels and 32 or 64 channels: the scatter
-  // runs on the MFMA units (per wave two 2 KB weight tiles; dCol rows padded
-  // to 16 extra channels so transposed reads of four rows hit distinct banks)
-  const bool mf = d.dtype == DEFT_BF16 && ch * cw <= 64 && cb % 32 == 0;
-  int ldx, ldc;
+  // runs on the MFMA units (its buffer offsets into one image's dCol rows
+  // are 32-bit)
+  const bool mf = d.dtype == DEFT_BF16 && ch * cw <= 64 && cb % 32 == 0 &&
+                  (size_t)s.ho * s.wo * s.ck * 2 < ((size_t)1 << 31);
+  const int xstr = mf ? cb : cb + vec;  // staged input pixel stride (elements)
+  const int lx = align16((ch + 2) * (cw + 2) * xstr * s.esz);
+  int ldx, ldc, lfl = 0;
   if (mf) {
-    ldx = 4 * 4096;
-    ldc = 4 * 32 * (cb + 16) * 2;  // with the tiles, also holds the final 2 x [channel][65] fp32 sums
+    // blocks of blk = 2048 / cb list entries: two buffers of bf16 weight
+    // tiles (hi and lo, [64 pixels][blk]), two staged dCol tiles [blk][cb],
+    // 4-bit non-finite flags per (pixel, channel) and one word
+    const int blk = 2048 / cb;
+    ldx = 2 * 2 * 64 * blk * 2;
+    ldc = 2 * blk * cb * 2;
+    lfl = 64 * cb / 2 + 16;
   } else {
     // fixed-point dX of the core, spill slots, non-finite flags (4 bits per element)
     ldx = align16((ch * cw * cb + 64) * (d.dtype == DEFT_BF16 ? 4 : 8) + (ch * cw * cb + 7) / 8 * 4);
     ldc = 4 * 32 * (cb + vec) * s.esz;  // 4 waves x 32 rows
   }
-  const int total = lx + ldx + ldc + 16 + 4 * 49 * 4 + 48 * 8;  // + list counter and per-tap tables
+  const int total = lx + ldx + ldc + lfl;
   if (total > p.max_lds) return false;
   p.btile_h = ch; p.btile_w = cw;
   p.btiles_h = (d.h + ch - 1) / ch; p.btiles_w = (d.w + cw - 1) / cw;
