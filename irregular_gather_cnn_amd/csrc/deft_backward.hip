@@ -6,8 +6,8 @@
 // run on the MFMA GEMMs (deft_gemm.hip, deft_gemm_dl.hip); this file holds
 //   k_prep_backward -- one launch: per (core tile of input pixels, offset
 //                     group) the list of (output pixel, tap) pairs whose
-//                     corners touch the core within the halo; dY sums for db;
-//                     W2 / W_off^T layouts; zeroing.
+//                     corners touch the core within the halo, in candidate
+//                     order; dY sums for db; W2 / W_off^T layouts; zeroing.
 //   k_sample_bwd_mf -- bf16, per (core, group, 64- or 32-channel chunk): dX
 //                     of the core as MFMA products of sparse bilinear-weight
 //                     tiles with the listed entries' dCol rows, each wave
@@ -143,11 +143,24 @@ __device__ __forceinline__ void doffset_owned(const int4 cur, int nb, int lane, 
 
 // The (output pixel, tap) pairs whose corners touch one core tile of input
 // pixels (for one offset group), written to that core's list; shared by the
-// core's channel-chunk workgroups of the sampling backward.  Runs inside the
-// backward's preparation launch (its first num_tg workgroups).
-__device__ __forceinline__ void sample_bwd_list(const BwdParams& p, int bid) {
-  __shared__ int tabs[4 + 48 * 3 + 49 + 96];
-  const int tid = threadIdx.x;
+// core's channel-chunk workgroups of the sampling backward.  One 256-thread
+// workgroup per (core, group), the first num_tg workgroups of the
+// backward's preparation launch: the candidates (for every tap, the output
+// pixels whose tap grid point lies within halo+1 above/left and halo
+// below/right of the core, where a corner can touch it) are evaluated four
+// per thread per round, all loads of a round in flight together.  The kept
+// pairs are compacted in candidate order (ballots and one prefix over the
+// workgroup's waves per round), so a list, and everything summed in its
+// order, is the same on every run.
+__device__ __forceinline__ void bwd_lists_body(const BwdParams& p, int bid) {
+  constexpr int NW = 4;  // waves
+  constexpr int NT = 64 * NW;
+  constexpr int U = 8;   // candidates per thread per round
+  __shared__ int rlo_h[48], rlo_w[48], rnw[48], rsz[48], rmax;
+  __shared__ uint32_t rdiv[96];
+  __shared__ int wcnt[2][U * NW];  // per round parity: kept pairs per (step u, wave)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tg = xcd_swizzle(bid, p.num_tg);
   const int tile = tg / p.G, g = tg - tile * p.G;
   const int tpi = p.bt_h * p.bt_w;
@@ -156,20 +169,12 @@ __device__ __forceinline__ void sample_bwd_list(const BwdParams& p, int bid) {
   const int chn = min(p.CH, p.H - Y0), cwn = min(p.CW, p.W - X0);
   const int obase = 2 * g * p.K2;
   const int HoWo = p.Ho * p.Wo;
-  int* cnt = tabs;
   int4* list = p.lists + (size_t)tg * p.list_cap;
   const float* __restrict__ offn = p.off + ((size_t)n * p.Oc + obase) * HoWo;
 
-  // ---- the pairs touching this core ----
-  // Candidates: for every tap, the output pixels whose tap grid point lies
-  // within halo+1 above/left and halo below/right of the core (where a corner
-  // can touch it).  The per-tap rectangles are flattened into one index space
-  // and evaluated four per thread per step, loads first.
-  int* rlo_h = cnt + 4;          // per tap: first output row / column of the
-  int* rlo_w = rlo_h + 48;        // candidate rectangle, its width (as a
-  int* rnw = rlo_w + 48;          // divisor), and the prefix sum of the
-  int* rstart = rnw + 48;         // rectangle sizes
-  uint32_t* rdiv = (uint32_t*)(rstart + 49);  // [48][2] FastDiv of the widths
+  // per tap: first output row / column of the candidate rectangle, its
+  // width (as a divisor) and size; candidates are numbered t*R + k with R
+  // the largest rectangle, so a candidate's tap is one division away
   if (tid < p.K2) {
     const int t = tid;
     const int ti = t / p.KW, tj = t - ti * p.KW;
@@ -181,29 +186,30 @@ __device__ __forceinline__ void sample_bwd_list(const BwdParams& p, int bid) {
     rlo_h[t] = ho_lo; rlo_w[t] = wo_lo; rnw[t] = nw > 0 ? nw : 1;
     const FastDiv fd = make_fastdiv(nw > 0 ? nw : 1);
     rdiv[2 * t] = fd.m; rdiv[2 * t + 1] = fd.s;
-    rstart[t + 1] = nh * nw;
+    rsz[t] = nh * nw;
   }
-  if (tid == 0) *cnt = 0;
   __syncthreads();
   if (tid == 0) {
-    rstart[0] = 0;
-    for (int t = 0; t < p.K2; ++t) rstart[t + 1] += rstart[t];
+    int m = 1;
+    for (int t = 0; t < p.K2; ++t) m = max(m, rsz[t]);
+    rmax = m;
   }
   __syncthreads();
-  const int ncand = rstart[p.K2];
-  for (int e0 = tid; e0 < ncand; e0 += 4 * 256) {
-    float dyv[4], dxv[4];
-    int tt[4], pp[4], hh[4], ww[4];
+  const int R = rmax;
+  const FastDiv dR = make_fastdiv(R);
+  const int ncand = p.K2 * R;
+  int running = 0;  // pairs kept in earlier rounds
+  for (int e0 = 0, round = 0; e0 < ncand; e0 += U * NT, ++round) {
+    float dyv[U], dxv[U];
+    int tt[U], pp[U], hh[U], ww[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + u * 256;
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * NT + tid;
       tt[u] = -1;
       dyv[u] = dxv[u] = 0.f;
       pp[u] = hh[u] = ww[u] = 0;
-      if (e < ncand) {
-        int t = 0;
-        while (e >= rstart[t + 1]) ++t;
-        const int k = e - rstart[t];
+      const int t = fdiv(e, dR), k = e - t * R;
+      if (e < ncand && k < rsz[t]) {
         const FastDiv fd{rdiv[2 * t], rdiv[2 * t + 1]};
         const int kr = fdiv(k, fd);
         const int ho = rlo_h[t] + kr, wo = rlo_w[t] + (k - kr * rnw[t]);
@@ -214,34 +220,59 @@ __device__ __forceinline__ void sample_bwd_list(const BwdParams& p, int bid) {
         dxv[u] = offn[(size_t)(2 * t + 1) * HoWo + pp[u]];
       }
     }
+    int4 ent[U];
+    unsigned long long keep[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int t = tt[u];
-      if (t < 0) continue;
-      const int ti = t / p.KW, tj = t - ti * p.KW;
-      const int ho = hh[u], wo = ww[u];
-      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
-      const TapIndex ix = tap_index(by, bx, dyv[u], dxv[u], p.H, p.W);
-      if (ix.outside) continue;
-      if (max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo) continue;
-      uint32_t cm = 0;
+      bool k = false;
+      ent[u] = make_int4(0, 0, 0, 0);
+      if (t >= 0) {
+        const int ti = t / p.KW, tj = t - ti * p.KW;
+        const int by = hh[u] * p.SH - p.PH + ti * p.DH, bx = ww[u] * p.SW - p.PW + tj * p.DW;
+        const TapIndex ix = tap_index(by, bx, dyv[u], dxv[u], p.H, p.W);
+        if (!ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) <= p.halo) {
+          uint32_t cm = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cy = ix.y0 + (q >> 1), cx = ix.x0 + (q & 1);
-        if (cy >= Y0 && cy < Y0 + chn && cx >= X0 && cx < X0 + cwn) cm |= 1u << q;
+          for (int q = 0; q < 4; ++q) {
+            const int cy = ix.y0 + (q >> 1), cx = ix.x0 + (q & 1);
+            if (cy >= Y0 && cy < Y0 + chn && cx >= X0 && cx < X0 + cwn) cm |= 1u << q;
+          }
+          if (cm) {
+            const int oy = max(ix.y0, 0), ox = max(ix.x0, 0);
+            const uint32_t owned = (oy >= Y0 && oy < Y0 + chn && ox >= X0 && ox < X0 + cwn) ? 1u : 0u;
+            ent[u] = make_int4(pp[u], (int)((uint32_t)t | (owned << 8) | (cm << 9) |
+                                            ((uint32_t)(ix.y0 - Y0 + 1) << 16) | ((uint32_t)(ix.x0 - X0 + 1) << 24)),
+                               __float_as_int(ix.ly), __float_as_int(ix.lx));
+            k = true;
+          }
+        }
       }
-      if (!cm) continue;
-      const int oy = max(ix.y0, 0), ox = max(ix.x0, 0);
-      const uint32_t owned = (oy >= Y0 && oy < Y0 + chn && ox >= X0 && ox < X0 + cwn) ? 1u : 0u;
-      const int slot = atomicAdd(cnt, 1);
-      list[slot] = make_int4(pp[u], (int)((uint32_t)t | (owned << 8) | (cm << 9) | ((uint32_t)(ix.y0 - Y0 + 1) << 16) |
-                                          ((uint32_t)(ix.x0 - X0 + 1) << 24)),
-                             __float_as_int(ix.ly), __float_as_int(ix.lx));
+      keep[u] = __builtin_amdgcn_ballot_w64(k);
     }
+    // slots in candidate order: step u, then wave, then lane
+    int* wc = wcnt[round & 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (lane == 0) wc[u * NW + wave] = __builtin_popcountll(keep[u]);
+    __syncthreads();
+    // lanes of every wave: inclusive prefix over the U x NW counts
+    int c = lane < U * NW ? wc[lane] : 0;
+#pragma unroll
+    for (int s = 1; s < U * NW; s <<= 1) {
+      const int o = __shfl_up(c, s);
+      if (lane >= s) c += o;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = u * NW + wave;
+      const int base = running + __shfl(c, idx) - wc[idx];
+      if ((keep[u] >> lane) & 1ull) list[base + __builtin_popcountll(keep[u] & below)] = ent[u];
+    }
+    running += __shfl(c, U * NW - 1);
   }
-  __syncthreads();
-  __syncthreads();
-  if (tid == 0) p.counts[tg] = *cnt;
+  if (tid == 0) p.counts[tg] = running;
 }
 
 // Corner q of a tap: (y0 + (q >> 1), x0 + (q & 1)), the order of tap_weights.
@@ -1234,51 +1265,57 @@ __device__ __forceinline__ void prep_backward_body(int bid, int nblocks, const T
   }
 }
 
-// Per-(channel, image) sums: part[ch][n] = sum over pixels of dY (ch < Cout)
-// or of dOffset (ch >= Cout).  Fixed-order tree reduction.
-// Sum of dY over the pixels of one (output channel, image): bias partial
-// part[ch * N + n] (16-byte loads for bf16 when the plane allows).
+// Sum of dY over the pixels of one (output channel, image) plane, by one
+// wave: the bias partial part[ch * N + n].  bf16 planes whose length allows
+// it are read as 16-byte pieces, four per lane in flight; the lanes' sums are
+// then added in a fixed order.
 template <typename T>
 __device__ __forceinline__ void bias_dy_body(const T* __restrict__ dy, float* part, int Cout, int N, int HoWo, int ch,
                                              int n) {
-  __shared__ float red[256];
+  const int lane = threadIdx.x & 63;
   const size_t base = ((size_t)n * Cout + ch) * HoWo;
   float s = 0.f;
   if (sizeof(T) == 2 && (HoWo & 7) == 0) {
-    for (int q = threadIdx.x * 8; q < HoWo; q += 256 * 8) {
-      float f[8];
-      unpack8(*(const uint4*)((const bf16_t*)dy + base + q), f);
-      s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+    const uint4* src = (const uint4*)((const bf16_t*)dy + base);
+    const int nv = HoWo >> 3;
+    for (int q0 = lane; q0 < nv; q0 += 4 * 64) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = q0 + u * 64 < nv ? src[q0 + u * 64] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float f[8];
+        unpack8(v[u], f);
+        s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+      }
     }
   } else {
-    for (int q = threadIdx.x; q < HoWo; q += 256) s += Elem<T>::to_f32(dy[base + q]);
+    for (int q = lane; q < HoWo; q += 64) s += Elem<T>::to_f32(dy[base + q]);
   }
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) part[(size_t)ch * N + n] = red[0];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) part[(size_t)ch * N + n] = s;
 }
 
 // The backward's preparation in one launch: workgroups [0, num_tg) build the
-// candidate lists, the next Cout*N sum dY per (channel, image), the rest lay
-// out W2 and W_off^T and zero the dOffset partials and the max word.
+// candidate lists, the next ceil(Cout*N / 4) sum dY per (channel, image)
+// plane, one wave per plane, the rest lay out W2 and W_off^T and zero the
+// dOffset partials and the max word.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_backward(const BwdParams b, const T* __restrict__ w,
                                                        const T* __restrict__ w_off, T* w2, T* wofft, float* z0,
                                                        size_t nz0, int Cout, int Cin, int K2, int Oc, int KKP,
                                                        const T* __restrict__ dy, float* bpart, int N, int HoWo) {
-  const int bid = blockIdx.x;
+  const int bid = (int)blockIdx.x;
+  const int nbias = (Cout * N + 3) / 4;
   if (bid < b.num_tg) {
-    sample_bwd_list(b, bid);
-  } else if (bid < b.num_tg + Cout * N) {
-    const int r = bid - b.num_tg;
-    bias_dy_body<T>(dy, bpart, Cout, N, HoWo, r % Cout, r / Cout);
+    bwd_lists_body(b, bid);
+  } else if (bid < b.num_tg + nbias) {
+    const int r = (bid - b.num_tg) * 4 + (int)(threadIdx.x >> 6);
+    if (r < Cout * N) bias_dy_body<T>(dy, bpart, Cout, N, HoWo, r % Cout, r / Cout);
   } else {
-    const int base = b.num_tg + Cout * N;
-    prep_backward_body<T>(bid - base, gridDim.x - base, w, w_off, w2, wofft, z0, nz0, Cout, Cin, K2, Oc, KKP);
+    const int base = b.num_tg + nbias;
+    prep_backward_body<T>(bid - base, (int)gridDim.x - base, w, w_off, w2, wofft, z0, nz0, Cout, Cin, K2, Oc, KKP);
   }
 }
 
@@ -1375,7 +1412,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     // partials (fully outside taps keep 0) and the max |dCol| word after them
     const size_t nz = ndoff * (size_t)(p.cg / p.chunk_b) + 4;
     const size_t total = (size_t)d.c_out * p.ck + (size_t)d.c_in * p.kk_pad + nz / 4 + 4;
-    const unsigned grid = (unsigned)b.num_tg + (unsigned)(d.c_out * d.n) + grid_cap(total, 8192);
+    const unsigned grid = (unsigned)b.num_tg + (unsigned)((d.c_out * d.n + 3) / 4) + grid_cap(total, 8192);
     DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid), dim3(256), 0, st, b, (const T*)a.w,
                 (const T*)a.w_off, w2, wofft, doffp, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad, (const T*)a.dy,
                 bpart, d.n, p.ho * p.wo);
