@@ -47,7 +47,7 @@ KERNELS = {
     "gemm_dw": (r"k_gemm_(dl|ws)<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "sample_backward": (r"k_sample_bwd<|k_sample_bwd_mf\b", ["deft_backward.hip", "deft_device.h"]),
     "sample_backward_miss": (r"k_sample_bwd_miss<", ["deft_backward.hip", "deft_device.h"]),
-    "sample_backward_list": (r"k_sample_bwd_list\b", ["deft_backward.hip", "deft_device.h"]),
+
     "offset_weight_backward": (r"k_woff_bwd<", ["deft_backward.hip", "deft_device.h"]),
     "dx_final": (r"k_dx_final<", ["deft_backward.hip", "deft_device.h"]),
     "doff_sum": (r"k_doff_sum\b", ["deft_backward.hip"]),
