@@ -906,9 +906,12 @@ struct WoffParams {
 
 // dW_off partial of one (image, 32-channel slice, band of output rows): a
 // GEMM with rows = offset channels, columns = (tap, channel), depth = the
-// band's output pixels.  The band's input rows ([ch][row][XS], column XL is
-// x = 0) and its dOffset rows ([o][row][DLS], bf16) are staged once; the
-// taps then read their shifted windows from LDS.
+// band's output pixels.  The band's input rows are staged once (bf16:
+// [row][pixel][32 channels]; fp32: [ch][row][XS], column XL is x = 0) and
+// the taps read their shifted windows from LDS.  bf16 reads the dOffset
+// operand straight from global memory as MFMA fragments (8 pixels of one
+// offset channel per lane, rounded to bf16), one k-chunk ahead, in two fixed
+// register slots; fp32 stages the dOffset rows too ([o][row][DLS]).
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
@@ -967,7 +970,9 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
       xs[e] = v;
     }
   }
-  if (sizeof(T) == 2 && (p.Wo & 3) == 0 && (HoWo & 3) == 0 && (p.DLS & 3) == 0) {
+  if constexpr (kHwc) {
+    // the dOffset operand is read in the tap loop below
+  } else if (sizeof(T) == 2 && (p.Wo & 3) == 0 && (HoWo & 3) == 0 && (p.DLS & 3) == 0) {
     // four pixels per piece (one 16-byte load, one 8-byte store), eight
     // pieces per thread per pass; padding rows and columns are zero
     const int pr = p.DLS >> 2, rowp = p.band_rows * pr;
@@ -1012,6 +1017,120 @@ __global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
   }
   if (kHwc && p.xh) wait_vm<0>();
   __syncthreads();
+  if constexpr (kHwc) {
+    // ---- taps in groups of 12 (three per wave) ----
+    const int g4 = lane >> 4, j4 = lane & 15;
+    // this lane's transposed-read position inside a tap's window
+    const int lofs = 16 * (g4 & 1) + 4 * (j4 & 3) + (8 * (g4 >> 1) + (j4 >> 2)) * p.SW * 32;
+    const int nkc = p.WoP / KC, niter = nrows * nkc;
+    const FastDiv dk = make_fastdiv(nkc);
+    const bool vec4 = (p.Wo & 3) == 0;
+    // dOffset planes of this image through a buffer: loads of lanes with
+    // nothing to load go past its range and read zero, so every step issues
+    // the same loads and the waits for them stay exact
+    const __amdgpu_buffer_rsrc_t drs = make_brsrc(doff, (uint32_t)((size_t)p.Oc * HoWo * 4));
+    int orow[MB];  // byte offset of this lane's offset channel (o0 + mb*32 + lane%32) at the band's first row
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int o = mb * 32 + cl;
+      orow[mb] = o < p.orows ? ((p.o0 + o) * HoWo + ho0 * p.Wo) * 4 : -1;
+    }
+    // operand of k-chunk `it` (row it / nkc, pixels kc + 8*half .. +7)
+    auto load_a = [&](int it, uint4* a) {
+      const int ry = fdiv(it, dk), kc = (it - ry * nkc) * KC;
+      const int w0 = kc + half * VEC;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bool ok = orow[mb] >= 0 && it < niter;
+        const int b0 = orow[mb] + (ry * p.Wo + w0) * 4;
+        float f[8];
+        if (vec4) {
+          const uint4 u0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         drs, ok && w0 < p.Wo ? b0 : kOOB, 0, 0));
+          const uint4 u1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         drs, ok && w0 + 4 < p.Wo ? b0 + 16 : kOOB, 0, 0));
+          f[0] = __uint_as_float(u0.x); f[1] = __uint_as_float(u0.y);
+          f[2] = __uint_as_float(u0.z); f[3] = __uint_as_float(u0.w);
+          f[4] = __uint_as_float(u1.x); f[5] = __uint_as_float(u1.y);
+          f[6] = __uint_as_float(u1.z); f[7] = __uint_as_float(u1.w);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            f[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, ok && w0 + i < p.Wo ? b0 + 4 * i : kOOB,
+                                                                        0, 0));
+        }
+        a[mb] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                           pack_bf16x2(f[6], f[7]));
+      }
+    };
+    for (int tg = 0; tg < p.K2; tg += 12) {
+      f32x16_t acc[MB][3];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[mb][j][q] = 0.f;
+      const T* tb[3];
+      int ntap = 0;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int t = tg + wave + 4 * j;
+        tb[j] = xs;
+        if (t < p.K2) {
+          const int ti = t / p.KW, tj = t - ti * p.KW;
+          tb[j] = xs + ((size_t)ti * p.DH * p.XS + tj * p.DW) * 32 + lofs;
+          ntap = j + 1;
+        }
+      }
+      auto step = [&](int it, const uint4* a) {
+        const int ry = fdiv(it, dk), kc = (it - ry * nkc) * KC;
+        const int ofs = (ry * p.SH * p.XS + kc * p.SW) * 32;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          if (j >= ntap) break;
+          uint2 hh[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            hh[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                  (__attribute__((address_space(3))) bf16x4_t*)(
+                                                      (const bf16_t*)tb[j] + ofs + h * 4 * p.SW * 32)));
+          const uint4 b = make_uint4(hh[0].x, hh[0].y, hh[1].x, hh[1].y);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) mfma_chunk(acc[mb][j], a[mb], b, T());
+        }
+      };
+      // four fixed slots, each operand loaded three k-chunks before its use
+      uint4 a0[MB], a1[MB], a2[MB], a3[MB];
+      load_a(0, a0);
+      load_a(1, a1);
+      load_a(2, a2);
+      for (int it = 0; it < niter; it += 4) {
+        load_a(it + 3, a3);
+        step(it, a0);
+        load_a(it + 4, a0);
+        if (it + 1 < niter) step(it + 1, a1);
+        load_a(it + 5, a1);
+        if (it + 2 < niter) step(it + 2, a2);
+        load_a(it + 6, a2);
+        if (it + 3 < niter) step(it + 3, a3);
+      }
+      float* part = p.part + (size_t)(n * p.bands + band) * p.Oc * p.K2 * p.Cin;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int t = tg + wave + 4 * j;
+        if (t >= p.K2) break;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int o = mb * 32 + acc_row(lane, q);
+            if (o < p.orows && c < p.Cin) part[((size_t)(p.o0 + o) * p.K2 + t) * p.Cin + c] = acc[mb][j][q];
+          }
+      }
+    }
+    return;
+  }
   // ---- taps in groups of 12 (three per wave) ----
   for (int tg = 0; tg < p.K2; tg += 12) {
     f32x16_t acc[MB][3];
@@ -1469,7 +1588,8 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
       w.o0 = o0;
       w.orows = p.oc - o0 < 96 ? p.oc - o0 : 96;
       const int mb = (w.orows + 31) / 32;
-      const int lds = ((32 * w.XR * w.XS * (int)sizeof(T) + 15) & ~15) + mb * 32 * w.band_rows * w.DLS * (int)sizeof(T);
+      const int lds = ((32 * w.XR * w.XS * (int)sizeof(T) + 15) & ~15) +
+                      (sizeof(T) == 2 ? 0 : mb * 32 * w.band_rows * w.DLS * (int)sizeof(T));
       if (mb == 1) {
         e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e == hipSuccess)

@@ -166,7 +166,8 @@ bool layout_backward(deft_plan& p) {
   const int mbw = std::min(3, (s.oc + 31) / 32);
   auto woff_lds = [&](int rows) {
     const int xr = (rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1;
-    return align16(32 * xr * xs * s.esz) + mbw * 32 * rows * (wop + vec) * s.esz;
+    // bf16 reads its dOffset operand from global memory; fp32 stages it too
+    return align16(32 * xr * xs * s.esz) + (d.dtype == DEFT_BF16 ? 0 : mbw * 32 * rows * (wop + vec) * s.esz);
   };
   int bands = 1;
   while (bands < s.ho) {
