@@ -860,6 +860,192 @@ struct DlDcol {
   __device__ void store_acc(const TileCoord&, int, int, const f32x16_t&, int) const {}
 };
 
+// ---- dCol with the weight block resident in LDS ----
+// dcol[q][e] = sum_co W2[e][co] dY[img(q)][co][p(q)] for K = Cout = 256.  The
+// 256 x 256 block of W2 that a workgroup's rows need (128 KB) is loaded once
+// and stays in LDS; only dY streams, through a 4-stage ring that runs on
+// across the workgroup's pixel tiles, so a CU receives its W2 block once
+// instead of once per output tile.  A workgroup owns one 256-row block of e
+// and a contiguous range of 128-pixel tiles; the 9 workgroups that share a
+// pixel range (and so its dY) are consecutive after the XCD swizzle.  Eight
+// waves, 4 (e) x 2 (pixels), each 64 x 64 of the tile.
+//
+// Between tiles the ring doubles as the epilogue's transpose buffer (4 KB a
+// wave): each wave leaves its block as 32-pixel passes of whole 128-byte
+// rows, eight rows per store instruction.  So that the ring is free then,
+// the next tile's first three dY stages are loaded into registers during the
+// last three stages of the current one and written into the ring after the
+// epilogue.  Every wave issues the same loads and stores in every tile
+// (out-of-range ones carry an offset past the buffer), and vector-memory
+// operations retire in issue order here, so the wait counts are constants.
+struct DcolRes {
+  static constexpr int BM = 256, BN = 128, K = 256, BK = 32, SL = K / BK;  // SL stages (W2 slices) per tile
+  static constexpr int RING = 4, kSlice = BM * BK * 2, kStage = BK * BN * 2;
+  static constexpr int kLds = SL * kSlice + RING * kStage;  // 128 KB + 32 KB
+  const bf16_t* w2;  // [M][K]
+  const bf16_t* dy;  // [img][K][HoWo]
+  bf16_t* dcol;      // [N][M]
+  int M, N, HoWo, nrb, groups, tilesN;
+  FastDiv div_howo;
+};
+static_assert(DcolRes::kLds <= 160 * 1024, "LDS");
+static_assert(DcolRes::SL == 8 && DcolRes::RING == 4, "the stage schedule below assumes 8 stages and 4 slots");
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dcol_res(const DcolRes p) {
+  using C = DcolRes;
+  constexpr int K = C::K, BK = C::BK, SL = C::SL;
+  typedef unsigned v4u32_t __attribute__((ext_vector_type(4)));
+  constexpr int kNt = 2;  // non-temporal stores: the sampling backward reads dCol next, from HBM
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* wblk = smem;                   // [SL][BM rows][BK] row form, rows of 64 bytes
+  unsigned char* ring = smem + SL * C::kSlice;  // [RING][BK k rows][BN] k-major
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int lb = xcd_swizzle(blockIdx.x, p.nrb * p.groups);
+  const int grp = lb / p.nrb, rb = lb - grp * p.nrb;
+  const int t0 = (int)((long long)p.tilesN * grp / p.groups), t1 = (int)((long long)p.tilesN * (grp + 1) / p.groups);
+  const int e0 = rb * C::BM;
+  if (t1 <= t0) return;  // (uniform)
+  const rsrc_t rw = make_rsrc(p.w2, rsrc_bytes((size_t)p.M * K * 2));
+  const rsrc_t rd = make_rsrc(p.dy, rsrc_bytes((size_t)p.N * K * 2));
+  const __amdgpu_buffer_rsrc_t rdb = make_brsrc(p.dy, rsrc_bytes((size_t)p.N * K * 2));
+  const __amdgpu_buffer_rsrc_t rc = make_brsrc(p.dcol, (uint32_t)((size_t)p.N * p.M * 2));
+
+  // W2 slice s (k in [32 s, 32 s + 32)): 16 loads of 1 KB, two per wave; load
+  // b covers rows 16 b .. 16 b + 15, lane -> row 16 b + lane / 4, slot chunk
+  // lane % 4 holding logical chunk (lane % 4) ^ swz(row)
+  int wofs[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = wave * 2 + i, row = 16 * b + lane / 4;
+    wofs[i] = ((e0 + row) * K + 8 * ((lane % 4) ^ swz_row<BK>(row))) * 2;
+  }
+  const uint32_t wlds = lds_addr_of(wblk) + wave * 2 * 1024;
+  auto issue_w = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) load_lds16_so(rw, wlds + s * C::kSlice + i * 1024, wofs[i], s * BK * 2);
+  };
+  // dY stage (32 k rows x 128 pixels): the 1 KB share of `wave` holds k rows
+  // 4 wave .. 4 wave + 3, lane -> k row 4 wave + lane / 16, slot chunk lane %
+  // 16 holding the 8 pixels of logical chunk (lane % 16) ^ swz_kmaj(k row)
+  const int krow = 4 * wave + lane / 16;
+  const int dchunk = (lane % 16) ^ swz_kmaj(krow);
+  const uint32_t dlds = lds_addr_of(ring) + wave * 1024;
+  int dbase = kOOB;  // byte offset of (k row krow, the lane's 8 pixels) of the tile being loaded
+  auto set_tile = [&](int t) {
+    const int q = t * C::BN + 8 * dchunk;
+    if (t < t1 && q < p.N) {
+      const int img = fdiv(q, p.div_howo), pp = q - img * p.HoWo;
+      dbase = ((img * K + krow) * p.HoWo + pp) * 2;
+    } else {
+      dbase = kOOB;
+    }
+  };
+  auto issue_d = [&](int s) {  // stage s of the tile being loaded, into slot s % 4
+    load_lds16_so(rd, dlds + (s % C::RING) * C::kStage, dbase, s * BK * p.HoWo * 2);
+  };
+
+  // prologue: W0 D0 W1 D1 W2 D2 W3..W7 (the first tile waits slice by slice)
+  set_tile(t0);
+  issue_w(0);
+  issue_d(0);
+  issue_w(1);
+  issue_d(1);
+  issue_w(2);
+  issue_d(2);
+#pragma unroll
+  for (int s = 3; s < SL; ++s) issue_w(s);
+
+  f32x16_t acc[2][2];
+  uint4 rnext[3];  // stages 0..2 of the next tile, loaded during stages 5..7
+  unsigned char* epi = ring + wave * 4096;  // this wave's transpose buffer: 32 pixels x 128 bytes
+  const int ntile = t1 - t0;
+  for (int t = 0; t < ntile; ++t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      // Operations issued after stage s's dY load.  First tile: W slices and
+      // dY stages as in the prologue, then the two younger loads.  Later
+      // tiles: stages 0..2 came through registers (no wait); from stage 3 on
+      // the two younger loads.
+      if (s == 0) { if (t == 0) wait_vm<16>(); }
+      else if (s == 1) { if (t == 0) wait_vm<14>(); }
+      else if (s == 2) { if (t == 0) wait_vm<12>(); }
+      else wait_vm<2>();
+      __syncthreads();  // stage s visible to all; the slot read in stage s - 1 is free
+      if (s + 3 < SL) {
+        issue_d(s + 3);
+      } else {
+        if (s + 3 == SL) set_tile(t0 + t + 1);
+        const int u = s + 3 - SL;
+        rnext[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rdb, dbase, u * BK * p.HoWo * 2, 0));
+      }
+      const unsigned char* a = wblk + s * C::kSlice;
+      const unsigned char* b = ring + (s % C::RING) * C::kStage;
+      uint4 fa[2][2], fb[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[ks][i] = fragment<false, C::BM, BK>(a, wm * 64 + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[ks][j] = fragment<true, C::BN, BK>(b, wn * 64 + j * 32, ks, lane);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[ks][i]),
+                                                                __builtin_bit_cast(bf16x8_t, fb[ks][j]), acc[i][j], 0, 0,
+                                                                0);
+    }
+    // Epilogue of tile t.  A lane of a 32 x 32 block holds 4 consecutive e of
+    // one pixel per register group; trading lanes 32..63 of one group with
+    // lanes 0..31 of the next gives each lane 8 consecutive e (16 bytes).
+    // Chunks are XOR-swizzled by (row / 2) % 8 so the writes of 16 rows hit
+    // distinct banks.
+    __syncthreads();  // every wave is done with the ring
+    const int n0 = (t0 + t) * C::BN + wn * 64, half = lane >> 5, row = lane & 31;
+    const int ew = e0 + wm * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // register groups 2h (rows +0..3) and 2h + 1 (rows +8..11)
+          const f32x16_t& v = acc[i][j];
+          const uint32_t ylo = pack_bf16x2(v[8 * h + 0], v[8 * h + 1]), yhi = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
+          const uint32_t xlo = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]), xhi = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
+          const auto sl = __builtin_amdgcn_permlane32_swap(ylo, xlo, false, false);
+          const auto sh = __builtin_amdgcn_permlane32_swap(yhi, xhi, false, false);
+          const int c = 4 * i + 2 * h + half;  // 16-byte chunk of the 128-byte row
+          *(uint4*)(epi + row * 128 + ((c ^ ((row >> 1) & 7)) << 4)) = make_uint4(sl[0], sh[0], sl[1], sh[1]);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qr = 8 * u + lane / 8, c = lane % 8;
+        const uint4 w = *(const uint4*)(epi + qr * 128 + ((c ^ ((qr >> 1) & 7)) << 4));
+        const int q = n0 + 32 * j + qr;
+        const v4u32_t val = {w.x, w.y, w.z, w.w};
+        __builtin_amdgcn_raw_buffer_store_b128(val, rc, q < p.N ? (q * p.M + ew + 8 * c) * 2 : kOOB, 0, kNt);
+      }
+    }
+    __syncthreads();  // the transpose buffers are read
+    if (t + 1 < ntile) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) *(uint4*)(ring + u * C::kStage + wave * 1024 + lane * 16) = rnext[u];
+    }
+  }
+  wait_vm<0>();  // the out-of-range tail loads have landed before the workgroup ends
+}
+
 // ---- dW partial of split z: part[z][co][e] = sum_{q in split} dY[img(q)][co][p(q)] cols[q][e] ----
 template <class CfgT>
 struct DlDwT {
@@ -1001,6 +1187,19 @@ hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols,
 
 hipError_t dl_gemm_dcol(const deft_plan& p, const void* w2, const void* dy, void* dcol, uint32_t* maxbits,
                         hipStream_t st) {
+  const int M = p.ck, N = p.d.n * p.ho * p.wo;
+  if (!maxbits && p.d.c_out == DcolRes::K && M % DcolRes::BM == 0) {
+    DcolRes op;
+    op.w2 = (const bf16_t*)w2; op.dy = (const bf16_t*)dy; op.dcol = (bf16_t*)dcol;
+    op.M = M; op.N = N; op.HoWo = p.ho * p.wo; op.div_howo = make_fastdiv(op.HoWo);
+    op.nrb = M / DcolRes::BM; op.tilesN = tiles(N, DcolRes::BN);
+    op.groups = std::max(1, std::min(op.tilesN, p.cus / op.nrb));
+    constexpr int lds = DcolRes::kLds;
+    hipError_t e = hipFuncSetAttribute((const void*)k_dcol_res, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    DEFT_LAUNCH("gemm_dcol", k_dcol_res, dim3(op.nrb * op.groups), dim3(512), lds, st, op);
+    return hipGetLastError();
+  }
   DlDcol op;
   op.w2 = (const bf16_t*)w2; op.dy = (const bf16_t*)dy; op.dcol = (bf16_t*)dcol; op.maxbits = maxbits;
   op.M = p.ck; op.N = p.d.n * p.ho * p.wo; op.K = p.d.c_out; op.HoWo = p.ho * p.wo;
