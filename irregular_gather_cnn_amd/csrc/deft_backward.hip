@@ -52,7 +52,8 @@ struct BwdParams {
   const void* dcol;
   const uint32_t* maxbits;  // max |dcol| as fp32 bits
   float* dxs;    // [N][H][W][Cin] fp32 (channel-minor): the sampling part of dX
-  float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials, zeroed beforehand
+  float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials: the pairs a core owns are written
+                 // by the sampling backward, the others (fully outside, beyond the halo) by k_sample_bwd_miss
   int4* lists;   // [num_tg][list_cap]: one list per (core, group)
   int* counts;   // [num_tg]: entries in each list
   int num_tg;    // cores x groups
@@ -780,6 +781,16 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
       const TapIndex ix = tap_index(by, bx, offp[pix], offp[HoWo + pix], p.H, p.W);
       miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
+      // No core owns this pair: its chunk partials are written here, zero for
+      // a fully outside tap and for every chunk but the first of a miss.
+      if (ix.outside || miss) {
+        const size_t cstride = (size_t)p.N * p.Oc * HoWo;
+        float* dz = p.doffp + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
+        for (int c = miss ? 1 : 0; c < p.Cg / p.CC; ++c) {
+          dz[c * cstride] = 0.f;
+          dz[c * cstride + HoWo] = 0.f;
+        }
+      }
     }
     unsigned long long mask = __ballot(miss);
     while (mask) {
@@ -789,7 +800,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
       const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
       const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
       const size_t oidx = ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
-      float* dd = p.doffp + oidx;  // chunk-0 partial; the other chunks' stay 0 for a miss
+      float* dd = p.doffp + oidx;  // chunk-0 partial (the other chunks' were zeroed above)
       const TapIndex ix = tap_index(by, bx, p.off[oidx], p.off[oidx + HoWo], p.H, p.W);
       float w[4];
       tap_weights(ix, w);
@@ -1527,13 +1538,13 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.num_tg = p.num_btiles * d.offset_groups;
   b.counts = (int*)(ws + p.ws_lcount);
   {
-    // candidate lists, dY bias sums, W2 / W_off^T, and zero: the dOffset
-    // partials (fully outside taps keep 0) and the max |dCol| word after them
-    const size_t nz = ndoff * (size_t)(p.cg / p.chunk_b) + 4;
+    // candidate lists, dY bias sums, W2 / W_off^T, and zero the max |dCol|
+    // word (the dOffset partials are all written by the two sampling kernels)
+    const size_t nz = 4;
     const size_t total = (size_t)d.c_out * p.ck + (size_t)d.c_in * p.kk_pad + nz / 4 + 4;
-    const unsigned grid = (unsigned)b.num_tg + (unsigned)((d.c_out * d.n + 3) / 4) + grid_cap(total, 8192);
+    const unsigned grid = (unsigned)b.num_tg + (unsigned)((d.c_out * d.n + 3) / 4) + grid_cap(total, 512);
     DEFT_LAUNCH("prep_backward", k_prep_backward<T>, dim3(grid), dim3(256), 0, st, b, (const T*)a.w,
-                (const T*)a.w_off, w2, wofft, doffp, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad, (const T*)a.dy,
+                (const T*)a.w_off, w2, wofft, (float*)maxbits, nz, d.c_out, d.c_in, p.taps, p.oc, p.kk_pad, (const T*)a.dy,
                 bpart, d.n, p.ho * p.wo);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
