@@ -60,6 +60,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
     ap.add_argument("--no-dwconv", action="store_true", help="skip the dilated depthwise conv timings")
     ap.add_argument("--no-other", action="store_true", help="skip the forward at the other configurations")
+    ap.add_argument("--no-libgemm", action="store_true",
+                    help="skip timing the library GEMM (torch.matmul) on the three GEMM shapes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) after the timed steps, as the "
                          "reference kernel for scaling hardware byte counters")
@@ -178,6 +180,42 @@ def main():
         return {"copy_gbs": round(copy, 1), "fill_gbs": round(fill, 1), "bytes": nb}
     hbm_meas = hbm_rates()
     log("measured HBM: %s" % hbm_meas)
+
+    # Context for the three GEMMs: the vendor library (torch.matmul, i.e.
+    # hipBLASLt) on the same bf16 shapes with contiguous row-major operands:
+    # y = cols @ W^T, dCol = dY @ W, dW = dY^T @ cols (median of 10 calls).
+    libgemm = None
+    if not args.no_libgemm and wl.dtype == "bf16":
+        P_, K_, O_ = wl.n * info["ho"] * info["wo"], wl.c_in * wl.kh * wl.kw, wl.c_out
+        g = torch.Generator(device=dev).manual_seed(0)
+        colsm = torch.randn(P_, K_, device=dev, generator=g).bfloat16()
+        wtm = torch.randn(K_, O_, device=dev, generator=g).bfloat16()
+        wm = wtm.t().contiguous()
+        dym = torch.randn(P_, O_, device=dev, generator=g).bfloat16()
+        dytm = dym.t().contiguous()
+        ym = torch.empty(P_, O_, device=dev, dtype=torch.bfloat16)
+        dcm = torch.empty(P_, K_, device=dev, dtype=torch.bfloat16)
+        dwm = torch.empty(O_, K_, device=dev, dtype=torch.bfloat16)
+
+        def lib_time(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(10):
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                fn()
+                b_.record()
+                torch.cuda.synchronize()
+                ts.append(a_.elapsed_time(b_) * 1000)
+            return round(sorted(ts)[5], 1)
+        libgemm = {"forward_us": lib_time(lambda: torch.matmul(colsm, wtm, out=ym)),
+                   "dcol_us": lib_time(lambda: torch.matmul(dym, wm, out=dcm)),
+                   "dw_us": lib_time(lambda: torch.matmul(dytm, colsm, out=dwm)),
+                   "operands": "contiguous row-major bf16, torch.matmul"}
+        del colsm, wtm, wm, dym, dytm, ym, dcm, dwm
+        log("library GEMMs: %s" % libgemm)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -440,6 +478,7 @@ def main():
         "fused_sample_with_prologue_hbm_frac": prologue_frac,
         "main_gemm_mfma_frac": kernels.get("gemm_forward", {}).get("mfma_frac"),
         "fusion": fusion,
+        "library_gemm": libgemm,
         "depthwise_dilated_1d": dwc or None,
         "other_configs_forward": others or None,
         "roofline": roof,

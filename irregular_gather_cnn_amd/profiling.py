@@ -43,7 +43,7 @@ KERNELS = {
     "dwpw1d": (r"k_dwpw1d\b", ["deft_dwpw.hip"]),
     "gemm_forward": (r"k_gemm_(dl|vd)<.*(DlFwd|FwdBal)|k_gemm<.*FwdOp",
                      ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
-    "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
+    "gemm_dcol": (r"k_gemm_dl<.*DlDcol|k_dcol_res\b|k_gemm<.*DcolOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "gemm_dw": (r"k_gemm_(dl|ws)<.*DlDw|k_gemm<.*DwOp", ["deft_gemm_dl.hip", "deft_gemm.hip", "deft_device.h"]),
     "sample_backward": (r"k_sample_bwd<|k_sample_bwd_mf\b", ["deft_backward.hip", "deft_device.h"]),
     "sample_backward_miss": (r"k_sample_bwd_miss<", ["deft_backward.hip", "deft_device.h"]),
