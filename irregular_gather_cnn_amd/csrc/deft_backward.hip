@@ -18,15 +18,17 @@
 //                     channels scatter dCol x weight into a fixed-point LDS
 //                     copy of the core with integer LDS atomics (order-
 //                     independent sums).
-//   k_sample_bwd_miss -- the rare taps beyond the halo: dOffset from global
-//                     memory, dX added with global atomics.
+//   k_sample_bwd_miss -- dOffset of every (pixel, tap) pair: the owning
+//                     core's chunk partials summed in chunk order, zero for a
+//                     fully outside tap; the rare taps beyond the halo
+//                     computed from global memory, their dX added with global
+//                     atomics; per-block dOffset sums for db_off.
 //   k_woff_bwd     -- per (image, 32-channel slice, band of output rows):
 //                     dW_off partials = dOffset rows against the plain
 //                     patches of x, both staged in LDS, on MFMA.
 //   k_dx_final     -- per 64 input pixels x 256 channels: dX_offset, the
 //                     transposed offset convolution (MFMA), plus the sampling
 //                     part of dX; rounded once.
-//   k_doff_sum     -- dOffset from the per-chunk partials, and db_off sums.
 //   k_reduce_final -- one fixed-order reduction of all partials to dW,
 //                     dW_off, db, db_off.
 // Global atomics are avoided on every hot path: on gfx950 they run far below
@@ -52,8 +54,10 @@ struct BwdParams {
   const void* dcol;
   const uint32_t* maxbits;  // max |dcol| as fp32 bits
   float* dxs;    // [N][H][W][Cin] fp32 (channel-minor): the sampling part of dX
-  float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials: the pairs a core owns are written
-                 // by the sampling backward, the others (fully outside, beyond the halo) by k_sample_bwd_miss
+  float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials of the pairs a core owns
+  float* doff;   // [N][Oc][Ho][Wo] dOffset, written by k_sample_bwd_miss
+  float* bpart;  // bias partials: [Cout][N] (dY sums), then [Oc][N][ceil(Ho*Wo/256)] (dOffset sums)
+  int Cout;
   int4* lists;   // [num_tg][list_cap]: one list per (core, group)
   int* counts;   // [num_tg]: entries in each list
   int num_tg;    // cores x groups
@@ -761,144 +765,103 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
 // has written dX.  Grid: N*G*K2 planes x ceil(Ho*Wo / 256) blocks.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
-  const int lane = threadIdx.x & 63;
+  __shared__ float red[4][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int HoWo = p.Ho * p.Wo;
   const int bpp = (HoWo + 255) / 256;  // blocks per plane
   const int plane = blockIdx.x / bpp, blk = blockIdx.x - plane * bpp;  // uniform
   const int r2 = plane / p.K2, t = plane - r2 * p.K2;
   const int n = r2 / p.G, g = r2 - n * p.G;
   const int ti = t / p.KW, tj = t - ti * p.KW;
+  const int oy = 2 * (g * p.K2 + t);  // offset channels oy (dy) and oy + 1 (dx)
   const size_t HW = (size_t)p.H * p.W;
+  const size_t cstride = (size_t)p.N * p.Oc * HoWo;  // between chunk partials
   const T* __restrict__ x = (const T*)p.x;
   const T* __restrict__ dcol = (const T*)p.dcol;
-  const float* __restrict__ offp = p.off + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo;
+  const size_t obase = ((size_t)n * p.Oc + oy) * HoWo;
+  const float* __restrict__ offp = p.off + obase;
   const int wpix0 = blk * 256 + (threadIdx.x & ~63);  // first pixel of this wave
-  {
-    const int pix = wpix0 + lane;
-    bool miss = false;
-    if (pix < HoWo) {
-      const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
-      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
-      const TapIndex ix = tap_index(by, bx, offp[pix], offp[HoWo + pix], p.H, p.W);
-      miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
-      // No core owns this pair: its chunk partials are written here, zero for
-      // a fully outside tap and for every chunk but the first of a miss.
-      if (ix.outside || miss) {
-        const size_t cstride = (size_t)p.N * p.Oc * HoWo;
-        float* dz = p.doffp + ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
-        for (int c = miss ? 1 : 0; c < p.Cg / p.CC; ++c) {
-          dz[c * cstride] = 0.f;
-          dz[c * cstride + HoWo] = 0.f;
-        }
+  const int pix = wpix0 + lane;
+  float vy = 0.f, vx = 0.f;
+  bool miss = false;
+  if (pix < HoWo) {
+    const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
+    const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
+    const TapIndex ix = tap_index(by, bx, offp[pix], offp[HoWo + pix], p.H, p.W);
+    miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
+    if (!ix.outside && !miss) {
+      // the owning core wrote one partial per channel chunk: summed in chunk order
+      const float* py = p.doffp + obase + pix;
+      vy = py[0];
+      vx = py[HoWo];
+      for (int c = 1; c < p.Cg / p.CC; ++c) {
+        vy += py[c * cstride];
+        vx += py[c * cstride + HoWo];
       }
     }
-    unsigned long long mask = __ballot(miss);
-    while (mask) {
-      const int l = __ffsll((long long)mask) - 1;
-      mask &= mask - 1;
-      const int pix = wpix0 + l;
-      const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
-      const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
-      const size_t oidx = ((size_t)n * p.Oc + 2 * (g * p.K2 + t)) * HoWo + pix;
-      float* dd = p.doffp + oidx;  // chunk-0 partial (the other chunks' were zeroed above)
-      const TapIndex ix = tap_index(by, bx, p.off[oidx], p.off[oidx + HoWo], p.H, p.W);
-      float w[4];
-      tap_weights(ix, w);
-      const int y0 = ix.y0, x0 = ix.x0;
-      const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
-      float gy = 0.f, gx = 0.f;
-      for (int c = lane; c < p.Cg; c += 64) {
-        const int cg = g * p.Cg + c;
-        const float gcv = Elem<T>::to_f32(dcol[((size_t)n * HoWo + pix) * p.Ck + (size_t)t * p.Cin + cg]);
-        const T* pl = x + ((size_t)n * p.Cin + cg) * HW;
-        float* dl = p.dxs + (size_t)n * HW * p.Cin + cg;  // channel-minor: pixel stride Cin
-        const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
-        const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
-        const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
-        const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
-        if (r0 && q0) atomicAdd(dl + ((size_t)y0 * p.W + x0) * p.Cin, w[0] * gcv);
-        if (r0 && q1) atomicAdd(dl + ((size_t)y0 * p.W + x0 + 1) * p.Cin, w[1] * gcv);
-        if (r1 && q0) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0) * p.Cin, w[2] * gcv);
-        if (r1 && q1) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0 + 1) * p.Cin, w[3] * gcv);
-        gy += gcv * ((1.0f - ix.lx) * (v10 - v00) + ix.lx * (v11 - v01));
-        gx += gcv * ((1.0f - ix.ly) * (v01 - v00) + ix.ly * (v11 - v10));
-      }
-      for (int s = 1; s < 64; s <<= 1) {
-        gy += __shfl_xor(gy, s);
-        gx += __shfl_xor(gx, s);
-      }
-      if (lane == 0) {
-        dd[0] = gy;
-        dd[HoWo] = gx;
-      }
+  }
+  // taps beyond the halo, one at a time per wave: its lanes split the channels
+  unsigned long long mask = __ballot(miss);
+  while (mask) {
+    const int l = __ffsll((long long)mask) - 1;
+    mask &= mask - 1;
+    const int mpix = wpix0 + l;
+    const int ho = mpix / p.Wo, wo = mpix - ho * p.Wo;
+    const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
+    const TapIndex ix = tap_index(by, bx, offp[mpix], offp[HoWo + mpix], p.H, p.W);
+    float w[4];
+    tap_weights(ix, w);
+    const int y0 = ix.y0, x0 = ix.x0;
+    const bool r0 = y0 >= 0, r1 = y0 + 1 < p.H, q0 = x0 >= 0, q1 = x0 + 1 < p.W;
+    float gy = 0.f, gx = 0.f;
+    for (int c = lane; c < p.Cg; c += 64) {
+      const int cg = g * p.Cg + c;
+      const float gcv = Elem<T>::to_f32(dcol[((size_t)n * HoWo + mpix) * p.Ck + (size_t)t * p.Cin + cg]);
+      const T* pl = x + ((size_t)n * p.Cin + cg) * HW;
+      float* dl = p.dxs + (size_t)n * HW * p.Cin + cg;  // channel-minor: pixel stride Cin
+      const float v00 = (r0 && q0) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0]) : 0.f;
+      const float v01 = (r0 && q1) ? Elem<T>::to_f32(pl[(size_t)y0 * p.W + x0 + 1]) : 0.f;
+      const float v10 = (r1 && q0) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0]) : 0.f;
+      const float v11 = (r1 && q1) ? Elem<T>::to_f32(pl[(size_t)(y0 + 1) * p.W + x0 + 1]) : 0.f;
+      if (r0 && q0) atomicAdd(dl + ((size_t)y0 * p.W + x0) * p.Cin, w[0] * gcv);
+      if (r0 && q1) atomicAdd(dl + ((size_t)y0 * p.W + x0 + 1) * p.Cin, w[1] * gcv);
+      if (r1 && q0) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0) * p.Cin, w[2] * gcv);
+      if (r1 && q1) atomicAdd(dl + ((size_t)(y0 + 1) * p.W + x0 + 1) * p.Cin, w[3] * gcv);
+      gy += gcv * ((1.0f - ix.lx) * (v10 - v00) + ix.lx * (v11 - v01));
+      gx += gcv * ((1.0f - ix.ly) * (v01 - v00) + ix.ly * (v11 - v10));
     }
+    for (int s = 1; s < 64; s <<= 1) {
+      gy += __shfl_xor(gy, s);
+      gx += __shfl_xor(gx, s);
+    }
+    if (lane == l) {
+      vy = gy;
+      vx = gx;
+    }
+  }
+  if (pix < HoWo) {
+    p.doff[obase + pix] = vy;
+    p.doff[obase + HoWo + pix] = vx;
+  }
+  // this block's sums of the two offset channels: db_off partials, added in a
+  // fixed order (lanes by the xor tree, then waves in order)
+  float sy = vy, sx = vx;
+  for (int s = 32; s > 0; s >>= 1) {
+    sy += __shfl_xor(sy, s);
+    sx += __shfl_xor(sx, s);
+  }
+  if (lane == 0) {
+    red[wave][0] = sy;
+    red[wave][1] = sx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float* bo = p.bpart + (size_t)p.Cout * p.N;
+    bo[((size_t)oy * p.N + n) * bpp + blk] = ((red[0][0] + red[1][0]) + red[2][0]) + red[3][0];
+    bo[((size_t)(oy + 1) * p.N + n) * bpp + blk] = ((red[0][1] + red[1][1]) + red[2][1]) + red[3][1];
   }
 }
 
-// dOffset = sum of the per-chunk partials, in chunk order.
-// dOffset = the sum of the per-chunk partials, one workgroup per (offset
-// channel, image) plane, which also leaves that plane's sum as the db_off
-// partial bpart[(Cout + o) * N + n].
-__global__ __launch_bounds__(256) void k_doff_sum(const float* __restrict__ part, float* doff, size_t n, int chunks,
-                                                  int Oc, int N, int HoWo, int Cout, float* bpart) {
-  __shared__ float red[256];
-  const int o = blockIdx.x, img = blockIdx.y;
-  const size_t base = ((size_t)img * Oc + o) * HoWo;
-  float s = 0.f;
-  if ((HoWo & 3) == 0 && (n & 3) == 0 && chunks <= 4) {
-    // up to four chunks: two passes of four pixels per thread with all their
-    // 16-byte loads in flight together, summed in chunk order
-    for (int q0 = threadIdx.x * 4; q0 < HoWo; q0 += 256 * 4 * 2) {
-      float4 u[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int q = q0 + h * 256 * 4;
-          u[h][k] = (q < HoWo && k < chunks) ? *(const float4*)(part + (size_t)k * n + base + q)
-                                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = q0 + h * 256 * 4;
-        if (q >= HoWo) break;
-        float4 v = u[h][0];
-#pragma unroll
-        for (int k = 1; k < 4; ++k)
-          if (k < chunks) {
-            v.x += u[h][k].x; v.y += u[h][k].y; v.z += u[h][k].z; v.w += u[h][k].w;
-          }
-        *(float4*)(doff + base + q) = v;
-        s += (v.x + v.y) + (v.z + v.w);
-      }
-    }
-  } else if ((HoWo & 3) == 0 && (n & 3) == 0) {
-    // four pixels per thread per pass; each chunk's partial one 16-byte load
-    for (int q = threadIdx.x * 4; q < HoWo; q += 256 * 4) {
-      float4 v = *(const float4*)(part + base + q);
-      for (int k = 1; k < chunks; ++k) {
-        const float4 u = *(const float4*)(part + (size_t)k * n + base + q);
-        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-      }
-      *(float4*)(doff + base + q) = v;
-      s += (v.x + v.y) + (v.z + v.w);
-    }
-  } else {
-    for (int q = threadIdx.x; q < HoWo; q += 256) {
-      float v = part[base + q];
-      for (int k = 1; k < chunks; ++k) v += part[(size_t)k * n + base + q];
-      doff[base + q] = v;
-      s += v;
-    }
-  }
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) bpart[(size_t)(Cout + o) * N + img] = red[0];
-}
 
 // ---------------------------------------------------------------------------
 // dW_off partials.  GEMM rows o (MB blocks of 32 starting at o0), columns
@@ -1452,45 +1415,55 @@ __global__ __launch_bounds__(256) void k_prep_backward(const BwdParams b, const 
 // All weight and bias gradients from their partials, summed in a fixed order
 // and rounded once: dw[co][c][t] (from [ndw][co][t][c], one partial per
 // pixel range of the dW GEMM), dw_off[o][c][t] (from
-// [N*bands][o][t][c]), db, db_off (from [ch][N]).  Each thread sums one
-// element's partials in ascending order with up to 32 loads in flight; the
-// dw_off elements, which have the most partials (one per image and band),
-// come first so that they are not left for the end of the launch.
+// [N*bands][o][t][c]), db (from [co][N]), db_off (from [o][N][blocks of 256
+// pixels]).  The first workgroups take the bias channels, one wave each (its
+// lanes add strided partials in ascending order, then a fixed xor tree).
+// Every other thread sums one weight element's partials in ascending order
+// with up to 32 loads in flight; the dw_off elements, which have the most
+// partials (one per image and band), come first so that they are not left for
+// the end of the launch.
 template <typename T>
 __global__ __launch_bounds__(256) void k_reduce_final(const float* __restrict__ dwpart, int ndw, T* dw, int Cout,
                                                       const float* __restrict__ dwoffpart, T* dwoff, int Oc, int nwp,
                                                       const float* __restrict__ bpart, T* db, T* dboff, int N, int Cin,
-                                                      int K2) {
+                                                      int K2, int nbo) {
+  const int nch = Cout + Oc;
+  const int nbw = (nch + 3) / 4;  // the first workgroups: one wave per bias channel
+  if ((int)blockIdx.x < nbw) {
+    const int ch = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (ch >= nch) return;
+    T* dst = ch < Cout ? db : dboff;
+    if (!dst) return;
+    const float* src = ch < Cout ? bpart + (size_t)ch * N : bpart + (size_t)Cout * N + (size_t)(ch - Cout) * nbo;
+    const int cnt = ch < Cout ? N : nbo;
+    float s = 0.f;
+    for (int z = lane; z < cnt; z += 64) s += src[z];  // each lane in ascending order, then a fixed tree
+    for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k);
+    if (lane == 0) dst[ch < Cout ? ch : ch - Cout] = Elem<T>::from_f32(s);
+    return;
+  }
   const size_t ck = (size_t)Cin * K2;
-  const size_t n1 = (size_t)Cout * ck, n2 = (size_t)Oc * ck, n3 = (size_t)Cout + Oc;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2 + n3; e += (size_t)gridDim.x * 256) {
-    if (e < n1 + n2) {
-      const bool woff = e < n2;
-      const size_t f = woff ? e : e - n2;  // partial order: [o][t][c]
-      const int fi = (int)f;               // weight tensors: below 2^31 elements
-      const int r = fi / Cin, c = fi - r * Cin;
-      const int o = r / K2, t = r - o * K2;
-      const float* src = woff ? dwoffpart : dwpart;
-      const size_t stride = woff ? n2 : n1;
-      const int cnt = woff ? nwp : ndw;
-      float s = 0.f;
-      for (int z = 0; z < cnt; z += 32) {
-        float v[32];
+  const size_t n1 = (size_t)Cout * ck, n2 = (size_t)Oc * ck;
+  const size_t b0 = blockIdx.x - nbw, nb = gridDim.x - nbw;
+  for (size_t e = b0 * 256 + threadIdx.x; e < n1 + n2; e += nb * 256) {
+    const bool woff = e < n2;
+    const size_t f = woff ? e : e - n2;  // partial order: [o][t][c]
+    const int fi = (int)f;               // weight tensors: below 2^31 elements
+    const int r = fi / Cin, c = fi - r * Cin;
+    const int o = r / K2, t = r - o * K2;
+    const float* src = woff ? dwoffpart : dwpart;
+    const size_t stride = woff ? n2 : n1;
+    const int cnt = woff ? nwp : ndw;
+    float s = 0.f;
+    for (int z = 0; z < cnt; z += 32) {
+      float v[32];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) v[u] = z + u < cnt ? src[(size_t)(z + u) * stride + f] : 0.f;
+      for (int u = 0; u < 32; ++u) v[u] = z + u < cnt ? src[(size_t)(z + u) * stride + f] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (z + u < cnt) s += v[u];
-      }
-      (woff ? dwoff : dw)[((size_t)o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
-    } else {
-      const int ch = (int)(e - n1 - n2);
-      T* dst = ch < Cout ? db : dboff;
-      if (!dst) continue;
-      float s = 0.f;
-      for (int z = 0; z < N; ++z) s += bpart[(size_t)ch * N + z];
-      dst[ch < Cout ? ch : ch - Cout] = Elem<T>::from_f32(s);
+      for (int u = 0; u < 32; ++u)
+        if (z + u < cnt) s += v[u];
     }
+    (woff ? dwoff : dw)[((size_t)o * Cin + c) * K2 + t] = Elem<T>::from_f32(s);
   }
 }
 
@@ -1517,7 +1490,6 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   float* dwpart = (float*)(ws + p.ws_dwpart);
   float* dwoffpart = (float*)(ws + p.ws_dwoffpart);
   float* bpart = (float*)(ws + p.ws_biaspart);
-  const size_t ndoff = (size_t)d.n * p.oc * p.ho * p.wo;
   hipError_t e;
   BwdParams b;
   b.N = d.n; b.Cin = d.c_in; b.H = d.h; b.W = d.w; b.Ho = p.ho; b.Wo = p.wo; b.KH = d.kh; b.KW = d.kw;
@@ -1534,6 +1506,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.lds_dx = p.lb_dx; b.lds_dc = p.lb_dc; b.lds_cnt = p.lb_cnt;
   b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
   b.lists = lists;
+  b.doff = doff; b.bpart = bpart; b.Cout = d.c_out;
   b.xh = (p.direct && p.bwd_mf) ? (const bf16_t*)(ws + p.ws_xh) : nullptr;
   b.num_tg = p.num_btiles * d.offset_groups;
   b.counts = (int*)(ws + p.ws_lcount);
@@ -1554,7 +1527,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   e = launch_gemm_dw(p, a.dy, cols, dwpart, st);
   if (e != hipSuccess) return e;
 
-  // sampling backward, the taps beyond the halo, then dOffset
+  // sampling backward, then dOffset of every pair (with the taps beyond the halo)
   {
     auto kern = !p.bwd_mf ? k_sample_bwd<T> : p.chunk_b == 64 ? k_sample_bwd_mf<64> : k_sample_bwd_mf<32>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lb_total);
@@ -1566,11 +1539,6 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     const size_t mgrid = (size_t)d.n * d.offset_groups * p.taps * (size_t)((p.ho * p.wo + 255) / 256);
     if (mgrid > 0x7fffffffu) return hipErrorInvalidValue;
     if (mgrid) DEFT_LAUNCH("sample_backward_miss", k_sample_bwd_miss<T>, dim3((unsigned)mgrid), dim3(256), 0, st, b);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int chunks = p.cg / p.chunk_b;
-    DEFT_LAUNCH("doff_sum", k_doff_sum, dim3(p.oc, d.n), dim3(256), 0, st, doffp, doff, ndoff, chunks, p.oc, d.n,
-                p.ho * p.wo, d.c_out, bpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1642,10 +1610,11 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   }
   // bias partials, then every weight / bias gradient
   {
-    const size_t total = ((size_t)d.c_out + p.oc) * p.ck + d.c_out + p.oc;
-    DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(grid_cap(total, 4096)), dim3(256), 0, st, dwpart, p.dw_splits, (T*)a.dw,
+    const size_t total = ((size_t)d.c_out + p.oc) * p.ck;
+    const unsigned nbw = (unsigned)(d.c_out + p.oc + 3) / 4;  // bias workgroups, then the weight sums
+    DEFT_LAUNCH("reduce_final", k_reduce_final<T>, dim3(nbw + grid_cap(total, 4096)), dim3(256), 0, st, dwpart, p.dw_splits, (T*)a.dw,
                 d.c_out, dwoffpart, (T*)a.dw_off, p.oc, d.n * p.woff_bands, bpart, (T*)a.db, (T*)a.db_off, d.n,
-                d.c_in, p.taps);
+                d.c_in, p.taps, d.n * ((p.ho * p.wo + 255) / 256));
     e = hipGetLastError();
   }
   return e;

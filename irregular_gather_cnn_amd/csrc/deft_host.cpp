@@ -282,7 +282,8 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   }
   p.ws_dwpart = o; o = align256(o + (size_t)p.dw_splits * d.c_out * s.ck * 4);
   p.ws_dwoffpart = o; o = align256(o + (size_t)d.n * p.woff_bands * s.oc * s.ck * 4);
-  p.ws_biaspart = o; o = align256(o + (size_t)(d.c_out + s.oc) * d.n * 4);
+  // bias partials: [Cout][N] dY sums, then [Oc][N][blocks of 256 pixels] dOffset sums
+  p.ws_biaspart = o; o = align256(o + ((size_t)d.c_out + (size_t)s.oc * (((size_t)s.ho * s.wo + 255) / 256)) * d.n * 4);
   p.ws_train_end = o;
   return true;
 }

@@ -50,7 +50,6 @@ KERNELS = {
 
     "offset_weight_backward": (r"k_woff_bwd<", ["deft_backward.hip", "deft_device.h"]),
     "dx_final": (r"k_dx_final<", ["deft_backward.hip", "deft_device.h"]),
-    "doff_sum": (r"k_doff_sum\b", ["deft_backward.hip"]),
     "bias_partial": (r"k_bias_partial<", ["deft_backward.hip"]),
     "reduce_final": (r"k_reduce_final<", ["deft_backward.hip"]),
     "prep_backward": (r"k_prep_backward<", ["deft_backward.hip"]),
