@@ -301,6 +301,21 @@ def main():
         gg_fn = lambda: gg.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y, offsets=offs)
         fusion["gather_gemm_fwd_ms"] = round(time_forward(gg_fn), 4)
         del gg
+    # The pages' own staging (tile + halo of the input in LDS, out-of-halo
+    # taps from global memory) on the same inputs, under a few forced plans:
+    # the forward the default direct gather replaced, re-measured.
+    if wl.dtype == "bf16":
+        lds = {}
+        for th, tw, hh, ch in ((8, 8, 2, 64), (8, 8, 3, 64), (8, 8, 2, 32), (4, 16, 2, 64)):
+            try:
+                lh = DeformConv(**geo, plan=(th, tw, hh, ch), training=False, device=dev)
+            except L.DeftError:
+                continue
+            lh_fn = lambda: lh.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], y=y)
+            lds["%dx%d_halo%d_chunk%d" % (th, tw, hh, ch)] = round(time_forward(lh_fn), 4)
+            del lh
+        if lds:
+            fusion["lds_halo_fwd_ms"] = lds
     L.deft_timing_start(8 * args.steps)
     for _ in range(args.steps):
         unfused_fn()
