@@ -400,6 +400,11 @@ def test_backward_halo_planned_apart_from_forward(dtype):
     dict(n=2, c_in=16, c_out=8, h=8, w=8),                # single partial tile everywhere
     dict(n=2, c_in=32, c_out=264, h=8, w=6, groups=2),    # c_out over one 256-wide tile
     dict(n=1, c_in=32, c_out=16, h=16, w=16, stride=2),   # Ho*Wo = 64
+    # c_out = 256 and 9*c_in a multiple of 256: the dCol GEMM with the W2
+    # block resident in LDS; pixel tiles of 128 that are ragged (360 and 192
+    # pixels) and cross image boundaries
+    dict(n=3, c_in=256, c_out=256, h=10, w=12),
+    dict(n=3, c_in=256, c_out=256, h=16, w=16, stride=2),
 ])
 def test_backward_bf16_direct_gemm(case):
     """Shapes that take the direct global-to-LDS GEMMs (bf16, Ho*Wo and c_out
