@@ -800,6 +800,8 @@ struct FwdBalT {
 };
 
 using FwdVd = FwdBalT<VdCfg<224, 256>>;
+// the same kernel for layers with few output rows per CU (at most 64)
+using FwdVdSmall = FwdBalT<VdCfg<64, 256>>;
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
@@ -1172,6 +1174,17 @@ hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols,
     const int gm = std::min(units, std::max((p.cus + gn - 1) / gn, tiles(units, FwdVd::Cfg::BM / 8)));
     if (p.ck % FwdVd::Cfg::BK == 0 && gm > 0 && 8 * (units / gm) >= 160) {
       FwdVd op;
+      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
+      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
+      op.div_howo = make_fastdiv(op.HoWo);
+      op.units = units; op.gn = gn; op.gm = gm;
+      return run_vd("gemm_forward", op, gm * gn, st);
+    }
+    // few rows per CU (the largest share at most 64): all 256 output
+    // channels of them per workgroup, one workgroup per CU
+    if (p.ck % FwdVdSmall::Cfg::BK == 0 && gm > 0 && 8 * ((units + gm - 1) / gm) <= FwdVdSmall::Cfg::BM &&
+        8 * (units / gm) >= 32) {
+      FwdVdSmall op;
       op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
       op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
       op.div_howo = make_fastdiv(op.HoWo);
