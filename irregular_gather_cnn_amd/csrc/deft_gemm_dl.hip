@@ -800,8 +800,9 @@ struct FwdBalT {
 };
 
 using FwdVd = FwdBalT<VdCfg<224, 256>>;
-// the same kernel for layers with few output rows per CU (at most 64)
+// the same kernel for layers with few output rows per CU (at most 64 or 128)
 using FwdVdSmall = FwdBalT<VdCfg<64, 256>>;
+using FwdVdMid = FwdBalT<VdCfg<128, 256>>;
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
@@ -1185,6 +1186,15 @@ hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols,
     if (p.ck % FwdVdSmall::Cfg::BK == 0 && gm > 0 && 8 * ((units + gm - 1) / gm) <= FwdVdSmall::Cfg::BM &&
         8 * (units / gm) >= 32) {
       FwdVdSmall op;
+      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
+      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
+      op.div_howo = make_fastdiv(op.HoWo);
+      op.units = units; op.gn = gn; op.gm = gm;
+      return run_vd("gemm_forward", op, gm * gn, st);
+    }
+    if (p.ck % FwdVdMid::Cfg::BK == 0 && gm > 0 && 8 * ((units + gm - 1) / gm) <= FwdVdMid::Cfg::BM &&
+        8 * (units / gm) >= 64) {
+      FwdVdMid op;
       op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
       op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
       op.div_howo = make_fastdiv(op.HoWo);
