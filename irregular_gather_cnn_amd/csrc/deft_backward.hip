@@ -1204,6 +1204,7 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
   const int c0 = cb * 256 + wave * 32;  // eight waves, 32 channels each
   const bool active = c0 < p.Cin;
   const T* __restrict__ wt = (const T*)p.wofft;
+  const __amdgpu_buffer_rsrc_t wrs = make_brsrc(wt, (uint32_t)((size_t)p.Cin * p.KKP * sizeof(T)));
   f32x16_t acc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -1270,15 +1271,33 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
     }
     __syncthreads();
     if (active) {
+      // The weight operand of k-chunk kc comes from global memory three
+      // chunks ahead, in three fixed register slots (the loop is unrolled by
+      // three); the loads are always issued (past the chunks or the channels
+      // they read zero), so the compiler's waits stay exact.
       const int nkc = len / (2 * VEC);
-      for (int kc = 0; kc < nkc; ++kc) {
+      auto lda = [&](int kc) {
         const int kl = kc * 2 * VEC + (lane >> 5) * VEC;
-        const uint4 a = crow < p.Cin ? *(const uint4*)(wt + (size_t)crow * p.KKP + kb + kl) : make_uint4(0, 0, 0, 0);
+        const int off = kc < nkc && crow < p.Cin ? (crow * p.KKP + kb + kl) * (int)sizeof(T) : kOOB;
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+      };
+      auto mm = [&](int kc, const uint4& a) {
+        if (kc >= nkc) return;
+        const int kl = kc * 2 * VEC + (lane >> 5) * VEC;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint4 b = *(const uint4*)(bt + (j * 32 + (lane & 31)) * bstr + kl);
           mfma_chunk(acc[j], b, a, T());  // rows = pixels, columns = channels
         }
+      };
+      uint4 a0 = lda(0), a1 = lda(1), a2 = lda(2);
+      for (int kc = 0; kc < nkc; kc += 3) {
+        mm(kc, a0);
+        a0 = lda(kc + 3);
+        mm(kc + 1, a1);
+        a1 = lda(kc + 4);
+        mm(kc + 2, a2);
+        a2 = lda(kc + 5);
       }
     }
   }
