@@ -887,7 +887,8 @@ struct WoffParams {
 // offset channel per lane, rounded to bf16), one k-chunk ahead, in two fixed
 // register slots; fp32 stages the dOffset rows too ([o][row][DLS]).
 template <typename T, int MB>
-__global__ __launch_bounds__(256) void k_woff_bwd(const WoffParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2 : 1))) void k_woff_bwd(
+    const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int KC = 2 * VEC;  // pixels per k-chunk
   extern __shared__ __align__(16) unsigned char smem[];
