@@ -785,16 +785,31 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
   float vy = 0.f, vx = 0.f;
   bool miss = false;
   if (pix < HoWo) {
+    // the chunk partials (up to four) are loaded with the offsets, in one
+    // round trip, and kept only for a pair that a core owns
+    const int nch = p.Cg / p.CC;
+    const float* py = p.doffp + obase + pix;
+    float py4[4], px4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      py4[c] = c < nch ? py[c * cstride] : 0.f;
+      px4[c] = c < nch ? py[c * cstride + HoWo] : 0.f;
+    }
     const int ho = pix / p.Wo, wo = pix - ho * p.Wo;
     const int by = ho * p.SH - p.PH + ti * p.DH, bx = wo * p.SW - p.PW + tj * p.DW;
     const TapIndex ix = tap_index(by, bx, offp[pix], offp[HoWo + pix], p.H, p.W);
     miss = !ix.outside && max(abs(ix.y0 - by), abs(ix.x0 - bx)) > p.halo;
     if (!ix.outside && !miss) {
       // the owning core wrote one partial per channel chunk: summed in chunk order
-      const float* py = p.doffp + obase + pix;
-      vy = py[0];
-      vx = py[HoWo];
-      for (int c = 1; c < p.Cg / p.CC; ++c) {
+      vy = py4[0];
+      vx = px4[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c)
+        if (c < nch) {
+          vy += py4[c];
+          vx += px4[c];
+        }
+      for (int c = 4; c < nch; ++c) {
         vy += py[c * cstride];
         vx += py[c * cstride + HoWo];
       }
