@@ -230,13 +230,14 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   if (direct) {
     // offsets, then one region shared in turn by the double-buffered
     // footprint staging (256 * stage_d 16-byte slots per buffer), the
-    // phase-A partial sums and the tap table (int4) + weights (float4)
+    // phase-A partial sums and the tap table (int4 corner offsets, float4
+    // weights, int column offset)
     p.stage_d = (p.foot_h * p.foot_w * (p.chunk_a / 8) + 255) / 256;
     if (p.stage_d > 7) return false;
     p.lds_off = 0;
     p.lds_info = align16(ocw * pt * 4);
     p.lds_region = p.lds_info;
-    p.lds_total = p.lds_info + std::max({4 * ocw * pt * 4, 32 * s.taps * pt, 2 * p.stage_d * 4096});
+    p.lds_total = p.lds_info + std::max({4 * ocw * pt * 4, 36 * s.taps * pt, 2 * p.stage_d * 4096});
   } else {
     p.lds_off = align16(region);
     p.lds_info = p.lds_off + align16(ocw * pt * 4);

@@ -434,8 +434,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int obase = 2 * g * p.K2;
   const int HW = p.H * p.W;
   float* off_l = (float*)(smem + p.lds_off);                                  // [ocw][PT]
-  int4* tab = (int4*)(smem + p.lds_info);                                     // [PT][K2]
-  float4* wts = (float4*)(smem + p.lds_info + PT * p.K2 * 16);                // [PT][K2]
+  int4* tab = (int4*)(smem + p.lds_info);                                     // [PT][K2] corner byte offsets
+  float4* wts = (float4*)(smem + p.lds_info + PT * p.K2 * 16);                // [PT][K2] corner weights
+  int* cof = (int*)(smem + p.lds_info + PT * p.K2 * 32);                      // [PT][K2] column offset
   const bf16_t* __restrict__ xn = p.xh + (size_t)n * (HW + 1) * p.Cin;
   const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
 
@@ -601,12 +602,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 
   if (p.hist) tile_halo_hist(p, off_l, 1, oh0, ow0, thn, twn);
-  // ---- tap index stage: corner pixel, corner mask, column offset, weights ----
+  // ---- tap index stage: corner byte offsets, column offset, weights ----
+  // A corner outside the image (and every corner of a fully outside tap)
+  // points at the copy's zero pixel; -1 marks a pixel beyond the tile.
   const int nent = PT * p.K2;
+  const int zpix = HW * p.Cin * 2;
   for (int e = tid; e < nent; e += 256) {
     const int pix = fdiv(e, p.div_k2), t = e - pix * p.K2;
     const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
-    int4 tb = make_int4(0, 0, -1, 0);
+    int4 tb = make_int4(zpix, zpix, zpix, zpix);
+    int co = -1;
     float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
     if (ty < thn && tx < twn) {
       const int ti = t / p.KW, tj = t - ti * p.KW;
@@ -615,10 +620,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const float dy = off_l[(2 * t) * PT + pix];
       const float dx = off_l[(2 * t + 1) * PT + pix];
       const TapIndex ix = tap_index(by, bx, dy, dx, p.H, p.W);
-      tb.z = (ty * p.Wo + tx) * p.Ck + t * p.Cin;
+      co = (ty * p.Wo + tx) * p.Ck + t * p.Cin;
       if (!ix.outside) {
-        tb.x = ix.y0 * p.W + ix.x0;
-        tb.y = (int)corner_mask(ix, p.H, p.W);
+        const int b = (ix.y0 * p.W + ix.x0) * p.Cin * 2, cw1 = p.Cin * 2, cwW = p.W * p.Cin * 2;
+        const uint32_t m = corner_mask(ix, p.H, p.W);
+        tb.x = (m & 1) ? b : zpix;
+        tb.y = (m & 2) ? b + cw1 : zpix;
+        tb.z = (m & 4) ? b + cwW : zpix;
+        tb.w = (m & 8) ? b + cwW + cw1 : zpix;
         float w[4];
         tap_weights(ix, w);
         wv = make_float4(w[0], w[1], w[2], w[3]);
@@ -626,37 +635,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     tab[e] = tb;
     wts[e] = wv;
+    cof[e] = co;
   }
   __syncthreads();
 
   // ---- phase B: every (pixel, tap) x 8 channels, corners from the copy ----
+  // 32-bit buffer offsets: the table's corner offset plus the lane's channels.
   const int nvm = (1 << p.nv_log) - 1;
   const int v = tid & nvm, e0 = tid >> p.nv_log, estep = 256 >> p.nv_log;
   const int cofs = g * p.Cg + v * 8;
-  const bf16_t* __restrict__ xc = xn + cofs;
+  const __amdgpu_buffer_rsrc_t xb = make_brsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * 2));
+  const int lofs = cofs * 2;
   bf16_t* __restrict__ colt = (bf16_t*)p.cols + ((size_t)n * p.Ho * p.Wo + (size_t)oh0 * p.Wo + ow0) * p.Ck + cofs;
-  const int cw1 = p.Cin, cwW = p.W * p.Cin, zero = HW * p.Cin;
   for (int e = e0; e < nent; e += 2 * estep) {
-    int4 tb[2];
+    int co[2];
     float w[2][4];
     uint4 q[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int eu = e + u * estep;
-      tb[u] = eu < nent ? tab[eu] : make_int4(0, 0, -1, 0);
-      const float4 wq = wts[eu < nent ? eu : e];
+      const int ec = eu < nent ? eu : e;
+      const int4 tb = tab[ec];
+      co[u] = eu < nent ? cof[ec] : -1;
+      const float4 wq = wts[ec];
       w[u][0] = wq.x; w[u][1] = wq.y; w[u][2] = wq.z; w[u][3] = wq.w;
-      const int b = tb[u].x * p.Cin, m = tb[u].y;
-      const int a0 = (m & 1) ? b : zero, a1 = (m & 2) ? b + cw1 : zero;
-      const int a2 = (m & 4) ? b + cwW : zero, a3 = (m & 8) ? b + cwW + cw1 : zero;
-      q[u][0] = *(const uint4*)(xc + a0);
-      q[u][1] = *(const uint4*)(xc + a1);
-      q[u][2] = *(const uint4*)(xc + a2);
-      q[u][3] = *(const uint4*)(xc + a3);
+      q[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xb, tb.x + lofs, 0, 0));
+      q[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xb, tb.y + lofs, 0, 0));
+      q[u][2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xb, tb.z + lofs, 0, 0));
+      q[u][3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xb, tb.w + lofs, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if (tb[u].z < 0) continue;
+      if (co[u] < 0) continue;
       float f00[8], f01[8], f10[8], f11[8], o8[8];
       unpack8(q[u][0], f00);
       unpack8(q[u][1], f01);
@@ -664,7 +674,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       unpack8(q[u][3], f11);
 #pragma unroll
       for (int c = 0; c < 8; ++c) o8[c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
-      store8_nt(colt + tb[u].z, o8);
+      store8_nt(colt + co[u], o8);
     }
   }
 }
