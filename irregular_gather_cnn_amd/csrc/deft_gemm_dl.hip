@@ -664,11 +664,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     __syncthreads();
     constexpr int kCh = C::WM / 8, kRows = 64 / kCh;
-    static_assert(C::WN % kRows == 0, "epilogue passes");
 #pragma unroll 4
-    for (int it = 0; it < C::WN / kRows; ++it) {
+    for (int it = 0; it < (C::WN + kRows - 1) / kRows; ++it) {
       const int nl = it * kRows + lane / kCh, c = lane % kCh;
-      if (lane < kRows * kCh && c * 8 < tile_rows) {  // kCh need not divide 64
+      // kCh need not divide 64, nor kRows WN
+      if (lane < kRows * kCh && nl < C::WN && c * 8 < tile_rows) {
         const uint4 v = *(const uint4*)(reg + nl * kEpiStride + c * 16);
         op.store_chunk(tc, nw + nl, mw + c * 8, v);
       }
@@ -800,9 +800,11 @@ struct FwdBalT {
 };
 
 using FwdVd = FwdBalT<VdCfg<224, 256>>;
-// the same kernel for layers with few output rows per CU (at most 64 or 128)
-using FwdVdSmall = FwdBalT<VdCfg<64, 256>>;
+// the same kernel for shares of at most 192, 160, 128 or 64 rows
+using FwdVd192 = FwdBalT<VdCfg<192, 256>>;
+using FwdVd160 = FwdBalT<VdCfg<160, 256>>;
 using FwdVdMid = FwdBalT<VdCfg<128, 256>>;
+using FwdVdSmall = FwdBalT<VdCfg<64, 256>>;
 
 // ---- dCol: C[m = e][n = q] = sum_co W2[e][co] dY[img(q)][co][p(q)]; dcol[q][e] ----
 struct DlDcol {
@@ -1167,39 +1169,33 @@ hipError_t dl_gemm_forward(const deft_plan& p, const void* wt, const void* cols,
                            hipStream_t st) {
   const int M = p.d.n * p.ho * p.wo, N = p.d.c_out;
   // Row-balanced four-wave kernel: one workgroup per CU, each an equal share
-  // of whole 8-row units (at most 224 rows) and 256 output channels.  Used
-  // where the shares fill most of a 224-row tile (it computes all 7 row
-  // blocks) and k comes in whole 64-deep stages.
+  // of whole 8-row units and 256 output channels, in the instance with the
+  // smallest row tile that holds the share (it computes every row block of
+  // its tile); k in whole 64-deep stages.  More rows than one round of
+  // 224-row shares holds run in as many rounds as needed, each CU taking one
+  // share per round.  Shares of fewer than 32 rows go to the tiled kernels.
   {
     const int units = M / 8, gn = tiles(N, FwdVd::Cfg::BN);
-    const int gm = std::min(units, std::max((p.cus + gn - 1) / gn, tiles(units, FwdVd::Cfg::BM / 8)));
-    if (p.ck % FwdVd::Cfg::BK == 0 && gm > 0 && 8 * (units / gm) >= 160) {
-      FwdVd op;
-      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
-      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
-      op.div_howo = make_fastdiv(op.HoWo);
-      op.units = units; op.gn = gn; op.gm = gm;
-      return run_vd("gemm_forward", op, gm * gn, st);
-    }
-    // few rows per CU (the largest share at most 64): all 256 output
-    // channels of them per workgroup, one workgroup per CU
-    if (p.ck % FwdVdSmall::Cfg::BK == 0 && gm > 0 && 8 * ((units + gm - 1) / gm) <= FwdVdSmall::Cfg::BM &&
-        8 * (units / gm) >= 32) {
-      FwdVdSmall op;
-      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
-      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
-      op.div_howo = make_fastdiv(op.HoWo);
-      op.units = units; op.gn = gn; op.gm = gm;
-      return run_vd("gemm_forward", op, gm * gn, st);
-    }
-    if (p.ck % FwdVdMid::Cfg::BK == 0 && gm > 0 && 8 * ((units + gm - 1) / gm) <= FwdVdMid::Cfg::BM &&
-        8 * (units / gm) >= 64) {
-      FwdVdMid op;
-      op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
-      op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
-      op.div_howo = make_fastdiv(op.HoWo);
-      op.units = units; op.gn = gn; op.gm = gm;
-      return run_vd("gemm_forward", op, gm * gn, st);
+    const int slots = (p.cus + gn - 1) / gn;  // row ranges per round
+    const int rounds = std::max(1, tiles(units, slots * (FwdVd::Cfg::BM / 8)));
+    const int gm = std::min(units, rounds * slots);
+    if (p.ck % FwdVd::Cfg::BK == 0 && gm > 0) {
+      const int smax = 8 * ((units + gm - 1) / gm), smin = 8 * (units / gm);
+      auto run = [&](auto op) {
+        op.cols = (const bf16_t*)cols; op.wt = (const bf16_t*)wt; op.bias = (const bf16_t*)b; op.y = (bf16_t*)y;
+        op.M = M; op.N = N; op.K = p.ck; op.HoWo = p.ho * p.wo;
+        op.div_howo = make_fastdiv(op.HoWo);
+        op.units = units; op.gn = gn; op.gm = gm;
+        return run_vd("gemm_forward", op, gm * gn, st);
+      };
+      if (smax > FwdVd192::Cfg::BM) return run(FwdVd());
+      if (smax > FwdVd160::Cfg::BM) return run(FwdVd192());
+      if (smax > FwdVdMid::Cfg::BM) return run(FwdVd160());
+      if (smax > FwdVdSmall::Cfg::BM) {
+        if (smin >= 64) return run(FwdVdMid());
+      } else if (smin >= 32) {
+        return run(FwdVdSmall());
+      }
     }
   }
   auto count = [&](int bm, int bn) { return tiles(M, bm) * tiles(N, bn); };

@@ -98,6 +98,33 @@ def test_forward_matches_oracle(name):
         assert e_y <= tol
 
 
+@pytest.mark.parametrize("n", [12, 15, 20, 24])
+def test_forward_gemm_row_shares(n):
+    """The main GEMM's row-balanced forms: each CU takes an equal share of
+    the output rows in the instance whose row tile holds it (152-row shares
+    at 12 images: the 160-row tile; 184 at 15: the 192-row tile), in two
+    rounds where one round of 224-row shares does not hold them (128-row
+    shares at 20 images, 152 at 24).  Each row's k order is the same in every
+    form, so y of the images a batch shares with the 16-image batch (one
+    round of the 224-row tile) is equal bit for bit; the batch's last image
+    is checked against the oracle."""
+    big = WORKLOADS["bf16_n16_c256_56x56"].scaled(n=max(n, 16))
+    say("forward GEMM row shares", n)
+    inp = make_inputs(big)
+    t = {k: dev(v, big.dtype) for k, v in inp.items()}
+    wl = big.scaled(n=n)
+    y, _ = make_layer(wl).forward(t["x"][:n].contiguous(), t["w_off"], t["b_off"], t["w"], t["b"])
+    y16, _ = make_layer(big.scaled(n=16)).forward(t["x"][:16].contiguous(), t["w_off"], t["b_off"], t["w"], t["b"])
+    torch.cuda.synchronize()
+    m = min(n, 16)
+    assert torch.equal(y[:m], y16[:m])
+    s1 = image_shape(wl, 1)
+    y_ref, _ = oracle.forward(s1, inp["x"][n - 1:n], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+    e_y = rel(host(y[n - 1:n]), y_ref)
+    say("  image %d: y %.2e" % (n - 1, e_y))
+    assert e_y <= TOL[wl.dtype]
+
+
 @pytest.mark.parametrize("name", FWD)
 def test_index_stage_bit_exact(name):
     """Tap index / corner mask from the GPU's own offsets equals the oracle's
