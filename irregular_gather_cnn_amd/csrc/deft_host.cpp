@@ -155,9 +155,11 @@ bool layout_backward(deft_plan& p) {
   const int wh = (p.btile_h + 2 * p.bhalo + 1 + d.stride_h - 1) / d.stride_h + 1;
   const int ww = (p.btile_w + 2 * p.bhalo + 1 + d.stride_w - 1) / d.stride_w + 1;
   p.list_cap = s.taps * std::min(wh, s.ho) * std::min(ww, s.wo);
-  // offset-weight backward: (image, channel slice, row band) workgroups; a
-  // band's rows are staged at once, so bands are as tall as two workgroups
-  // per CU allow, and numerous enough to fill the chip
+  // offset-weight backward: (image, channel slice, row band) workgroups, two
+  // per CU (one where a launch covers more than 32 offset channels); a band's
+  // input rows are staged at once.  The band count minimises the staged rows
+  // per workgroup times the rounds of workgroups the chip runs, the fewest
+  // bands among equals (each band adds a dW_off partial to the reduction).
   const int slices = (d.c_in + 31) / 32;
   const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
   const int wop = (s.wo + kc - 1) / kc * kc;
@@ -169,12 +171,17 @@ bool layout_backward(deft_plan& p) {
     // bf16 reads its dOffset operand from global memory; fp32 stages it too
     return align16(32 * xr * xs * s.esz) + (d.dtype == DEFT_BF16 ? 0 : mbw * 32 * rows * (wop + vec) * s.esz);
   };
-  int bands = 1;
-  while (bands < s.ho) {
-    const int rows = (s.ho + bands - 1) / bands;
-    if (woff_lds(rows) <= p.max_lds / 2 && (double)d.n * slices * bands >= 512) break;
-    ++bands;
+  const long slots = (long)std::max(1, p.cus) * (mbw == 1 ? 2 : 1);
+  int bands = 0;
+  long best = 0;
+  for (int nb = 1; nb <= s.ho; ++nb) {
+    const int rows = (s.ho + nb - 1) / nb;
+    if (woff_lds(rows) > p.max_lds / 2) continue;
+    const long rounds = ((long)d.n * slices * nb + slots - 1) / slots;
+    const long cost = rounds * ((rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1);
+    if (!bands || cost < best) { bands = nb; best = cost; }
   }
+  if (!bands) bands = s.ho;
   // the offset-weight backward stages whole input rows: a band of the rows
   // it settled on must fit the LDS, else this shape has no backward here
   if (woff_lds((s.ho + bands - 1) / bands) > p.max_lds) return false;
