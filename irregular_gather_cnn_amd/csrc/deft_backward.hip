@@ -56,6 +56,7 @@ struct BwdParams {
   float* dxs;    // [N][H][W][Cin] fp32 (channel-minor): the sampling part of dX
   float* doffp;  // [Cg/CC][N][Oc][Ho][Wo] per-chunk dOffset partials of the pairs a core owns
   float* doff;   // [N][Oc][Ho][Wo] dOffset, written by k_sample_bwd_miss
+  bf16_t* doff16;  // the same rounded to bf16 (bf16 layers), or null
   float* bpart;  // bias partials: [Cout][N] (dY sums), then [Oc][N][ceil(Ho*Wo/256)] (dOffset sums)
   int Cout;
   int4* lists;   // [num_tg][list_cap]: one list per (core, group)
@@ -857,6 +858,10 @@ __global__ __launch_bounds__(256) void k_sample_bwd_miss(const BwdParams p) {
   if (pix < HoWo) {
     p.doff[obase + pix] = vy;
     p.doff[obase + HoWo + pix] = vx;
+    if (p.doff16) {
+      p.doff16[obase + pix] = f32_to_bf16(vy);
+      p.doff16[obase + HoWo + pix] = f32_to_bf16(vx);
+    }
   }
   // this block's sums of the two offset channels: db_off partials, added in a
   // fixed order (lanes by the xor tree, then waves in order)
@@ -889,6 +894,7 @@ struct WoffParams {
   int o0, orows, slices, bands, band_rows, num_wg, WoP, XR, XS, XL, DLS;
   const void* x;
   const float* doff;
+  const bf16_t* doff16;  // dOffset rounded to bf16, or null
   float* part;  // [N*bands][Oc][K2][Cin]
   const bf16_t* xh;  // channel-minor copy of x left by a direct-gather forward, or null
 };
@@ -901,8 +907,11 @@ struct WoffParams {
 // operand straight from global memory as MFMA fragments (8 pixels of one
 // offset channel per lane, rounded to bf16), one k-chunk ahead, in two fixed
 // register slots; fp32 stages the dOffset rows too ([o][row][DLS]).
-template <typename T, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2 : 1))) void k_woff_bwd(
+// A16: the dOffset operand comes from its bf16 copy in aligned 8-pixel
+// pieces (bf16, one 32-row block, row length a multiple of 8): no fp32
+// loads, registers for four waves per SIMD.
+template <typename T, int MB, bool A16 = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(A16 ? 4 : (MB == 1 ? 2 : 1)))) void k_woff_bwd(
     const WoffParams p) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int KC = 2 * VEC;  // pixels per k-chunk
@@ -1019,11 +1028,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2
     // nothing to load go past its range and read zero, so every step issues
     // the same loads and the waits for them stay exact
     const __amdgpu_buffer_rsrc_t drs = make_brsrc(doff, (uint32_t)((size_t)p.Oc * HoWo * 4));
-    int orow[MB];  // byte offset of this lane's offset channel (o0 + mb*32 + lane%32) at the band's first row
+    // the bf16 copy, where every 8-pixel group of a row is one aligned piece
+    const __amdgpu_buffer_rsrc_t d16 =
+        make_brsrc(A16 ? p.doff16 + (size_t)n * p.Oc * HoWo : nullptr, A16 ? (uint32_t)((size_t)p.Oc * HoWo * 2) : 0u);
+    int orow[MB];  // element offset of this lane's offset channel (o0 + mb*32 + lane%32) at the band's first row
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int o = mb * 32 + cl;
-      orow[mb] = o < p.orows ? ((p.o0 + o) * HoWo + ho0 * p.Wo) * 4 : -1;
+      orow[mb] = o < p.orows ? (p.o0 + o) * HoWo + ho0 * p.Wo : -1;
     }
     // operand of k-chunk `it` (row it / nkc, pixels kc + 8*half .. +7)
     auto load_a = [&](int it, uint4* a) {
@@ -1032,7 +1044,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const bool ok = orow[mb] >= 0 && it < niter;
-        const int b0 = orow[mb] + (ry * p.Wo + w0) * 4;
+        const int e0 = orow[mb] + ry * p.Wo + w0;
+        if constexpr (A16) {
+          a[mb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(d16, ok && w0 < p.Wo ? e0 * 2 : kOOB,
+                                                                                 0, 0));
+          continue;
+        }
+        const int b0 = e0 * 4;
         float f[8];
         if (vec4) {
           const uint4 u0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -1542,6 +1560,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.x = a.x; b.off = a.offsets; b.dcol = dcol; b.maxbits = maxbits; b.dxs = dxs; b.doffp = doffp;
   b.lists = lists;
   b.doff = doff; b.bpart = bpart; b.Cout = d.c_out;
+  b.doff16 = d.dtype == DEFT_BF16 ? (bf16_t*)(ws + p.ws_doff16) : nullptr;
   b.xh = (p.direct && p.bwd_mf) ? (const bf16_t*)(ws + p.ws_xh) : nullptr;
   b.num_tg = p.num_btiles * d.offset_groups;
   b.counts = (int*)(ws + p.ws_lcount);
@@ -1597,6 +1616,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
     w.XS = span;  // pixels per staged row, from x = -PW
     w.DLS = w.WoP + (d.dtype == DEFT_BF16 ? 8 : 4);
     w.x = a.x; w.doff = doff; w.part = dwoffpart;
+    w.doff16 = b.doff16;
     w.xh = p.direct ? (const bf16_t*)(ws + p.ws_xh) : nullptr;
     for (int o0 = 0; o0 < p.oc && w.num_wg; o0 += 96) {
       w.o0 = o0;
@@ -1604,7 +1624,11 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
       const int mb = (w.orows + 31) / 32;
       const int lds = ((32 * w.XR * w.XS * (int)sizeof(T) + 15) & ~15) +
                       (sizeof(T) == 2 ? 0 : mb * 32 * w.band_rows * w.DLS * (int)sizeof(T));
-      if (mb == 1) {
+      if (mb == 1 && woff_a16(d.dtype, p.oc, p.wo)) {
+        e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 1, true>), dim3(w.num_wg), dim3(256), lds, st, w);
+      } else if (mb == 1) {
         e = hipFuncSetAttribute((const void*)k_woff_bwd<T, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e == hipSuccess)
           DEFT_LAUNCH("offset_weight_backward", (k_woff_bwd<T, 1>), dim3(w.num_wg), dim3(256), lds, st, w);

@@ -155,11 +155,14 @@ bool layout_backward(deft_plan& p) {
   const int wh = (p.btile_h + 2 * p.bhalo + 1 + d.stride_h - 1) / d.stride_h + 1;
   const int ww = (p.btile_w + 2 * p.bhalo + 1 + d.stride_w - 1) / d.stride_w + 1;
   p.list_cap = s.taps * std::min(wh, s.ho) * std::min(ww, s.wo);
-  // offset-weight backward: (image, channel slice, row band) workgroups, two
-  // per CU (one where a launch covers more than 32 offset channels); a band's
-  // input rows are staged at once.  The band count minimises the staged rows
-  // per workgroup times the rounds of workgroups the chip runs, the fewest
-  // bands among equals (each band adds a dW_off partial to the reduction).
+  // offset-weight backward: (image, channel slice, row band) workgroups, four
+  // per CU in the bf16-operand form, else two (one where a launch covers
+  // more than 32 offset channels); a band's input rows are staged at once.
+  // The band count minimises an estimate of the launch plus the reduction of
+  // its partials: the staged rows per workgroup times the rounds of
+  // workgroups (fractional past the first), plus the partials' bytes at about
+  // 4.5 TB/s, counted in the same unit (a staged row takes about 2.8 us per
+  // round); the fewest bands among equals.
   const int slices = (d.c_in + 31) / 32;
   const int kc = d.dtype == DEFT_BF16 ? 16 : 8;
   const int wop = (s.wo + kc - 1) / kc * kc;
@@ -171,15 +174,17 @@ bool layout_backward(deft_plan& p) {
     // bf16 reads its dOffset operand from global memory; fp32 stages it too
     return align16(32 * xr * xs * s.esz) + (d.dtype == DEFT_BF16 ? 0 : mbw * 32 * rows * (wop + vec) * s.esz);
   };
-  const long slots = (long)std::max(1, p.cus) * (mbw == 1 ? 2 : 1);
+  const int per_cu = deft::woff_a16(d.dtype, s.oc, s.wo) ? 4 : (mbw == 1 ? 2 : 1);
+  const long slots = (long)std::max(1, p.cus) * per_cu;
   int bands = 0;
-  long best = 0;
+  double best = 0.0;
   for (int nb = 1; nb <= s.ho; ++nb) {
     const int rows = (s.ho + nb - 1) / nb;
-    if (woff_lds(rows) > p.max_lds / 2) continue;
-    const long rounds = ((long)d.n * slices * nb + slots - 1) / slots;
-    const long cost = rounds * ((rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1);
-    if (!bands || cost < best) { bands = nb; best = cost; }
+    if (woff_lds(rows) > p.max_lds / std::max(2, per_cu)) continue;
+    const double rounds = std::max(1.0, (double)d.n * slices * nb / (double)slots);
+    const double partials = (double)d.n * nb * s.oc * s.ck * 4;
+    const double cost = rounds * ((rows - 1) * d.stride_h + (d.kh - 1) * d.dil_h + 1) + partials / 12.6e6;
+    if (!bands || cost < best - 1e-9) { bands = nb; best = cost; }
   }
   if (!bands) bands = s.ho;
   // the offset-weight backward stages whole input rows: a band of the rows
@@ -272,6 +277,8 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   p.ws_dcol = o; o = align256(o + P * s.ck * s.esz);
   p.ws_dx32 = o; o = align256(o + (size_t)d.n * d.c_in * d.h * d.w * 4);
   p.ws_doff = o; o = align256(o + P * s.oc * 4);
+  // bf16: dOffset rounded once more, as the offset-weight backward reads it
+  p.ws_doff16 = o; if (d.dtype == DEFT_BF16) o = align256(o + P * s.oc * 2);
   p.ws_list = o;
   o = align256(o + (size_t)p.num_btiles * d.offset_groups * p.list_cap * 16);
   p.ws_lcount = o; o = align256(o + (size_t)p.num_btiles * d.offset_groups * 4);

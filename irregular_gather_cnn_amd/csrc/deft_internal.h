@@ -27,7 +27,7 @@ struct deft_plan {
   double est_miss;
   // workspace layout (byte offsets, 256-aligned)
   size_t ws_wt, ws_woff, ws_cols, ws_xh, ws_fwd_end;
-  size_t ws_w2, ws_dcol, ws_dx32, ws_doff, ws_wofft, ws_train_end;
+  size_t ws_w2, ws_dcol, ws_dx32, ws_doff, ws_doff16, ws_wofft, ws_train_end;
   int kk_pad;                  // padded (o, tap) depth of the transposed offset conv
   // sampling backward: each workgroup owns a core tile of input pixels
   // (btile_h x btile_w) and the (output pixel, tap) pairs that touch it
@@ -46,6 +46,11 @@ struct deft_plan {
 };
 
 namespace deft {
+
+// The offset-weight backward's form with its dOffset operand in bf16 pieces
+// (four workgroups per CU): bf16, at most 32 offset channels, output rows a
+// multiple of 8 pixels.
+inline bool woff_a16(int dtype, int oc, int wo) { return dtype == DEFT_BF16 && oc <= 32 && wo % 8 == 0; }
 
 // Records a HIP error for deft_last_hip_error and returns DEFT_ERR_HIP.
 int report_hip_error(hipError_t e);
