@@ -195,14 +195,16 @@ bool layout_backward(deft_plan& p) {
 }
 
 // The direct-gather forward (corners from a channel-minor copy of x) needs
-// bf16, at most 9 taps (one block of offset channels, at most three units
-// per wave and chunk), a power-of-two number of 8-channel slices per group
-// (at most 256) and byte offsets below 2^31 within one image's copy.
+// at most 9 taps (one block of offset channels, at most three units per wave
+// and chunk), a power-of-two number of 16-byte channel slices per group (8
+// bf16 or 4 fp32 channels; at most 256) and byte offsets below 2^31 within
+// one image's copy.
 bool direct_ok(const deft_desc& d) {
   const Shape s = shape_of(d);
-  const int nv = s.cg / 8;
-  return d.dtype == DEFT_BF16 && d.c_in % 16 == 0 && s.taps <= 9 && nv >= 1 && nv <= 256 &&
-         (nv & (nv - 1)) == 0 && ((size_t)d.h * d.w + 1) * d.c_in < 0x40000000u;
+  const int vec = d.dtype == DEFT_BF16 ? 8 : 4;
+  const int nv = s.cg / vec;
+  return d.c_in % 16 == 0 && s.cg % vec == 0 && s.taps <= 9 && nv >= 1 && nv <= 256 && (nv & (nv - 1)) == 0 &&
+         ((size_t)d.h * d.w + 1) * d.c_in * (d.dtype == DEFT_BF16 ? 2 : 4) < 0x80000000u;
 }
 
 // Fills every derived field of a plan for the given tile / halo / chunk
@@ -217,7 +219,11 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   p.ho = s.ho; p.wo = s.wo; p.taps = s.taps; p.oc = s.oc; p.cg = s.cg; p.ck = s.ck;
   p.tile_h = th; p.tile_w = tw; p.halo = halo; p.chunk = chunk;
   p.bhalo = bhalo < 0 ? halo : bhalo;
-  p.chunk_a = d.c_in % 64 == 0 ? 64 : (d.c_in % 32 == 0 ? 32 : 16);
+  // offset-conv chunk: at most four 16-byte k-steps per lane half (64 bf16
+  // or 32 fp32 channels), the same in every plan of a layer so its offsets
+  // are summed in one order
+  const int amax = d.dtype == DEFT_BF16 ? 64 : 32;
+  p.chunk_a = d.c_in % amax == 0 ? amax : (d.c_in % 32 == 0 ? 32 : 16);
   p.gw = 1;
   p.gsplit = d.offset_groups / p.gw;
   p.tiles_h = (s.ho + th - 1) / th;
@@ -244,7 +250,7 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
     // footprint staging (256 * stage_d 16-byte slots per buffer), the
     // phase-A partial sums and the tap table (int4 corner offsets, float4
     // weights, int column offset)
-    p.stage_d = (p.foot_h * p.foot_w * (p.chunk_a / 8) + 255) / 256;
+    p.stage_d = (p.foot_h * p.foot_w * (p.chunk_a / vec) + 255) / 256;
     if (p.stage_d > 7) return false;
     p.lds_off = 0;
     p.lds_info = align16(ocw * pt * 4);
@@ -418,8 +424,13 @@ int plan_auto(deft_plan& best, const deft_desc& d, const uint32_t* hist, int his
         const double busy = p.num_wg > 0 ? p.num_wg / (waves * slots) : 1.0;
         const double padded = (double)p.num_wg * th * tw;
         const double stage = (double)p.num_wg * p.foot_h * p.foot_w * d.c_in * s.esz;
+        // fewer than four workgroups resident per CU hide less latency (fp32
+        // on 64 x 64: 32-pixel tiles, four per CU, 58-61 us; 64-pixel tiles,
+        // two per CU, 66-68 us)
+        const double resident = std::min<double>(occ, std::ceil((double)p.num_wg / std::max(p.cus, 1)));
+        const double lat = 1.0 + 0.25 * (4.0 / std::max(resident, 1.0) - 1.0);
         const double cost =
-            (col_bytes * padded / std::max(valid, 1.0) + 0.25 * stage + (double)p.num_wg * 65536.0) /
+            lat * (col_bytes * padded / std::max(valid, 1.0) + 0.25 * stage + (double)p.num_wg * 65536.0) /
             std::max(busy, 0.05);
         if (cost < dbest * 0.999) {
           dbest = cost;

@@ -36,7 +36,7 @@ struct SampleParams {
   const float* off_in;
   float* off_out;
   void* cols;
-  const bf16_t* xh;  // direct path: x channel-minor [N][H*W+1][Cin], pixel H*W = 0
+  const void* xh;    // direct path: x channel-minor [N][H*W+1][Cin] (dtype), pixel H*W = 0
   int nv_log;        // direct path: log2(Cg / 8)
   int offsets_only;  // 1: stop after the offset convolution (offsets written to off_out)
   uint32_t* hist;    // nullable: the tile's required-halo histogram is added here
@@ -407,8 +407,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // ---------------------------------------------------------------------------
-// Direct-gather variant (bf16): the corners are read straight from a
-// channel-minor copy of the input (one 16-byte load = 8 channels of one
+// Direct-gather variant: the corners are read straight from a channel-minor
+// copy of the input (one 16-byte load = 8 bf16 or 4 fp32 channels of one
 // corner), which stays resident in the L2s and the 256 MB Infinity Cache; no
 // input staging, no halo, no chunk loop and no barriers in the blend.  The
 // offset conv reads its MFMA operand fragments from the same copy.  Out-of-
@@ -416,8 +416,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // to zero without a special case.
 // MODE: kFusedMode (offset conv + sampling), kOffsetsMode (offset conv only,
 // offsets to off_out), kSampleMode (sampling from offsets read from off_in).
-template <int MB, int MODE>
+template <typename T, int MB, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_direct(const SampleParams p) {
+  constexpr int VEC = Elem<T>::VEC, ESZ = (int)sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   int4* tab = (int4*)(smem + p.lds_info);                                     // [PT][K2] corner byte offsets
   float4* wts = (float4*)(smem + p.lds_info + PT * p.K2 * 16);                // [PT][K2] corner weights
   int* cof = (int*)(smem + p.lds_info + PT * p.K2 * 32);                      // [PT][K2] column offset
-  const bf16_t* __restrict__ xn = p.xh + (size_t)n * (HW + 1) * p.Cin;
+  const T* __restrict__ xn = (const T*)p.xh + (size_t)n * (HW + 1) * p.Cin;
   const int fy0 = oh0 * p.SH - p.PH, fx0 = ow0 * p.SW - p.PW;
 
   if constexpr (MODE == kSampleMode) {
@@ -462,20 +463,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     // Same unit walk as the LDS-staged kernel (bit-identical offsets); a
-    // unit here is one batch (CA <= 64 channels: at most four k-steps).  The
+    // unit here is one batch (at most four k-steps: CA <= 64 bf16 or 32 fp32
+    // channels).  The
     // tile's footprint, one chunk of CA channels at a time, is copied from
     // the channel-minor input into LDS by direct buffer-to-LDS loads (whole
     // 16-byte pieces of contiguous pixel rows), double buffered; 16-byte
     // piece q of footprint pixel P sits in slot P * nq + (q ^ (P % nq)), so
     // the 32 pixels of an operand read hit distinct banks.  The weights come
     // in fragment order: one 1 KB contiguous load per k-step.
-    const int nks = p.CA / 16, nch = p.Cin / p.CA, nq = p.CA / 8;
+    const int nks = p.CA / (2 * VEC), nch = p.Cin / p.CA, nq = p.CA / VEC;
     const int nslot = p.FH * p.FW * nq;
     const int D = p.stage_d;
     unsigned char* stg = smem + p.lds_region;  // [2][D * 256 slots][16 B]
-    const rsrc_t xr = make_rsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * 2));
+    const rsrc_t xr = make_rsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * ESZ));
     const bool nb1 = PT > 32;
-    const bf16_t* __restrict__ wf = (const bf16_t*)p.woff_p + (size_t)g * p.K2 * p.Cin * 32 + lane * 8;
+    const T* __restrict__ wf = (const T*)p.woff_p + (size_t)g * p.K2 * p.Cin * 32 + lane * VEC;
     int pixb[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
           const int fy = fdiv(P, p.div_fw), fx = P - fy * p.FW;
           const int y = fy0 + fy, xx = fx0 + fx;
           const int pix = ((unsigned)y < (unsigned)p.H && (unsigned)xx < (unsigned)p.W) ? y * p.W + xx : HW;
-          voff = (pix * p.Cin + c * p.CA + q * 8) * 2;
+          voff = (pix * p.Cin + c * p.CA + q * VEC) * ESZ;
         }
         load_lds16(xr, b + s0 * 16, voff);
       }
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
           tl[u] = uw.t; nu = u + 1;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(uw.t * nch + c) * nks + k) * 512);
+            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(uw.t * nch + c) * nks + k) * (64 * VEC));
           uw.next(p.K2, nks);
         }
       }
@@ -550,14 +552,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
               if (nb == 1 && !nb1) break;
               const int P = pixb[nb] + toff;
               const uint4 bq = *(const uint4*)(b + (P * nq + (q ^ (P & (nq - 1)))) * 16);
-              mfma_chunk(acc[0][nb], wa[u][k], bq, bf16_t());
+              mfma_chunk(acc[0][nb], wa[u][k], bq, T());
             }
           }
         }
         if (u < nn) {
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(tn[u] * nch + c + 1) * nks + k) * 512);
+            if (k < nks) wa[u][k] = *(const uint4*)(wf + ((size_t)(tn[u] * nch + c + 1) * nks + k) * (64 * VEC));
         }
       }
 #pragma unroll
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       float v = part[e] + part[tot + e];
       v += part[2 * tot + e];
       v += part[3 * tot + e];
-      if (p.b_off) v += bf16_to_f32(((const bf16_t*)p.b_off)[obase + o]);
+      if (p.b_off) v += Elem<T>::to_f32(((const T*)p.b_off)[obase + o]);
       off_l[e] = v;
       const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
       if (p.off_out && ty < thn && tx < twn)
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // A corner outside the image (and every corner of a fully outside tap)
   // points at the copy's zero pixel; -1 marks a pixel beyond the tile.
   const int nent = PT * p.K2;
-  const int zpix = HW * p.Cin * 2;
+  const int zpix = HW * p.Cin * ESZ;
   for (int e = tid; e < nent; e += 256) {
     const int pix = fdiv(e, p.div_k2), t = e - pix * p.K2;
     const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const TapIndex ix = tap_index(by, bx, dy, dx, p.H, p.W);
       co = (ty * p.Wo + tx) * p.Ck + t * p.Cin;
       if (!ix.outside) {
-        const int b = (ix.y0 * p.W + ix.x0) * p.Cin * 2, cw1 = p.Cin * 2, cwW = p.W * p.Cin * 2;
+        const int b = (ix.y0 * p.W + ix.x0) * p.Cin * ESZ, cw1 = p.Cin * ESZ, cwW = p.W * p.Cin * ESZ;
         const uint32_t m = corner_mask(ix, p.H, p.W);
         tb.x = (m & 1) ? b : zpix;
         tb.y = (m & 2) ? b + cw1 : zpix;
@@ -639,14 +641,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
   __syncthreads();
 
-  // ---- phase B: every (pixel, tap) x 8 channels, corners from the copy ----
+  // ---- phase B: every (pixel, tap) x 16 bytes of channels, corners from the copy ----
   // 32-bit buffer offsets: the table's corner offset plus the lane's channels.
   const int nvm = (1 << p.nv_log) - 1;
   const int v = tid & nvm, e0 = tid >> p.nv_log, estep = 256 >> p.nv_log;
-  const int cofs = g * p.Cg + v * 8;
-  const __amdgpu_buffer_rsrc_t xb = make_brsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * 2));
-  const int lofs = cofs * 2;
-  bf16_t* __restrict__ colt = (bf16_t*)p.cols + ((size_t)n * p.Ho * p.Wo + (size_t)oh0 * p.Wo + ow0) * p.Ck + cofs;
+  const int cofs = g * p.Cg + v * VEC;
+  const __amdgpu_buffer_rsrc_t xb = make_brsrc(xn, (uint32_t)((size_t)(HW + 1) * p.Cin * ESZ));
+  const int lofs = cofs * ESZ;
+  T* __restrict__ colt = (T*)p.cols + ((size_t)n * p.Ho * p.Wo + (size_t)oh0 * p.Wo + ow0) * p.Ck + cofs;
   for (int e = e0; e < nent; e += 2 * estep) {
     int co[2];
     float w[2][4];
@@ -667,14 +669,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (co[u] < 0) continue;
-      float f00[8], f01[8], f10[8], f11[8], o8[8];
-      unpack8(q[u][0], f00);
-      unpack8(q[u][1], f01);
-      unpack8(q[u][2], f10);
-      unpack8(q[u][3], f11);
+      if constexpr (VEC == 8) {
+        float f00[8], f01[8], f10[8], f11[8], o8[8];
+        unpack8(q[u][0], f00);
+        unpack8(q[u][1], f01);
+        unpack8(q[u][2], f10);
+        unpack8(q[u][3], f11);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o8[c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
-      store8_nt(colt + co[u], o8);
+        for (int c = 0; c < 8; ++c) o8[c] = blend4(w[u], f00[c], f01[c], f10[c], f11[c]);
+        store8_nt((bf16_t*)(colt + co[u]), o8);
+      } else {
+        auto bl = [&](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+          return __float_as_uint(
+              blend4(w[u], __uint_as_float(a), __uint_as_float(b), __uint_as_float(c), __uint_as_float(d)));
+        };
+        const uint4 o4 = make_uint4(bl(q[u][0].x, q[u][1].x, q[u][2].x, q[u][3].x),
+                                    bl(q[u][0].y, q[u][1].y, q[u][2].y, q[u][3].y),
+                                    bl(q[u][0].z, q[u][1].z, q[u][2].z, q[u][3].z),
+                                    bl(q[u][0].w, q[u][1].w, q[u][2].w, q[u][3].w));
+        store16_nt(colt + co[u], o4);
+      }
     }
   }
 }
@@ -720,6 +734,55 @@ __device__ __forceinline__ void x_channel_minor_body(int bid, const bf16_t* __re
     o.z = __builtin_amdgcn_perm(dw(rv[5]), dw(rv[4]), sel);
     o.w = __builtin_amdgcn_perm(dw(rv[7]), dw(rv[6]), sel);
     if (p0 + i <= HW) *(uint4*)(dst + (size_t)i * Cin) = o;
+  }
+}
+
+// fp32: x [N][Cin][H*W] -> xh [N][H*W+1][Cin], pixel H*W of every image
+// zero.  One workgroup moves a 64-channel x 64-pixel tile through LDS: loads
+// of 16 consecutive pixels x 4 per lane group (256-byte runs along the
+// pixels), stores of 16 channel quads (256-byte runs along the channels); the
+// LDS rows hold 65 floats, so both the scalar writes and the transposed
+// reads hit 64 distinct banks.
+__global__ __launch_bounds__(256) void k_x_channel_minor_f32(const float* __restrict__ x, float* __restrict__ xh,
+                                                             int Cin, int HW, int pblocks, int cblocks) {
+  __shared__ float tl[64 * 65];
+  const int t = threadIdx.x;
+  const int b = blockIdx.x;
+  const int cb = b % cblocks, r = b / cblocks;
+  const int pb = r % pblocks, n = r / pblocks;
+  const int c0 = cb * 64, p0 = pb * 64;
+  const float* src = x + (size_t)n * Cin * HW;
+  const bool vec = (HW & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = (t >> 4) + 16 * i, pq = (t & 15) * 4;
+    const int c = c0 + ci, p = p0 + pq;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < Cin) {
+      const float* row = src + (size_t)c * HW;
+      if (vec && p + 4 <= HW) {
+        v = *(const float4*)(row + p);
+      } else {
+        v.x = p < HW ? row[p] : 0.f;
+        v.y = p + 1 < HW ? row[p + 1] : 0.f;
+        v.z = p + 2 < HW ? row[p + 2] : 0.f;
+        v.w = p + 3 < HW ? row[p + 3] : 0.f;
+      }
+    }
+    tl[ci * 65 + pq] = v.x;
+    tl[ci * 65 + pq + 1] = v.y;
+    tl[ci * 65 + pq + 2] = v.z;
+    tl[ci * 65 + pq + 3] = v.w;
+  }
+  __syncthreads();
+  float* dst = xh + (size_t)n * (HW + 1) * Cin;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pi = (t >> 4) + 16 * i, cq = (t & 15) * 4;
+    const int p = p0 + pi, c = c0 + cq;
+    if (p > HW || c >= Cin) continue;
+    const float4 v = make_float4(tl[cq * 65 + pi], tl[(cq + 1) * 65 + pi], tl[(cq + 2) * 65 + pi], tl[(cq + 3) * 65 + pi]);
+    *(float4*)(dst + (size_t)p * Cin + c) = v;
   }
 }
 
@@ -796,14 +859,16 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
 // direct kernel's fragment order: per group, tap, chunk of CA channels and
 // k-step, the 64 lanes' 16-byte A operands back to back (lane L: offset
 // channel L % 32 of the group, zero past 2 * taps; channels
-// chunk * CA + (L / 32) * CA / 2 + step * 8 ... + 7).
+// chunk * CA + (L / 32) * CA / 2 + step * V ... + V - 1, V = 8 bf16 or 4
+// fp32 elements per 16 bytes).
 template <typename T>
 __device__ __forceinline__ void prep_forward_body(int bid, int nblocks, const T* __restrict__ w,
                                                   const T* __restrict__ w_off, T* wt, T* woff_p, int Cout, int Cin,
                                                   int K2, int Oc, int OcP, int G, int CA) {
   const size_t n1 = (size_t)Cout * K2 * Cin;
   const size_t n2 = CA > 0 ? (size_t)G * K2 * Cin * 32 : (size_t)OcP * K2 * Cin;
-  const int nks = CA / 16, nch = CA > 0 ? Cin / CA : 1;
+  constexpr int V = Elem<T>::VEC, LV = V == 8 ? 3 : 2;
+  const int nks = CA / (2 * V), nch = CA > 0 ? Cin / CA : 1;
   for (size_t e = (size_t)bid * 256 + threadIdx.x; e < n1 + n2; e += (size_t)nblocks * 256) {
     // weight tensors are far below 2^31 elements: 32-bit index arithmetic
     if (e < n1) {
@@ -813,14 +878,14 @@ __device__ __forceinline__ void prep_forward_body(int bid, int nblocks, const T*
       wt[e] = w[(co * Cin + c) * K2 + t];
     } else if (CA > 0) {
       const int f = (int)(e - n1);
-      const int e8 = f & 7, L = (f >> 3) & 63;
-      int r = f >> 9;
+      const int e8 = f & (V - 1), L = (f >> LV) & 63;
+      int r = f >> (LV + 6);
       const int k = r % nks; r /= nks;
       const int ch = r % nch; r /= nch;
       const int t = r % K2;
       const int g = r / K2;
       const int ol = L & 31;
-      const int c = ch * CA + (L >> 5) * (CA / 2) + k * 8 + e8;
+      const int c = ch * CA + (L >> 5) * (CA / 2) + k * V + e8;
       woff_p[f] = ol < 2 * K2 ? w_off[((2 * g * K2 + ol) * Cin + c) * K2 + t] : zero_elem<T>();
     } else {
       const int f = (int)(e - n1);
@@ -904,9 +969,9 @@ static hipError_t launch_sample_dt(const deft_plan& p, SampleMode mode, const Sa
   }
 }
 
-template <int MODE>
+template <typename T, int MODE>
 static hipError_t launch_direct_t(const deft_plan& p, const SampleParams& s, const char* name, hipStream_t st) {
-  auto kern = k_sample_direct<1, MODE>;
+  auto kern = k_sample_direct<T, 1, MODE>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
   if (e != hipSuccess) return e;
   DEFT_LAUNCH(name, kern, dim3(p.num_wg), dim3(256), p.lds_total, st, s);
@@ -919,15 +984,22 @@ hipError_t launch_sample(const deft_plan& p, SampleMode mode, const SampleArgs& 
   if (p.num_wg == 0) return hipSuccess;
   if (p.direct && a.xh) {
     // the gather from the channel-minor copy (built by the prologue launch)
-    s.xh = (const bf16_t*)a.xh;
+    s.xh = a.xh;
+    const bool bf = p.d.dtype == DEFT_BF16;
     int l = 0;
-    while ((1 << l) < p.cg / 8) ++l;
+    while ((1 << l) < p.cg / (bf ? 8 : 4)) ++l;
     s.nv_log = l;
     if (p.mblocks != 1) return hipErrorInvalidValue;
     switch (mode) {
-      case kFusedMode: return launch_direct_t<kFusedMode>(p, s, "fused_offset_sample", st);
-      case kOffsetsMode: return launch_direct_t<kOffsetsMode>(p, s, "offset_conv", st);
-      default: return launch_direct_t<kSampleMode>(p, s, "sample_only", st);
+      case kFusedMode:
+        return bf ? launch_direct_t<bf16_t, kFusedMode>(p, s, "fused_offset_sample", st)
+                  : launch_direct_t<float, kFusedMode>(p, s, "fused_offset_sample", st);
+      case kOffsetsMode:
+        return bf ? launch_direct_t<bf16_t, kOffsetsMode>(p, s, "offset_conv", st)
+                  : launch_direct_t<float, kOffsetsMode>(p, s, "offset_conv", st);
+      default:
+        return bf ? launch_direct_t<bf16_t, kSampleMode>(p, s, "sample_only", st)
+                  : launch_direct_t<float, kSampleMode>(p, s, "sample_only", st);
     }
   }
   return p.d.dtype == DEFT_BF16 ? launch_sample_dt<bf16_t>(p, mode, s, st)
@@ -978,6 +1050,17 @@ hipError_t launch_prep_forward(const deft_plan& p, const void* w, const void* w_
                        (ca ? (size_t)d.offset_groups * p.taps * d.c_in * 32 : (size_t)p.oc_pad * p.taps * d.c_in);
   unsigned g = grid_for(total);
   if (g > 4096) g = 4096;
+  if (p.direct && d.dtype != DEFT_BF16) {
+    // fp32: the channel-minor copy, then the weights (offset conv in fragment order)
+    const int HW = d.h * d.w;
+    const int pblocks = (HW + 1 + 63) / 64, cblocks = (d.c_in + 63) / 64;
+    DEFT_LAUNCH("x_channel_minor", k_x_channel_minor_f32, dim3(d.n * pblocks * cblocks), dim3(256), 0, st,
+                (const float*)x, (float*)xh, d.c_in, HW, pblocks, cblocks);
+    DEFT_LAUNCH("prep_forward", k_prep_forward<float>, dim3(g), dim3(256), 0, st, (const float*)w,
+                (const float*)w_off, (float*)wt, (float*)woff_p, d.c_out, d.c_in, p.taps, p.oc, p.oc_pad,
+                d.offset_groups, ca);
+    return hipGetLastError();
+  }
   if (p.direct) {
     const int HW = d.h * d.w;
     const int pgroups = (HW + 1 + 63) / 64, cgroups = (d.c_in + 63) / 64;
