@@ -197,8 +197,7 @@ def test_fused_equals_unfused_and_plan_invariance(name):
     t = {k: dev(v, wl.dtype) for k, v in inp.items()}
     ref = None
     plans = [None, (8, 8, 0, 16), (4, 16, 3, 32), (2, 8, 1, 0), (8, 8, 12, 0)]
-    if wl.dtype == "bf16":
-        plans += [(8, 8, 4, -1), (3, 7, 2, -1)]  # direct gather from the channel-minor copy
+    plans += [(8, 8, 4, -1), (3, 7, 2, -1)]  # direct gather from the channel-minor copy
     for plan in plans:
         say("plan", name, plan)
         layer = make_layer(wl, plan=plan)
