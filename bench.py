@@ -377,6 +377,19 @@ def main():
                                                                                           "gather_direct")}}
             if train_ms_o is not None:
                 rec["fwd_bwd_ms"] = round(train_ms_o, 4)
+            pro = [sum(v) / len(v) for k, v in oper.items() if k in ("x_channel_minor", "prep_forward")]
+            if pro:
+                rec["prologue_us"] = round(sum(pro) * 1e3, 1)
+            if not owl.train:
+                # the pages' staging (tile + halo of the input in LDS) on the same
+                # inputs, for comparison with the planned direct gather
+                try:
+                    lh = DeformConv(**ogeo, plan=(8, 8, max(1, olayer.info["halo"]), 32), training=False, device=dev)
+                    lh_fn = lambda: lh.forward(ot["x"], ot["w_off"], ot["b_off"], ot["w"], ot["b"], y=oy)
+                    rec["lds_halo_fwd_ms"] = round(time_forward(lh_fn), 4)
+                    del lh
+                except L.DeftError:
+                    pass
             for kname in ("fused_offset_sample", "gemm_forward"):
                 if kname in oper:
                     avg = sum(oper[kname]) / len(oper[kname])

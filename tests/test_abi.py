@@ -143,16 +143,17 @@ def test_forced_plan_limits():
 
 def test_direct_gather_selection():
     """The planner takes the direct-gather forward exactly where it applies:
-    bf16, at most 9 taps, a power-of-two number of 8-channel slices per
-    offset group; the forced plan's chunk -1 asks for it and is refused
-    elsewhere.  The direct variant's workspace holds the channel-minor copy
-    of x (one extra zero pixel per image)."""
+    at most 9 taps, a power-of-two number of 16-byte channel slices per
+    offset group (8 bf16 or 4 fp32 channels); the forced plan's chunk -1 asks
+    for it and is refused elsewhere.  The direct variant's workspace holds
+    the channel-minor copy of x (one extra zero pixel per image)."""
     def info(**kw):
         return L.deft_plan_get_info(L.deft_plan_create(desc(**kw)))
     assert info(n=2, c_in=32, dtype=L.DEFT_BF16)["gather_direct"] == 1
-    assert info(n=2, c_in=32, dtype=L.DEFT_F32)["gather_direct"] == 0
+    assert info(n=2, c_in=32, dtype=L.DEFT_F32)["gather_direct"] == 1  # 8 slices of 4 channels
     assert info(n=2, c_in=32, kh=5, kw=5, pad=(2, 2), dtype=L.DEFT_BF16)["gather_direct"] == 0
     assert info(n=2, c_in=48, dtype=L.DEFT_BF16)["gather_direct"] == 0  # 6 slices of 8 channels
+    assert info(n=2, c_in=48, dtype=L.DEFT_F32)["gather_direct"] == 0  # 12 slices of 4 channels
     assert info(n=2, c_in=64, groups=4, dtype=L.DEFT_BF16)["gather_direct"] == 1  # 2 slices per group
     dd = desc(n=2, c_in=32, dtype=L.DEFT_BF16)
     halo_plan = L.deft_plan_get_info(L.deft_plan_create_forced(dd, 8, 8, 2, 32))
@@ -160,7 +161,7 @@ def test_direct_gather_selection():
     assert halo_plan["gather_direct"] == 0 and direct_plan["gather_direct"] == 1
     copy_bytes = 2 * (9 * 11 + 1) * 32 * 2
     assert direct_plan["ws_forward"] >= halo_plan["ws_forward"] + copy_bytes - 256
-    for bad in (desc(n=2, c_in=32, dtype=L.DEFT_F32), desc(n=2, c_in=48, dtype=L.DEFT_BF16)):
+    for bad in (desc(n=2, c_in=48, dtype=L.DEFT_F32), desc(n=2, c_in=48, dtype=L.DEFT_BF16)):
         with pytest.raises(L.DeftError) as e:
             L.deft_plan_create_forced(bad, 8, 8, 2, -1)
         assert e.value.code == -9
