@@ -129,8 +129,9 @@ int deft_plan_create(const deft_desc* d, const uint32_t* halo_hist, int hist_len
 /* Plan with a forced tile (tile_h*tile_w <= 64), halo (0..32) and channel
  * chunk (multiple of 16 dividing Cin/G, at most 64; 0 = largest that fits;
  * -1 = direct gather: the forward reads the corners from a channel-minor copy
- * of x instead of an LDS halo, bf16 only, Cin/(8G) a power of two <= 256;
- * -2 = direct gather fused into the main GEMM, which also needs Cin/G and
+ * of x instead of an LDS halo; Cin a multiple of 16, at most 9 taps, and
+ * Cin/(vG) a power of two <= 256 with v = 8 (bf16) or 4 (fp32) channels per
+ * 16 bytes; -2 = direct gather fused into the main GEMM (bf16), which also needs Cin/G and
  * Cin multiples of 32, Ho*Wo and c_out multiples of 8).
  * DEFT_ERR_PLAN if its LDS does not fit or the direct gather is unsupported; deft_backward returns DEFT_ERR_PLAN
  * for a forced plan whose backward tile does not fit even with 8 channels.
