@@ -35,10 +35,10 @@ _CSRC = os.path.join(_HERE, "csrc")
 # benchmark name of a launch -> (pattern of the kernel symbol, source files of the kernel)
 KERNELS = {
     "x_channel_minor": (r"k_x_channel_minor", ["deft_sample.hip"]),
-    "fused_offset_sample": (r"k_sample_direct<1, 0>", ["deft_sample.hip", "deft_device.h"]),
+    "fused_offset_sample": (r"k_sample_direct<[^,>]*, 1, 0>", ["deft_sample.hip", "deft_device.h"]),
     "fused_offset_sample_lds_halo": (r"k_sample<[^>]*, true", ["deft_sample.hip", "deft_device.h"]),
-    "offset_conv": (r"k_sample_direct<1, 1>", ["deft_sample.hip", "deft_device.h"]),
-    "sample_only": (r"k_sample_direct<1, 2>", ["deft_sample.hip", "deft_device.h"]),
+    "offset_conv": (r"k_sample_direct<[^,>]*, 1, 1>", ["deft_sample.hip", "deft_device.h"]),
+    "sample_only": (r"k_sample_direct<[^,>]*, 1, 2>", ["deft_sample.hip", "deft_device.h"]),
     "sample_only_lds_halo": (r"k_sample<[^>]*, false", ["deft_sample.hip", "deft_device.h"]),
     "fused_gather_gemm": (r"k_igemm\b", ["deft_igemm.hip", "deft_device.h"]),
     "dwconv1d": (r"k_dwconv1d\b", ["deft_dwconv.hip"]),
