@@ -4,8 +4,9 @@ Tolerances (rel-L2 per output tensor): 1e-5 for fp32 workloads, 2e-2 for bf16
 inputs with fp32 accumulation; the integer tap-index / corner-mask stage is
 bit-exact; forward results are bit-identical across plans and between the
 fused and the unfused sampling paths.  The oracle always receives the same
-(bf16-rounded) input values; where a check isolates a later stage it also
-receives the GPU's fp32 offsets, so offset rounding does not blur it.
+(bf16-rounded) input values and never a value the GPU computed: backward
+checks give it the offsets of its own forward, and the check that isolates
+the sampling gives both sides the oracle's offsets rounded to fp32.
 """
 import numpy as np
 import pytest
@@ -56,6 +57,13 @@ def cols_to_oracle_layout(cols, wl):
     return np.transpose(cols, (0, 1, 3, 2))
 
 
+def oracle_offsets(s, inp, sl=slice(None)):
+    """The oracle's own forward offsets (fp64) of the images in ``sl``: the
+    backward's expected values are computed from them, so nothing of the
+    GPU's forward enters the oracle."""
+    return oracle.forward(s, inp["x"][sl], inp["w_off"], inp["b_off"], inp["w"], inp["b"])[1]
+
+
 def image_shape(wl, n):
     return oracle.Shape(n, wl.c_in, wl.h, wl.w, wl.c_out, wl.kh, wl.kw, (wl.stride,) * 2, (wl.pad,) * 2,
                         (wl.dil,) * 2, wl.groups)
@@ -74,21 +82,29 @@ def test_forward_matches_oracle(name):
     t = {k: dev(v, wl.dtype) for k, v in inp.items()}
     layer = make_layer(wl)
     y, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
-    cols = layer.cols_view()
     torch.cuda.synchronize()
     # images checked against the oracle: all for small workloads, first/last otherwise
     imgs = list(range(wl.n)) if wl.n * wl.c_in * wl.h * wl.w <= 8 * 128 * 64 * 64 else [0, wl.n - 1]
     s1 = image_shape(wl, 1)
     y_h, off_h = host(y), host(off)
-    cols_h = host(cols)
     tol = TOL[wl.dtype]
+    # the oracle's offsets of the checked images, rounded to fp32 (the offsets'
+    # storage type), given to the GPU's sampling from stored offsets, so the
+    # columns are compared on the same sample points with nothing of the GPU's
+    # forward in the oracle's inputs
+    refs = {}
+    off32 = np.zeros(off_h.shape, np.float32)
+    for n in imgs:
+        refs[n] = oracle.forward(s1, inp["x"][n:n + 1], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+        off32[n:n + 1] = refs[n][1]
+    cols_h = host(layer.sample(t["x"], torch.from_numpy(off32).cuda()))
+    torch.cuda.synchronize()
     for n in imgs:
         xs = inp["x"][n:n + 1]
-        y_ref, off_ref = oracle.forward(s1, xs, inp["w_off"], inp["b_off"], inp["w"], inp["b"])
+        y_ref, off_ref = refs[n]
         e_off = rel(off_h[n:n + 1], off_ref)
         e_y = rel(y_h[n:n + 1], y_ref)
-        # columns from the GPU's own offsets, so only the sampling is compared
-        col_ref = oracle.sample_cols(s1, xs, off_h[n:n + 1].astype(np.float64))
+        col_ref = oracle.sample_cols(s1, xs, off32[n:n + 1].astype(np.float64))
         e_col = rel(cols_to_oracle_layout(cols_h[n:n + 1], wl), col_ref)
         say("  image %d: rel offsets %.2e cols %.2e y %.2e" % (n, e_off, e_col, e_y))
         assert e_off <= 1e-5
@@ -127,17 +143,17 @@ def test_forward_gemm_row_shares(n):
 
 @pytest.mark.parametrize("name", FWD)
 def test_index_stage_bit_exact(name):
-    """Tap index / corner mask from the GPU's own offsets equals the oracle's
-    fp32 index stage on the same offsets, element for element."""
+    """The GPU's tap index / corner mask equals the oracle's fp32 index stage,
+    element for element, on the same offsets: the oracle forward's, rounded
+    to fp32 (the offsets' storage type)."""
     wl = WORKLOADS[name]
     say("index bit-exact", name)
     inp = make_inputs(wl)
-    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
     layer = make_layer(wl)
-    _, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
-    y0, x0, m = index_stage(layer.desc, off, wl.groups, wl.taps, layer.ho, layer.wo, wl.n)
+    off32 = oracle_offsets(shape_of(wl), inp).astype(np.float32)
+    y0, x0, m = index_stage(layer.desc, torch.from_numpy(off32).cuda(), wl.groups, wl.taps, layer.ho, layer.wo, wl.n)
     torch.cuda.synchronize()
-    ry0, rx0, rm = oracle.sample_index_f32(shape_of(wl), host(off))
+    ry0, rx0, rm = oracle.sample_index_f32(shape_of(wl), off32)
     assert np.array_equal(host(y0), ry0)
     assert np.array_equal(host(x0), rx0)
     assert np.array_equal(host(m), rm)
@@ -281,7 +297,7 @@ def test_replanning_from_observed_offsets(dtype):
     say("  backward halo %d -> %d, replans %d" % (halo0, layer.info["bwd_halo"], layer.replans))
     assert layer.replans == 1 and layer.info["bwd_halo"] > halo0
     assert torch.equal(y1, y0_) and torch.equal(off1, off0)
-    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off1).astype(np.float64), inp["dy"])
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], oracle_offsets(shape_of(wl), inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -292,13 +308,12 @@ def test_halo_histogram_matches_index_stage():
     wl = WORKLOADS["bf16_n16_c512_28x28_g4_wide"]
     say("halo histogram")
     inp = make_inputs(wl)
-    t = {k: dev(v, wl.dtype) for k, v in inp.items()}
     layer = make_layer(wl)
-    _, off = layer.forward(t["x"], t["w_off"], t["b_off"], t["w"], t["b"], want_offsets=True)
-    hist = halo_histogram(layer.desc, off, 16)
-    torch.cuda.synchronize()
     s = shape_of(wl)
-    ry0, rx0, rm = oracle.sample_index_f32(s, host(off))
+    off32 = oracle_offsets(s, inp).astype(np.float32)  # the oracle forward's offsets, on both sides
+    hist = halo_histogram(layer.desc, torch.from_numpy(off32).cuda(), 16)
+    torch.cuda.synchronize()
+    ry0, rx0, rm = oracle.sample_index_f32(s, off32)
     by = (np.arange(s.ho) - s.pad[0])[None, None, None, :, None] + (np.arange(9) // 3)[None, None, :, None, None]
     bx = (np.arange(s.wo) - s.pad[1])[None, None, None, None, :] + (np.arange(9) % 3)[None, None, :, None, None]
     need = np.maximum(np.abs(ry0 - by), np.abs(rx0 - bx))
@@ -373,7 +388,7 @@ def test_backward_matches_oracle_small(case, dtype):
     say("backward small", dtype, case)
     inp, layer, y, off, g = run_backward(wl)
     s = shape_of(wl)
-    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], oracle_offsets(s, inp), inp["dy"])
     tol = TOL[dtype]
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
@@ -394,7 +409,7 @@ def test_backward_small_halo_misses(plan, dtype):
     say("backward small halo", dtype, plan)
     inp, layer, y, off, g = run_backward(wl, plan=plan)
     s = shape_of(wl)
-    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], oracle_offsets(s, inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -414,7 +429,7 @@ def test_backward_halo_planned_apart_from_forward(dtype):
     inp, layer, y, off, g = run_backward(wl, plan=hist)
     say("  forward halo %d, backward halo %d" % (layer.info["halo"], layer.info["bwd_halo"]))
     assert layer.info["bwd_halo"] == 1
-    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], oracle_offsets(shape_of(wl), inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -444,7 +459,7 @@ def test_backward_bf16_direct_gemm(case):
     s = shape_of(wl)
     y_ref, _ = oracle.forward(s, inp["x"], inp["w_off"], inp["b_off"], inp["w"], inp["b"])
     assert rel(host(y), y_ref) <= TOL["bf16"]
-    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(s, inp["x"], inp["w_off"], inp["w"], oracle_offsets(s, inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -500,7 +515,7 @@ def test_backward_after_gather_fused_gemm_forward():
     say("backward after gather-fused GEMM forward")
     inp, layer, y, off, g = run_backward(wl, plan=(7, 7, 2, -2))
     assert layer.info["gather_gemm"] == 1
-    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], oracle_offsets(shape_of(wl), inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -520,7 +535,7 @@ def test_backward_after_unfused_forward(dtype):
     g3 = layer.backward(t["x"], t["w_off"], t["w"], off3, t["dy"])
     torch.cuda.synchronize()
     assert torch.equal(y3, y) and torch.equal(off3, off)
-    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+    ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], oracle_offsets(shape_of(wl), inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         e = rel(host(g3[k]), ref[k])
         say("  %s rel %.2e" % (k, e))
@@ -548,14 +563,13 @@ def test_training_step_full_size(name):
     wl = WORKLOADS[name]
     say("training step full size", name)
     inp, layer, y, off, g = run_backward(wl)
-    off_h = host(off).astype(np.float64)
     s1 = image_shape(wl, 1)
     y_h = host(y)
     tol = TOL[wl.dtype]
     sums = {k: None for k in ("dw", "db", "dw_off", "db_off")}
     for n in range(wl.n):
         sl = slice(n, n + 1)
-        ref = oracle.backward(s1, inp["x"][sl], inp["w_off"], inp["w"], off_h[sl], inp["dy"][sl])
+        ref = oracle.backward(s1, inp["x"][sl], inp["w_off"], inp["w"], oracle_offsets(s1, inp, sl), inp["dy"][sl])
         say("  oracle image %d done" % n)
         for k in sums:
             sums[k] = ref[k] if sums[k] is None else sums[k] + ref[k]
@@ -592,7 +606,7 @@ def test_nonfinite_dy_reaches_the_gradients(dtype, bad):
     g = layer.backward(t["x"], t["w_off"], t["w"], off, t["dy"])
     torch.cuda.synchronize()
     with np.errstate(invalid="ignore", over="ignore"):
-        ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], host(off).astype(np.float64), inp["dy"])
+        ref = oracle.backward(shape_of(wl), inp["x"], inp["w_off"], inp["w"], oracle_offsets(shape_of(wl), inp), inp["dy"])
     for k in ("dx", "dw_off", "db_off", "dw", "db"):
         a, b = host(g[k]).astype(np.float64), np.asarray(ref[k], np.float64)
         say("  %s: %d NaN / %d inf (oracle %d / %d)" % (k, np.isnan(a).sum(), np.isinf(a).sum(), np.isnan(b).sum(),
