@@ -455,6 +455,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     __syncthreads();
   } else {
   // ---- phase A: offsets of this tile, operand fragments from the copy ----
+    // The offset-conv bias of this thread's elements of the reduction below
+    // (at most four: e = tid + 256 k < ocw * PT <= 1152), loaded now so the
+    // reduction does not wait on them.
+    const int tot = ocw * PT;
+    float bias4[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int e = tid + 256 * k;
+      bias4[k] = p.b_off && e < tot ? Elem<T>::to_f32(((const T*)p.b_off)[obase + e / PT]) : 0.f;
+    }
     f32x16_t acc[MB][2];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -532,12 +542,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       int tlc[3];
 #pragma unroll
       for (int u = 0; u < 3; ++u) tlc[u] = tl[u];
-      // next chunk's units (same count pattern; loaded per unit below)
+      // next chunk's units (same count pattern; loaded per unit below);
+      // none after the last chunk
       UnitWalk un = uw;
       int tn[3], nn = 0;
 #pragma unroll
       for (int u = 0; u < 3; ++u)
-        if (un.c == c + 1) { tn[u] = un.t; nn = u + 1; un.next(p.K2, nks); }
+        if (un.c == c + 1 && c + 1 < nch) { tn[u] = un.t; nn = u + 1; un.next(p.K2, nks); }
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         if (u < nuc) {
@@ -579,13 +590,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
           if (row < ocw && col < PT) part[(wave * ocw + row) * PT + col] = acc[mb][nb][r];
         }
     __syncthreads();
-    const int tot = ocw * PT;
-    for (int e = tid; e < tot; e += 256) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int e = tid + 256 * k;
+      if (e >= tot) break;
       const int o = e / PT, pix = e - o * PT;
       float v = part[e] + part[tot + e];
       v += part[2 * tot + e];
       v += part[3 * tot + e];
-      if (p.b_off) v += Elem<T>::to_f32(((const T*)p.b_off)[obase + o]);
+      v += bias4[k];
       off_l[e] = v;
       const int ty = fdiv(pix, p.div_tw), tx = pix - ty * p.TW;
       if (p.off_out && ty < thn && tx < twn)
