@@ -82,6 +82,27 @@ __device__ __forceinline__ float dot2_bf16(const uint4 a, const uint4 b, float a
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.w), __builtin_bit_cast(b2_t, b.w), acc, false);
   return acc;
 }
+// Pins four 16-byte values as whole register quads (no code): the 16-byte
+// LDS reads that produced them are not split into 4-byte reads.
+__device__ __forceinline__ void keep_whole(uint4& a, uint4& b, uint4& c, uint4& d) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 va = __builtin_bit_cast(u32x4, a), vb = __builtin_bit_cast(u32x4, b);
+  u32x4 vc = __builtin_bit_cast(u32x4, c), vd = __builtin_bit_cast(u32x4, d);
+  asm volatile("" : "+v"(va), "+v"(vb), "+v"(vc), "+v"(vd));
+  a = __builtin_bit_cast(uint4, va); b = __builtin_bit_cast(uint4, vb);
+  c = __builtin_bit_cast(uint4, vc); d = __builtin_bit_cast(uint4, vd);
+}
+// the same from zero: the first pair on the three-operand form with a zero
+// addend, so no accumulator register is cleared first
+__device__ __forceinline__ float dot2_bf16_0(const uint4 a, const uint4 b) {
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  float acc;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a.x), "v"(b.x));
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.y), __builtin_bit_cast(b2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.z), __builtin_bit_cast(b2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.w), __builtin_bit_cast(b2_t, b.w), acc, false);
+  return acc;
+}
 
 // dOffset of a block's owned entries (each (pixel, tap) pair has exactly one
 // owner core): lanes = entries (lane & 31), the two lane halves take the two
@@ -94,10 +115,10 @@ __device__ __forceinline__ void doffset_owned(const int4 cur, int nb, int lane, 
   const int r = lane & 31, half = lane >> 5;
   const int ex = __shfl(cur.x, r), ey = __shfl(cur.y, r), ez = __shfl(cur.z, r), ew = __shfl(cur.w, r);
   const uint32_t info = (uint32_t)ey;
-  const bool own = r < nb && ((info >> 8) & 1u);
+  const bool own = r < nb && (int)info < 0;
   float gy = 0.f, gx = 0.f;
   if (own) {
-    const int cy = (info >> 16) & 255, cx = info >> 24;
+    const int cy = (info >> 16) & 255, cx = (info >> 24) & 127;
     const float ly = __int_as_float(ez), lx = __int_as_float(ew);
     const float hy = 1.0f - ly, hx = 1.0f - lx;
     const T* drow = dst + r * dcstr;
@@ -247,7 +268,7 @@ __device__ __forceinline__ void bwd_lists_body(const BwdParams& p, int bid) {
           if (cm) {
             const int oy = max(ix.y0, 0), ox = max(ix.x0, 0);
             const uint32_t owned = (oy >= Y0 && oy < Y0 + chn && ox >= X0 && ox < X0 + cwn) ? 1u : 0u;
-            ent[u] = make_int4(pp[u], (int)((uint32_t)t | (owned << 8) | (cm << 9) |
+            ent[u] = make_int4(pp[u], (int)((uint32_t)t | (cm << 9) | (owned << 31) |
                                             ((uint32_t)(ix.y0 - Y0 + 1) << 16) | ((uint32_t)(ix.x0 - X0 + 1) << 24)),
                                __float_as_int(ix.ly), __float_as_int(ix.lx));
             k = true;
@@ -278,6 +299,10 @@ __device__ __forceinline__ void bwd_lists_body(const BwdParams& p, int bid) {
     }
     running += __shfl(c, U * NW - 1);
   }
+  // the last block of the sampling backward's MFMA form ends on a multiple
+  // of 64 entries: the slots up to there hold entries with no corner and no
+  // owner whose dCol row (pixel Ho*Wo) lies past the image's rows
+  for (int i = running + tid; i < ((running + 63) & ~63); i += NT) list[i] = make_int4(HoWo, 0, 0, 0);
   if (tid == 0) p.counts[tg] = running;
 }
 
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
         for (int r = 0; r < nbs; ++r) {
           const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
           const uint32_t cm = (info >> 9) & 15u;
-          const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+          const int cy = (info >> 16) & 255, cx = (info >> 24) & 127;  // corner (y0, x0) relative to (Y0-1, X0-1)
           TapIndex ix;
           ix.outside = false;
           ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
@@ -437,7 +462,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd(const BwdParams p) {
             if (r >= nbs) break;
             const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(cur.y, r);
             const uint32_t cm = (info >> 9) & 15u;
-            const int cy = (info >> 16) & 255, cx = info >> 24;
+            const int cy = (info >> 16) & 255, cx = (info >> 24) & 127;
             TapIndex ix;
             ix.outside = false;
             ix.ly = __int_as_float(__builtin_amdgcn_readlane(cur.z, r));
@@ -548,12 +573,14 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
   constexpr int NFW = 64 * CC / 8;
 
   const int e = tid / PPE, v = tid % PPE;  // this lane's entry in a block and 8-channel piece
-  // Every load and store of the block loop is issued by every lane: entries
-  // past the list read zeros through the buffer range checks, and stores of
-  // lanes with nothing to store go past their buffer's range, where they are
-  // dropped.  The loop then has no branches around memory operations, and
+  // Every load and store of the block loop is issued by every lane: the
+  // list's last block is filled up with entries that have no corner and no
+  // owner and whose dCol rows lie past the buffer's range (read as zeros),
+  // blocks past the list (loaded ahead, never used) read zero entries, and
+  // stores of lanes with nothing to store go past their buffer's range,
+  // where they are dropped.  The loop then has no branches around memory operations, and
   // the waits for the loads in flight stay exact.
-  const __amdgpu_buffer_rsrc_t lrs = make_brsrc(list, (uint32_t)L * 16u);
+  const __amdgpu_buffer_rsrc_t lrs = make_brsrc(list, (uint32_t)((L + 63) & ~63) * 16u);
   const __amdgpu_buffer_rsrc_t drs = make_brsrc(dcol, (uint32_t)((size_t)HoWo * p.Ck * 2));
   const __amdgpu_buffer_rsrc_t ors = make_brsrc(doffp, (uint32_t)(2 * p.K2 * HoWo * 4));
   auto load_entry = [&](int b) {
@@ -561,7 +588,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
   };
   // dCol row of (output pixel, tap): (pix*K2 + tap)*Cin within the image
   auto load_piece = [&](int b, const int4 en) {
-    const int off = b * BLK + e < L ? ((en.x * p.K2 + (en.y & 255)) * p.Cin + v * 8) * 2 : kOOB;
+    const int off = ((en.x * p.K2 + (en.y & 255)) * p.Cin + v * 8) * 2;
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
   };
 
@@ -608,26 +635,35 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  int w0 = -1, w1 = -1;  // the weight this lane last wrote into each weight buffer
+  // weight-tile byte offset of this lane's entry column in row 0, and of its
+  // corner's core pixel relative to cy * CW + cx
+  const unsigned ecol = (unsigned)(((e >> 3) << 4) + (e & 7) * 2);
+  const unsigned pcv = (unsigned)((v >> 1) * p.CW + (v & 1) - p.CW - 1);
+  constexpr int WSH = RP == 4 ? 2 : 3;  // (P / RP) % NCH << 4 == (P << WSH) & ((NCH - 1) << 4)
+  static_assert(RP == 4 || RP == 2, "weight-tile swizzle period");
+  int w0 = (int)ecol, w1 = (int)ecol;  // the weight this lane last wrote into each weight buffer
 
   // One block: en, dq hold its list entry and dCol piece and are refilled
   // with those of blocks b + 4 and b + 2 (whose list entry is en2).
   auto step = [&](const int b, int4& en, uint4& dq, const int4& en2, int& wold, const int buf) {
-    const bool valid = b * BLK + e < L;
     const uint32_t info = (uint32_t)en.y;
     const float ly = __int_as_float(en.z), lx = __int_as_float(en.w);
     const float hy = 1.0f - ly, hx = 1.0f - lx;
-    const int cy = (info >> 16) & 255, cx = info >> 24;  // corner (y0, x0) relative to (Y0-1, X0-1)
+    const int cy = (info >> 16) & 255, cx = (info >> 24) & 127;  // corner (y0, x0) relative to (Y0-1, X0-1)
 
     // offset gradient over this lane's channels
     const bf16_t* c00 = xl + (cy * XW + cx) * CC + v * 8;
-    const uint4 x00 = *(const uint4*)c00, x01 = *(const uint4*)(c00 + CC);
-    const uint4 x10 = *(const uint4*)(c00 + XW * CC), x11 = *(const uint4*)(c00 + (XW + 1) * CC);
-    const float d00 = dot2_bf16(dq, x00, 0.f), d01 = dot2_bf16(dq, x01, 0.f);
-    const float d10 = dot2_bf16(dq, x10, 0.f), d11 = dot2_bf16(dq, x11, 0.f);
+    uint4 x00 = *(const uint4*)c00, x01 = *(const uint4*)(c00 + CC);
+    uint4 x10 = *(const uint4*)(c00 + XW * CC), x11 = *(const uint4*)(c00 + (XW + 1) * CC);
+    keep_whole(x00, x01, x10, x11);
+    const float d00 = dot2_bf16_0(dq, x00), d01 = dot2_bf16_0(dq, x01);
+    const float d10 = dot2_bf16_0(dq, x10), d11 = dot2_bf16_0(dq, x11);
     float gy = hx * (d10 - d00) + lx * (d11 - d01);
     float gx = hy * (d01 - d00) + ly * (d11 - d10);
-    const bool bad = valid & !(fabsf(gy) + fabsf(gx) <= 3.402823466e38f);
+    // (lane masks straight from the compares: no boolean is widened to a
+    // register for the ballot)
+    const float gsum = fabsf(gy) + fabsf(gx);
+    const unsigned long long badm = __builtin_amdgcn_fcmpf(gsum, 3.402823466e38f, 10 /* unordered or > */);
     gy += row_shr<1>(gy);
     gx += row_shr<1>(gx);
     gy += row_shr<2>(gy);
@@ -637,17 +673,18 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
       gx += row_shr<4>(gx);
     }
     {
-      const bool own = valid & (v == PPE - 1) & (((info >> 8) & 1u) != 0u);
-      const int o = own ? ((2 * (int)(info & 255u)) * HoWo + en.x) * 4 : kOOB;
-      // (the builtin stores 32-bit integers: pass the bits)
+      const bool own = (v == PPE - 1) & ((int)info < 0);
+      const int o = own ? (int)(__umul24(info & 255u, 2u * (unsigned)HoWo) + (unsigned)en.x) * 4 : kOOB;
+      // (the builtin stores 32-bit integers: pass the bits; gx goes one
+      // offset channel further through the scalar offset)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gy), ors, o, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gx), ors, own ? o + HoWo * 4 : kOOB, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gx), ors, o, HoWo * 4, 0);
     }
 
     // non-finite dCol values: flag the products, stage zeros
     uint4 dqs = dq;
-    if (__builtin_amdgcn_ballot_w64(bad)) {
-      if (bad) {
+    if (badm) {
+      if (!(gsum <= 3.402823466e38f)) {
         const uint32_t cm = (info >> 9) & 15u;
         uint4 keep = make_uint4(~0u, ~0u, ~0u, ~0u);
 #pragma unroll 1
@@ -676,17 +713,18 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
     unsigned char* wb = wtile + buf * 2 * TILE;
     unsigned char* sb = stg + buf * STG;
     if (v < 4) {
-      if (wold >= 0) {
-        *(bf16_t*)(wb + wold) = 0;
-        *(bf16_t*)(wb + TILE + wold) = 0;
-      }
-      wold = -1;
-      if (valid & (((info >> (9 + v)) & 1u) != 0u)) {
-        const unsigned P = (unsigned)((cy - 1 + (v >> 1)) * p.CW + (cx - 1 + (v & 1)));
+      // wold is in this lane's column (entry e): a location cleared already
+      // holds zero, and another corner of the entry written to it now is
+      // written after this clear
+      *(bf16_t*)(wb + wold) = 0;
+      *(bf16_t*)(wb + TILE + wold) = 0;
+      if (((info >> (9 + v)) & 1u) != 0u) {
+        const unsigned P = __umul24((unsigned)cy, (unsigned)p.CW) + (unsigned)cx + pcv;
         const float w = ((v >> 1) ? ly : hy) * ((v & 1) ? lx : hx);
         const bf16_t hi = f32_to_bf16(w);
         const bf16_t lo = f32_to_bf16(w - bf16_to_f32(hi));
-        wold = (int)(P * ROWB + ((((unsigned)e >> 3) ^ ((P / RP) % NCH)) << 4) + (e & 7) * 2);
+        // row P, 16-byte chunk (e / 8) ^ ((P / RP) % NCH), element e % 8
+        wold = (int)((P * ROWB + ecol) ^ ((P << WSH) & ((NCH - 1) << 4)));
         *(bf16_t*)(wb + wold) = hi;
         *(bf16_t*)(wb + TILE + wold) = lo;
       }
@@ -1551,7 +1589,7 @@ static hipError_t backward_t(const deft_plan& p, const BackwardArgs& a, hipStrea
   b.CH = p.btile_h; b.CW = p.btile_w; b.bt_h = p.btiles_h; b.bt_w = p.btiles_w; b.halo = p.bhalo;
   b.CC = p.chunk_b;
   b.dcstr = p.chunk_b + (p.bwd_mf ? 16 : (d.dtype == DEFT_BF16 ? 8 : 4));
-  b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap;
+  b.num_wg = p.num_btiles * d.offset_groups * (p.cg / p.chunk_b); b.list_cap = p.list_cap + 64;  // list stride: room for the last block's filler entries
   int cb = 0;
   while ((1 << cb) < p.list_cap + 1) ++cb;
   b.capbits = cb;

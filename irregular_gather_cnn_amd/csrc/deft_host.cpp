@@ -286,7 +286,7 @@ bool layout_plan(deft_plan& p, int th, int tw, int halo, int chunk, bool direct 
   // bf16: dOffset rounded once more, as the offset-weight backward reads it
   p.ws_doff16 = o; if (d.dtype == DEFT_BF16) o = align256(o + P * s.oc * 2);
   p.ws_list = o;
-  o = align256(o + (size_t)p.num_btiles * d.offset_groups * p.list_cap * 16);
+  o = align256(o + (size_t)p.num_btiles * d.offset_groups * (p.list_cap + 64) * 16);
   p.ws_lcount = o; o = align256(o + (size_t)p.num_btiles * d.offset_groups * 4);
   // dOffset partials (one per backward channel chunk) followed by one word
   // for max |dCol|; both zeroed by the backward's prep kernel
