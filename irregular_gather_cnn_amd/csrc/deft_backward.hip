@@ -1311,22 +1311,24 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
     }
     __syncthreads();
     // B tile: dOffset at the output pixel whose tap lands on the input pixel.
-    // Lane = pixel, wave = depth index (stepping by 8): a wave's 64 gathers
-    // read one dOffset plane at a shifted run of consecutive pixels, a few
-    // cache lines; eight gathers per thread in flight at a time
+    // Lane = pixel, wave = a run of eight consecutive depth indices (runs
+    // stepping by 64; len is a multiple of 16): each of a wave's gathers
+    // reads one dOffset plane at a shifted run of consecutive pixels, a few
+    // cache lines, eight per thread in flight at a time; the run goes to LDS
+    // in 16-byte writes (rows 16-byte aligned, no bank conflicts)
     {
       const int pix = tid & 63;
       const int q = pix0 + pix;
       const int y = fdiv(q, p.div_w), xx = q - y * p.W;
-      for (int k0 = wave; k0 < len; k0 += 8 * 8) {
+      for (int k0 = wave * 8; k0 < len; k0 += 8 * 8) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int kl = k0 + 8 * u;
-          const int4 ki = kinfo[kl < len ? kl : 0];
+          const int kl = k0 + u;
+          const int4 ki = kinfo[kl];
           v[u] = 0.f;
           const int ny = y + ki.y, nx = xx + ki.z;
-          if (kl < len && ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
+          if (ki.x >= 0 && q < HW && ny >= 0 && nx >= 0) {
             int ho = ny, wo = nx;
             bool ok = true;
             if (p.SH != 1) { ho = fdiv(ny, p.div_sh); ok = ho * p.SH == ny; }
@@ -1334,11 +1336,12 @@ __global__ __launch_bounds__(512) void k_dx_final(const DxParams p) {
             if (ok && ho < p.Ho && wo < p.Wo) v[u] = doff[(size_t)ki.x + (size_t)ho * p.Wo + wo];
           }
         }
+        alignas(16) T o[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int kl = k0 + 8 * u;
-          if (kl < len) bt[pix * bstr + kl] = Elem<T>::from_f32(v[u]);
-        }
+        for (int u = 0; u < 8; ++u) o[u] = Elem<T>::from_f32(v[u]);
+        uint4* dst = (uint4*)(bt + pix * bstr + k0);
+#pragma unroll
+        for (int h = 0; h < (int)sizeof(o) / 16; ++h) dst[h] = ((const uint4*)o)[h];
       }
     }
     __syncthreads();
