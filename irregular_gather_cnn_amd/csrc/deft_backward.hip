@@ -674,7 +674,7 @@ __global__ __launch_bounds__(256) void k_sample_bwd_mf(const BwdParams p) {
     }
     {
       const bool own = (v == PPE - 1) & ((int)info < 0);
-      const int o = own ? (int)(__umul24(info & 255u, 2u * (unsigned)HoWo) + (unsigned)en.x) * 4 : kOOB;
+      const int o = own ? (int)((info & 255u) * (2u * (unsigned)HoWo) + (unsigned)en.x) * 4 : kOOB;
       // (the builtin stores 32-bit integers: pass the bits; gx goes one
       // offset channel further through the scalar offset)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gy), ors, o, 0, 0);
